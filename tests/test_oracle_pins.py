@@ -1,0 +1,476 @@
+"""Pins of the reference oracle against what the pages and mathematics fix (CPU only).
+
+Each test checks the oracle against something other than itself: hand-derived values from
+the format definition, torch's float8_e4m3fn codec (a library routine), brute-force nearest
+search, exact rational arithmetic (fractions), integer matmul special cases, closed forms and
+invariants.  A plausible mistake anywhere in the oracle (wrong rounding direction, dropped
+saturation, sign of zero, transposed scale index, wrong group boundary, a sign or index error
+in the GEMM) fails at least one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qr_synth
+from exact_ref import (bf16_bits_of, e4m3_nearest, e4m3_values_torch, f32_of, rn32, rn_bf16)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+def bf16_f32(bits):
+    return qr_synth.bf16_bits_to_f32(np.asarray(bits, np.uint16))
+
+
+# ============================================================== E4M3 codec
+
+def test_anchor_codes_hand_derived():
+    n = 0
+    for parts in _golden_lines("e4m3_anchor_codes.txt"):
+        v = np.float32(parts[0])
+        assert Fraction(float(v)) == Fraction(parts[0].lstrip("-")) * (-1 if parts[0].startswith("-") else 1) \
+            or parts[0] in ("-0.0",)
+        assert oracle.e4m3_encode(v) == int(parts[1], 16), parts
+        n += 1
+    assert n >= 25
+
+
+def test_decode_matches_torch_float8_all_codes():
+    mine = oracle.e4m3_decode_table()
+    ref = e4m3_values_torch()
+    nan = np.isnan(ref)
+    assert list(np.flatnonzero(nan)) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert math.copysign(1.0, mine[0x80]) == -1.0      # 0x80 is -0
+
+
+def test_decode_structure():
+    v = oracle.e4m3_decode_table()
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                     # monotone over 0x00..0x7E
+    assert pos[-1] == 448.0 and pos[1] == 2.0 ** -9 and pos[8] == 2.0 ** -6 and pos[0x38] == 1.0
+    assert np.array_equal(v[0x80:0xFF], -pos)           # sign symmetry
+    finite = v[~np.isnan(v)]
+    assert len(set(finite.tolist())) == 253             # +0 and -0 compare equal
+
+
+def test_roundtrip_all_finite_codes():
+    v = oracle.e4m3_decode_table()
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert oracle.e4m3_encode(np.float32(v[c]) if c != 0x80 else np.float32(-0.0)) == c
+
+
+def _midpoint_probe_values():
+    pos = oracle.e4m3_decode_table()[:0x7F]
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)          # exact in binary32
+    assert np.array_equal(mids.astype(np.float64), (pos[:-1] + pos[1:]) / 2)
+    vals = [mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+            pos.astype(np.float32), np.nextafter(pos.astype(np.float32), np.float32(np.inf)),
+            np.array([447.99997, 448.0, 448.00003, 463.99997, 464.0, 464.00003, 1e30,
+                      np.finfo(np.float32).max, np.finfo(np.float32).tiny, 1e-45, 2.0 ** -10,
+                      np.nextafter(np.float32(2.0 ** -10), np.float32(1))], np.float32)]
+    rng = np.random.default_rng(7)
+    for sc in (1e-4, 1e-2, 1.0, 30.0, 300.0):
+        vals.append((rng.standard_normal(4000) * sc).astype(np.float32))
+    v = np.concatenate(vals)
+    return np.concatenate([v, -v])
+
+
+def test_encode_matches_bruteforce_nearest():
+    v = _midpoint_probe_values()
+    mine = oracle.e4m3_encode_array(v)
+    ref = np.array([e4m3_nearest(x) for x in v], np.uint8)
+    bad = np.flatnonzero(mine != ref)
+    assert bad.size == 0, [(float(v[i]), hex(mine[i]), hex(ref[i])) for i in bad[:10]]
+
+
+def test_encode_matches_torch_cast_below_448():
+    rng = np.random.default_rng(11)
+    v = np.concatenate([(rng.standard_normal(200000) * s).astype(np.float32)
+                        for s in (1e-3, 0.05, 1.0, 40.0)])
+    v = v[np.abs(v) < 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode_array(v), ref)
+
+
+def test_encode_saturates_every_binade_above_448():
+    big = np.float32(448.0) * (np.float32(2.0) ** np.arange(0, 120, dtype=np.float32))
+    big = np.concatenate([big, np.nextafter(big, np.float32(np.inf)), [np.finfo(np.float32).max]])
+    big = big[np.isfinite(big)].astype(np.float32)
+    assert np.all(oracle.e4m3_encode_array(big) == 0x7E)
+    assert np.all(oracle.e4m3_encode_array(-big) == 0xFE)
+
+
+# ============================================================== scale and quotient
+
+def test_group_scale_exact_for_every_bf16_amax():
+    bits = np.arange(0x0000, 0x7F80, dtype=np.uint16)         # every finite non-negative bf16
+    amax = bf16_f32(bits)
+    # drive the real quantizer: each row's first element is the group's amax
+    x = np.zeros((bits.size, 128), np.uint16)
+    x[:, 0] = bits
+    _, s = oracle.quant_rows(x)
+    s = s[:, 0]
+    # exact rational reference on a deterministic subsample + library IEEE division on all
+    assert np.array_equal(s, (amax / np.float32(448.0)).astype(np.float32))
+    for i in range(0, bits.size, 97):
+        assert Fraction(float(s[i])) == rn32(Fraction(float(amax[i])) / 448), hex(bits[i])
+
+
+def _groups_for_amax(amax_bits):
+    """bf16 rows: a group per 127 values x with |x| <= amax, first element = amax."""
+    allb = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    allv = bf16_f32(allb)
+    ok = np.isfinite(allv) & (np.abs(allv) <= bf16_f32(np.uint16(amax_bits)))
+    xs = allb[ok]
+    pad = (-xs.size) % 127
+    xs = np.concatenate([xs, np.zeros(pad, np.uint16)])
+    body = xs.reshape(-1, 127)
+    rows = np.empty((body.shape[0], 128), np.uint16)
+    rows[:, 0] = amax_bits
+    rows[:, 1:] = body
+    return rows
+
+
+AMAX_SAMPLES = [0x3F80, 0x43E0, 0x4000, 0x3DCD, 0x4120, 0x3C23, 0x4B00, 0x7F7F, 0x0080, 0x0001,
+                0x0237, 0x1A2B, 0x2F11, 0x3A83, 0x3B12, 0x3FFF, 0x447A, 0x5F00, 0x60C1, 0x7000]
+
+
+@pytest.mark.parametrize("amax_bits", AMAX_SAMPLES)
+def test_codes_exhaustive_over_bf16_for_sampled_amax(amax_bits):
+    """Every bf16 x with |x| <= amax: oracle code == E4M3_RNE_SAT(IEEE binary32 x/s)."""
+    rows = _groups_for_amax(amax_bits)
+    q, s = oracle.quant_rows(rows)
+    sc = np.float32(bf16_f32(np.uint16(amax_bits)).item()) / np.float32(448.0)
+    assert np.all(s[:, 0] == sc)
+    x = bf16_f32(rows)
+    if sc == 0:
+        v = x
+    else:
+        with np.errstate(over="ignore"):
+            v = (x / sc).astype(np.float32)                   # IEEE division (library)
+    small = np.abs(v) < 448
+    ref = np.where(np.signbit(v), np.uint8(0xFE), np.uint8(0x7E))
+    ref[small] = torch.from_numpy(v[small]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    # exact rational check on a subsample: the quotient itself is correctly rounded
+    flat_x, flat_q = x.ravel(), q.ravel()
+    for i in range(0, flat_x.size, 211):
+        if sc != 0:
+            exact = rn32(Fraction(float(flat_x[i])) / Fraction(float(sc)))
+            xv = float(exact) if exact != 0 else (-0.0 if np.signbit(flat_x[i]) else 0.0)
+            assert flat_q[i] == e4m3_nearest(xv)
+
+
+def test_amax_element_encodes_to_448_and_zero_group():
+    x = qr_synth.normal_bf16(5, (64, 512), 1.0)
+    q, s = oracle.quant_rows(x)
+    xf = bf16_f32(x)
+    for r in range(64):
+        for g in range(4):
+            seg = xf[r, g * 128:(g + 1) * 128]
+            i = int(np.argmax(np.abs(seg)))
+            assert q[r, g * 128 + i] == (0xFE if seg[i] < 0 else 0x7E)
+    z = np.zeros((2, 128), np.uint16)
+    z[1, ::2] = 0x8000                                       # negative zeros
+    qz, sz = oracle.quant_rows(z)
+    assert np.all(sz == 0)
+    assert np.array_equal(qz[0], np.zeros(128, np.uint8))
+    assert np.array_equal(qz[1, ::2], np.full(64, 0x80, np.uint8))
+    assert np.array_equal(qz[1, 1::2], np.zeros(64, np.uint8))
+
+
+def test_per_element_error_bound():
+    """|x/s - dq(q)| <= half an E4M3 step at |dq(q)| unless saturated (where |x/s| > 448)."""
+    x = qr_synth.normal_bf16(9, (256, 512), 1.0, 10, 4)
+    q, s = oracle.quant_rows(x)
+    v = bf16_f32(x).astype(np.float64) / np.repeat(s, 128, axis=1).astype(np.float64)
+    d = oracle.e4m3_decode_table()[q]
+    a = np.abs(d)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    half_step = np.where(a < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
+    # a value rounding up into the next binade sits at most half a step of the lower binade
+    half_step = np.maximum(half_step, np.where(a == 2.0 ** e, 2.0 ** (e - 5), 0))
+    err = np.abs(v - d)
+    sat = np.abs(v) > 448
+    assert np.all(err[~sat] <= half_step[~sat] * (1 + 2.0 ** -20))
+    assert np.all(np.abs(d[sat]) == 448)
+
+
+# ============================================================== quantizer layouts
+
+def test_column_groups_equal_row_groups_of_transpose():
+    x = qr_synth.normal_bf16(21, (384, 200), 1.0, 22, 3)
+    qT, sT = oracle.quant_cols_T(x)
+    q2, s2 = oracle.quant_rows(np.ascontiguousarray(x.T))
+    assert np.array_equal(qT, q2) and np.array_equal(sT, s2)
+
+
+def test_block_quant_of_transpose_is_transpose():
+    w = qr_synth.normal_bf16(23, (384, 256), 0.02)
+    q, s = oracle.quant_blocks(w)
+    qt, st = oracle.quant_blocks(np.ascontiguousarray(w.T))
+    assert np.array_equal(qt, q.T) and np.array_equal(st, s.T)
+
+
+def test_block_scale_is_max_of_row_group_amax():
+    """A 128x128 block's amax is the max over its 128 rows' 1x128 amaxes, and s = amax/448 is
+    monotone, so the block scale equals the max of the row-group scales."""
+    w = qr_synth.normal_bf16(25, (256, 384), 0.02)
+    _, sb = oracle.quant_blocks(w)
+    _, sr = oracle.quant_rows(w)
+    assert np.array_equal(sb, sr.reshape(2, 128, 3).max(axis=1))
+
+
+def test_power_of_two_invariance():
+    x = qr_synth.normal_bf16(27, (128, 384), 1.0, 28, 2)
+    q, s = oracle.quant_rows(x)
+    for j in (-20, -3, 1, 5, 30):
+        x2 = qr_synth.f32_to_bf16_bits(bf16_f32(x) * np.float32(2.0 ** j))
+        q2, s2 = oracle.quant_rows(x2)
+        assert np.array_equal(q2, q)
+        assert np.array_equal(s2, s * np.float32(2.0 ** j))
+
+
+def test_partial_group_equals_zero_padded():
+    x = qr_synth.normal_bf16(29, (50, 200), 1.0)
+    q, s = oracle.quant_rows(x)
+    xp = np.zeros((50, 256), np.uint16)
+    xp[:, :200] = x
+    qp, sp = oracle.quant_rows(xp)
+    assert np.array_equal(q, qp[:, :200]) and np.array_equal(s, sp)
+    qT, sT = oracle.quant_cols_T(np.ascontiguousarray(x.T))      # rows = 200: partial group
+    assert np.array_equal(qT, q) and np.array_equal(sT, s)
+    w = qr_synth.normal_bf16(31, (200, 136), 0.02)
+    qb, sb = oracle.quant_blocks(w)
+    wp = np.zeros((256, 256), np.uint16)
+    wp[:200, :136] = w
+    qbp, sbp = oracle.quant_blocks(wp)
+    assert np.array_equal(qb, qbp[:200, :136]) and np.array_equal(sb, sbp)
+
+
+def test_nonfinite_input_rejected():
+    x = np.zeros((1, 128), np.uint16)
+    for bad in (0x7F80, 0xFF80, 0x7FC0):
+        x[0, 5] = bad
+        with pytest.raises(ValueError):
+            oracle.quant_rows(x)
+        with pytest.raises(ValueError):
+            oracle.quant_blocks(x)
+
+
+# ============================================================== GEMM
+
+def _random_codes(rng, shape):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38                               # no NaN codes
+    return c
+
+
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_gemm_bruteforce_fractions(K):
+    rng = np.random.default_rng(K)
+    M, N = 3, 5
+    qa = _random_codes(rng, (M, K))
+    sa = rng.uniform(1e-3, 2.0, (M, K // 128)).astype(np.float32)
+    qw = _random_codes(rng, (N, K))
+    sw = rng.uniform(1e-3, 2.0, (1, K // 128)).astype(np.float32)
+    Y, S = oracle.fprop(qa, sa, qw, sw)
+    tv = e4m3_values_torch()
+    for m in range(M):
+        for n in range(N):
+            y = Fraction(0)
+            a = Fraction(0)
+            for k in range(K):
+                p = (Fraction(float(tv[qa[m, k]])) * Fraction(float(sa[m, k // 128])) *
+                     Fraction(float(tv[qw[n, k]])) * Fraction(float(sw[0, k // 128])))
+                y += p
+                a += abs(p)
+            assert abs(Fraction(Y[m, n]) - y) <= Fraction(1, 10 ** 12) * a
+            assert abs(Fraction(S[m, n]) - a) <= Fraction(1, 10 ** 12) * a
+
+
+def _int_codes():
+    """Codes whose values are the integers -16..16 (all exact in E4M3)."""
+    tv = e4m3_values_torch()
+    lut = {}
+    for c in range(256):
+        v = tv[c]
+        if not np.isnan(v) and v == int(v) and abs(v) <= 16 and int(v) not in lut:
+            lut[int(v)] = c
+    assert sorted(lut) == list(range(-16, 17))
+    return lut
+
+
+def test_gemm_integer_special_case_exact():
+    lut = _int_codes()
+    rng = np.random.default_rng(3)
+    M, N, K = 7, 9, 256
+    ia = rng.integers(-16, 17, (M, K))
+    iw = rng.integers(-16, 17, (N, K))
+    qa = np.vectorize(lut.get)(ia).astype(np.uint8)
+    qw = np.vectorize(lut.get)(iw).astype(np.uint8)
+    Y, _ = oracle.fprop(qa, np.ones((M, 2), np.float32), qw, np.ones((1, 2), np.float32))
+    assert np.array_equal(Y, (ia.astype(np.int64) @ iw.T.astype(np.int64)).astype(np.float64))
+    # the same integers through DGrad's and WGrad's layouts
+    iw2 = rng.integers(-16, 17, (128, 9))                  # W [N=128, K=9] for DGrad
+    qw2 = np.vectorize(lut.get)(iw2).astype(np.uint8)
+    dX, _ = oracle.dgrad(np.ascontiguousarray(qa[:, :128]), np.ones((M, 1), np.float32), qw2,
+                         np.ones((1, 1), np.float32))
+    assert np.array_equal(dX, (ia[:, :128] @ iw2).astype(np.float64))
+    # WGrad operands are token-grouped rows: dY^T [7, 128 tokens], X^T [9, 128 tokens]
+    dW, _ = oracle.wgrad(np.ascontiguousarray(qa[:, :128]), np.ones((M, 1), np.float32),
+                         np.ascontiguousarray(qw[:, :128]), np.ones((N, 1), np.float32))
+    assert np.array_equal(dW, (ia[:, :128] @ iw[:, :128].T).astype(np.float64))
+
+
+def test_gemm_identity_weight():
+    x = qr_synth.normal_bf16(41, (64, 256), 1.0, 42, 2)
+    qa, sa = oracle.quant_rows(x)
+    qw = np.zeros((256, 256), np.uint8)
+    np.fill_diagonal(qw, 0x38)
+    Y, _ = oracle.fprop(qa, sa, qw, np.ones((2, 2), np.float32))
+    assert np.array_equal(Y, oracle.dequant_rows(qa, sa))
+
+
+def test_dgrad_is_fprop_with_transposed_weight():
+    dy = qr_synth.normal_bf16(43, (96, 256), 1e-3)
+    w = qr_synth.normal_bf16(44, (256, 384), 0.02)
+    qd, sd = oracle.quant_rows(dy)
+    qw, sw = oracle.quant_blocks(w)
+    dX, S1 = oracle.dgrad(qd, sd, qw, sw)
+    Y, S2 = oracle.fprop(qd, sd, np.ascontiguousarray(qw.T), np.ascontiguousarray(sw.T))
+    assert np.allclose(dX, Y, rtol=0, atol=1e-12 * S1.max()) and np.allclose(S1, S2)
+
+
+def test_gemms_against_numpy_blas():
+    x = qr_synth.normal_bf16(45, (256, 384), 1.0, 46, 4)
+    dy = qr_synth.normal_bf16(47, (256, 512), 1e-3)
+    qxT, sxT = oracle.quant_cols_T(x)
+    qdT, sdT = oracle.quant_cols_T(dy)
+    dW, S = oracle.wgrad(qdT, sdT, qxT, sxT)
+    A = oracle.dequant_rows(qdT, sdT)
+    B = oracle.dequant_rows(qxT, sxT)
+    assert dW.shape == (512, 384)
+    assert np.all(np.abs(dW - A @ B.T) <= 1e-12 * S)
+    assert np.allclose(S, np.abs(A) @ np.abs(B).T, rtol=1e-12)
+    # sampled sums equal the full ones exactly (same loop, same order)
+    mi = np.array([0, 5, 511, 100]), np.array([0, 383, 7, 200])
+    Ys, Ss = oracle.wgrad(qdT, sdT, qxT, sxT, sample=mi)
+    assert np.array_equal(Ys, dW[mi]) and np.array_equal(Ss, S[mi])
+
+
+# ============================================================== UAQ fold
+
+def test_uaq_golden_s1p5():
+    rows = [p for p in _golden_lines("uaq_s1p5.txt")]
+    wrows = [(int(a, 16), int(b, 16)) for a, b, *_ in rows if a != "gain"]
+    w = np.array([[a for a, _ in wrows]], np.uint16)
+    s = np.full(w.shape[1], 1.5, np.float32)
+    gains = [(np.float32(r[1]), np.float32(r[2])) for r in rows if r[0] == "gain"]
+    g = np.array([a for a, _ in gains] + [1.0] * (w.shape[1] - len(gains)), np.float32)
+    out, g2 = oracle.uaq_fold(w, s, g)
+    assert [int(v) for v in out[0]] == [b for _, b in wrows]
+    for i, (_, b) in enumerate(gains):
+        assert g2[i] == b
+
+
+def _uaq_cases():
+    """Random folds, plus near-midpoint folds: s = RN32(W / mid) for a bf16 midpoint mid puts
+    W/s within about 2^-24 (relative) of mid, where rounding W/s to binary32 first and then to
+    bf16 would often land on the midpoint and round the wrong way.  (An exact tie cannot
+    occur: a midpoint's odd 9-bit significand cannot divide an 8-bit one.)"""
+    rng = np.random.default_rng(51)
+    w = qr_synth.normal_bf16(52, (16, 96), 0.02)
+    s = rng.uniform(1.5, 4.0, 96).astype(np.float32)
+    wb = qr_synth.normal_bf16(60, (1, 400), 0.02)[0]
+    wv = bf16_f32(wb).astype(np.float64)
+    # a midpoint below |W|/1.5 so that s lands in the UAQ range (>= 1.5)
+    mids = []
+    for v in wv:
+        tgt = abs(v) / rng.uniform(1.5, 4.0)
+        e = math.floor(math.log2(tgt))
+        ulp = 2.0 ** (e - 7)
+        mids.append((math.floor(tgt / ulp) + 0.5) * ulp)
+    ms = np.array([abs(v) / m for v, m in zip(wv, mids)], np.float32)
+    return w, s, wb[None, :], ms
+
+
+def test_uaq_matches_exact_rational_rounding():
+    w, s, mw, ms = _uaq_cases()
+    naive_wrong = 0
+    for W, S in ((w, s), (mw, ms)):
+        out, _ = oracle.uaq_fold(W, S)
+        for (i, j), b in np.ndenumerate(W):
+            q = Fraction(float(bf16_f32(np.uint16(b)).item())) / Fraction(float(S[j]))
+            assert int(out[i, j]) & 0x7FFF == bf16_bits_of(abs(rn_bf16(q))), (hex(b), S[j])
+            assert (int(out[i, j]) >> 15) == (int(b) >> 15)
+            if W is mw:
+                naive = rn_bf16(rn32(q))
+                naive_wrong += naive != rn_bf16(q)
+    assert naive_wrong > 20          # the near-midpoint set does exercise double rounding
+
+
+def test_uaq_power_of_two_and_identity():
+    w = qr_synth.normal_bf16(53, (32, 256), 0.02)
+    out, _ = oracle.uaq_fold(w, np.ones(256, np.float32))
+    assert np.array_equal(out, w)
+    out, _ = oracle.uaq_fold(w, np.full(256, 4.0, np.float32))
+    assert np.array_equal(bf16_f32(out), bf16_f32(w) / np.float32(4.0))   # exact shift
+    # s = 2^j then 128x128 quantization: same codes, block scales divided by 2^j
+    q0, s0 = oracle.quant_blocks(w)
+    q1, s1 = oracle.quant_blocks(out)
+    assert np.array_equal(q0, q1) and np.array_equal(s1, s0 / np.float32(4.0))
+
+
+def test_uaq_preserves_product_exactly_before_rounding_and_within_bf16_after():
+    """WX = (W/s)(sX): exact in rationals; after the bf16 rounding of W/s the product moves
+    by at most 2^-8 * sum |W X| per output."""
+    rng = np.random.default_rng(55)
+    w = qr_synth.normal_bf16(56, (4, 128), 0.02)
+    x = qr_synth.normal_bf16(57, (3, 128), 1.0)
+    s = rng.uniform(1.5, 4.0, 128).astype(np.float32)
+    wf, xf = bf16_f32(w), bf16_f32(x)
+    out, _ = oracle.uaq_fold(w, s)
+    of = bf16_f32(out)
+    for n in range(4):
+        for m in range(3):
+            exact = sum(Fraction(float(wf[n, k])) * Fraction(float(xf[m, k])) for k in range(128))
+            folded = sum((Fraction(float(wf[n, k])) / Fraction(float(s[k]))) *
+                         (Fraction(float(s[k])) * Fraction(float(xf[m, k]))) for k in range(128))
+            assert folded == exact
+            rounded = sum(Fraction(float(of[n, k])) * Fraction(float(s[k])) *
+                          Fraction(float(xf[m, k])) for k in range(128))
+            bound = Fraction(1, 256) * sum(abs(Fraction(float(wf[n, k])) * Fraction(float(xf[m, k])))
+                                           for k in range(128))
+            assert abs(rounded - exact) <= bound
+
+
+def test_uaq_gain_and_rejections():
+    rng = np.random.default_rng(59)
+    s = rng.uniform(1.5, 4.0, 128).astype(np.float32)
+    g = rng.uniform(0.5, 2.0, 128).astype(np.float32)
+    _, g2 = oracle.uaq_fold(np.zeros((1, 128), np.uint16), s, g)
+    assert np.array_equal(g2, (g * s).astype(np.float32))
+    for i in range(0, 128, 17):
+        assert Fraction(float(g2[i])) == rn32(Fraction(float(g[i])) * Fraction(float(s[i])))
+    bad = s.copy()
+    bad[3] = 0.0
+    with pytest.raises(ValueError):
+        oracle.uaq_fold(np.zeros((1, 128), np.uint16), bad)
