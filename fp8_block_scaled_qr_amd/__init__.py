@@ -1,0 +1,222 @@
+"""Python binding of libqr.so, the gfx950 fine-grained FP8 quantize-and-multiply library.
+
+The functions below carry the names of the C entry points declared in include/qr.h and only
+marshal arguments: torch tensors on the GPU supply device pointers, torch's current HIP
+stream supplies the stream, and every step of the computation runs in the library's HIP
+kernels.  There is no CPU fallback: if libqr.so is missing or cannot be loaded, every call
+raises.
+
+Each ``qr_*`` function takes preallocated outputs (like the C ABI).  The ``quant_act``,
+``quant_w``, ``gemm_*`` and ``uaq_fold`` helpers allocate the outputs with torch and call the
+``qr_*`` function.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqr.so")
+
+QR_OK = 0
+QR_OUT_F32 = 0
+QR_OUT_BF16 = 1
+QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD = 0, 1, 2
+
+# Every entry point include/qr.h declares.
+EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant_w_128x128",
+           "qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad",
+           "qr_gemm_workspace_bytes", "qr_uaq_fold")
+
+_lib = None
+
+
+class QRError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load():
+    """Load libqr.so (raises if it is not built or cannot be loaded)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python fp8_block_scaled_qr_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.qr_status_string.argtypes = [I32]
+    L.qr_status_string.restype = ctypes.c_char_p
+    L.qr_abi_version.argtypes = []
+    L.qr_abi_version.restype = I32
+    L.qr_quant_act_1x128.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+    L.qr_quant_act_1x128.restype = I32
+    L.qr_quant_w_128x128.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+    L.qr_quant_w_128x128.restype = I32
+    for name in ("qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad"):
+        f = getattr(L, name)
+        f.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
+        f.restype = I32
+    L.qr_gemm_workspace_bytes.argtypes = [I32, I64, I64, I64]
+    L.qr_gemm_workspace_bytes.restype = SZ
+    L.qr_uaq_fold.argtypes = [P, I64, I64, I64, P, P, P, P]
+    L.qr_uaq_fold.restype = I32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().qr_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load().qr_abi_version())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status, where):
+    if status != QR_OK:
+        raise QRError(status, where)
+
+
+def _bits16(t):
+    """bf16 tensors travel as 16-bit patterns; accept bfloat16 or int16/uint16 views."""
+    return t
+
+
+# ------------------------------------------------------------------ C-ABI mirrors
+
+def qr_quant_act_1x128(x, rows, cols, ld_x, q_row, s_row, q_colT, s_colT, stream=None):
+    _check(load().qr_quant_act_1x128(_ptr(x), rows, cols, ld_x, _ptr(q_row), _ptr(s_row),
+                                     _ptr(q_colT), _ptr(s_colT), _stream(stream)),
+           "qr_quant_act_1x128")
+
+
+def qr_quant_w_128x128(w, n, k, ld_w, q, s, qT, sT, stream=None):
+    _check(load().qr_quant_w_128x128(_ptr(w), n, k, ld_w, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
+                                     _stream(stream)), "qr_quant_w_128x128")
+
+
+def _gemm(name, a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream):
+    f = getattr(load(), name)
+    _check(f(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(y), int(y_dtype), _ptr(ws),
+             int(ws_bytes), _stream(stream)), name)
+
+
+def qr_gemm_fp8_bsfprop(a, sa, b, sb, M, N, K, y, y_dtype, ws=None, ws_bytes=0, stream=None):
+    _gemm("qr_gemm_fp8_bsfprop", a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream)
+
+
+def qr_gemm_fp8_bsdgrad(dy, sdy, wT, swT, M, N, K, dx, dx_dtype, ws=None, ws_bytes=0,
+                        stream=None):
+    _gemm("qr_gemm_fp8_bsdgrad", dy, sdy, wT, swT, M, N, K, dx, dx_dtype, ws, ws_bytes, stream)
+
+
+def qr_gemm_fp8_bswgrad(dyT, sdyT, xT, sxT, M, N, K, dw, dw_dtype, ws=None, ws_bytes=0,
+                        stream=None):
+    _gemm("qr_gemm_fp8_bswgrad", dyT, sdyT, xT, sxT, M, N, K, dw, dw_dtype, ws, ws_bytes, stream)
+
+
+def qr_gemm_workspace_bytes(kind, M, N, K) -> int:
+    return int(load().qr_gemm_workspace_bytes(int(kind), M, N, K))
+
+
+def qr_uaq_fold(w, n, k, ld_w, s, w_out, gain=None, stream=None):
+    _check(load().qr_uaq_fold(_ptr(w), n, k, ld_w, _ptr(s), _ptr(w_out), _ptr(gain),
+                              _stream(stream)), "qr_uaq_fold")
+
+
+# ------------------------------------------------------------------ allocating helpers
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def quant_act(x, row=True, col=False, stream=None):
+    """x: bf16 [rows, cols] on the GPU.  Returns (q_row, s_row, q_colT, s_colT), with None for
+    the pair not requested."""
+    import torch
+    rows, cols = x.shape
+    dev = x.device
+    q_row = s_row = q_colT = s_colT = None
+    if row:
+        q_row = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s_row = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=dev)
+    if col:
+        q_colT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        s_colT = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.float32, device=dev)
+    qr_quant_act_1x128(x, rows, cols, x.stride(0), q_row, s_row, q_colT, s_colT, stream)
+    return q_row, s_row, q_colT, s_colT
+
+
+def quant_w(w, transposed=False, stream=None):
+    """w: bf16 [n, k] on the GPU.  Returns (q, s, qT, sT) (qT, sT None unless transposed)."""
+    import torch
+    n, k = w.shape
+    dev = w.device
+    q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    s = torch.empty((_cdiv(n, 128), _cdiv(k, 128)), dtype=torch.float32, device=dev)
+    qT = sT = None
+    if transposed:
+        qT = torch.empty((k, n), dtype=torch.uint8, device=dev)
+        sT = torch.empty((_cdiv(k, 128), _cdiv(n, 128)), dtype=torch.float32, device=dev)
+    qr_quant_w_128x128(w, n, k, w.stride(0), q, s, qT, sT, stream)
+    return q, s, qT, sT
+
+
+def _workspace(kind, M, N, K, device):
+    import torch
+    nb = qr_gemm_workspace_bytes(kind, M, N, K)
+    return (torch.empty(nb, dtype=torch.uint8, device=device) if nb else None), nb
+
+
+def _out(M, N, out_dtype, device):
+    import torch
+    return torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == QR_OUT_BF16 else torch.float32,
+                       device=device)
+
+
+def gemm_fprop(a, sa, b, sb, out_dtype=QR_OUT_BF16, stream=None):
+    M, K = a.shape
+    N = b.shape[0]
+    y = _out(M, N, out_dtype, a.device)
+    ws, nb = _workspace(QR_GEMM_FPROP, M, N, K, a.device)
+    qr_gemm_fp8_bsfprop(a, sa, b, sb, M, N, K, y, out_dtype, ws, nb, stream)
+    return y
+
+
+def gemm_dgrad(dy, sdy, wT, swT, out_dtype=QR_OUT_BF16, stream=None):
+    M, N = dy.shape
+    K = wT.shape[0]
+    dx = _out(M, K, out_dtype, dy.device)
+    ws, nb = _workspace(QR_GEMM_DGRAD, M, N, K, dy.device)
+    qr_gemm_fp8_bsdgrad(dy, sdy, wT, swT, M, N, K, dx, out_dtype, ws, nb, stream)
+    return dx
+
+
+def gemm_wgrad(dyT, sdyT, xT, sxT, out_dtype=QR_OUT_BF16, stream=None):
+    N, M = dyT.shape
+    K = xT.shape[0]
+    dw = _out(N, K, out_dtype, dyT.device)
+    ws, nb = _workspace(QR_GEMM_WGRAD, M, N, K, dyT.device)
+    qr_gemm_fp8_bswgrad(dyT, sdyT, xT, sxT, M, N, K, dw, out_dtype, ws, nb, stream)
+    return dw
+
+
+def uaq_fold(w, s, gain=None, inplace=False, stream=None):
+    """Returns the folded weight (bf16); gain (fp32, may be None) is updated in place."""
+    import torch
+    n, k = w.shape
+    out = w if inplace else torch.empty((n, k), dtype=w.dtype, device=w.device)
+    qr_uaq_fold(w, n, k, w.stride(0), s, out, gain, stream)
+    return out

@@ -1,0 +1,265 @@
+// C ABI of the gfx950 FP8 quantize-and-multiply library: argument validation (on the host,
+// before any HIP call) and dispatch to the kernels.  See include/qr.h for the contract.
+#include "qr.h"
+
+#include "qr_internal.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty if lo == hi
+};
+
+Range span(const void *p, int64_t bytes)
+{
+    Range r;
+    if (p && bytes > 0) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + (uintptr_t)bytes;
+    }
+    return r;
+}
+
+// Bytes spanned by a row-major [rows, cols] tensor with leading dimension ld.
+int64_t strided_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t elem)
+{
+    if (rows <= 0 || cols <= 0)
+        return 0;
+    return ((rows - 1) * ld + cols) * elem;
+}
+
+bool overlap(const Range &a, const Range &b)
+{
+    return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Products of the sizes must stay far below 2^62; every tensor handled here is < 2^40 bytes.
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+qr_status launch_status(hipError_t e) { return e == hipSuccess ? QR_OK : QR_ERR_LAUNCH; }
+
+qr_status check_gemm(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                     int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype, void *ws,
+                     size_t ws_bytes, int bscale, int64_t sb_rows)
+{
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (K % 128 != 0)
+        return QR_ERR_SHAPE;
+    if (y_dtype != QR_OUT_F32 && y_dtype != QR_OUT_BF16)
+        return QR_ERR_ARG;
+    if (M == 0 || N == 0)
+        return QR_OK;
+    if (!y)
+        return QR_ERR_NULL;
+    if (K > 0 && (!a || !sa || !b || !sb))
+        return QR_ERR_NULL;
+    // buffer descriptors address a tile of up to 256 rows with 32-bit offsets
+    if (K * 256 >= (int64_t(1) << 31) || (K / 128) * 4 * 256 >= (int64_t(1) << 31))
+        return QR_ERR_SHAPE;
+    if (misaligned(a, 16) || misaligned(b, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
+        misaligned(sb, 4) || misaligned(ws, 16))
+        return QR_ERR_ALIGN;
+    const int64_t nk = K / 128;
+    const int64_t esz = y_dtype == QR_OUT_BF16 ? 2 : 4;
+    const qr::GemmPlan plan = qr::plan_gemm(bscale, M, N, K);
+    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
+        return QR_ERR_WORKSPACE;
+    const Range ry = span(y, M * N * esz);
+    const Range rw = span(ws, plan.ws_bytes > 0 ? (int64_t)plan.ws_bytes : 0);
+    const Range ins[4] = {span(a, M * K), span(sa, M * nk * 4), span(b, N * K),
+                          span(sb, sb_rows * nk * 4)};
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rw, r))
+            return QR_ERR_ALIAS;
+    if (overlap(ry, rw))
+        return QR_ERR_ALIAS;
+    return QR_OK;
+}
+
+qr_status run_gemm(int bscale, const uint8_t *a, const float *sa, const uint8_t *b,
+                   const float *sb, int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype,
+                   void *ws, size_t ws_bytes, qr_stream stream)
+{
+    const int64_t sb_rows = bscale == qr::BSCALE_ROW ? N : cdiv(N, 128);
+    qr_status st = check_gemm(a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, bscale, sb_rows);
+    if (st != QR_OK || M == 0 || N == 0)
+        return st;
+    // K == 0 (empty contraction) runs the same kernel: no step executes and zeros are stored
+    const qr::GemmPlan plan = qr::plan_gemm(bscale, M, N, K);
+    return launch_status(qr::launch_gemm(bscale, y_dtype == QR_OUT_BF16, a, sa, b, sb, M, N, K, y,
+                                         ws, plan, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qr_status_string(qr_status status)
+{
+    switch (status) {
+    case QR_OK: return "QR_OK";
+    case QR_ERR_NULL: return "QR_ERR_NULL: a required pointer is NULL";
+    case QR_ERR_SHAPE: return "QR_ERR_SHAPE: a size is negative or violates the entry point's size rules";
+    case QR_ERR_ALIGN: return "QR_ERR_ALIGN: a pointer is not aligned as required";
+    case QR_ERR_ALIAS: return "QR_ERR_ALIAS: an output overlaps an input or another output";
+    case QR_ERR_WORKSPACE: return "QR_ERR_WORKSPACE: the workspace is smaller than required";
+    case QR_ERR_LAUNCH: return "QR_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case QR_ERR_ARG: return "QR_ERR_ARG: an enumerated argument is out of range";
+    default: return "unknown qr_status";
+    }
+}
+
+int32_t qr_abi_version(void) { return kAbiVersion; }
+
+qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t *q_row, float *s_row, uint8_t *q_colT, float *s_colT,
+                             qr_stream stream)
+{
+    if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_colT == nullptr) != (s_colT == nullptr))
+        return QR_ERR_NULL;
+    const bool row = q_row != nullptr, col = q_colT != nullptr;
+    if (!row && !col)
+        return QR_ERR_NULL;
+    if (cols % 8 != 0 || ld_x % 8 != 0 || (rows > 0 && ld_x < cols) || (col && rows % 8 != 0))
+        return QR_ERR_SHAPE;
+    if (cdiv(rows, 128) > 65535)
+        return QR_ERR_SHAPE;
+    if (rows == 0 || cols == 0)
+        return QR_OK;
+    if (!x_bf16)
+        return QR_ERR_NULL;
+    if (misaligned(x_bf16, 16) || misaligned(q_row, 16) || misaligned(q_colT, 16) ||
+        misaligned(s_row, 4) || misaligned(s_colT, 4))
+        return QR_ERR_ALIGN;
+    const Range rx = span(x_bf16, strided_bytes(rows, cols, ld_x, 2));
+    const Range outs[4] = {span(q_row, rows * cols), span(s_row, rows * cdiv(cols, 128) * 4),
+                           span(q_colT, rows * cols), span(s_colT, cols * cdiv(rows, 128) * 4)};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], rx))
+            return QR_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j]))
+                return QR_ERR_ALIAS;
+    }
+    const int mode = (row ? qr::QMODE_ROW : 0) | (col ? qr::QMODE_COL : 0);
+    return launch_status(qr::launch_quant_tile(mode, static_cast<const uint16_t *>(x_bf16), rows,
+                                               cols, ld_x, q_row, s_row, q_colT, s_colT,
+                                               (hipStream_t)stream));
+}
+
+qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *q,
+                             float *s, uint8_t *qT, float *sT, qr_stream stream)
+{
+    if (n < 0 || k < 0 || n >= kMaxDim || k >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (!q || !s || (qT == nullptr) != (sT == nullptr))
+        return QR_ERR_NULL;
+    if (n % 8 != 0 || k % 8 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k))
+        return QR_ERR_SHAPE;
+    if (cdiv(n, 128) > 65535)
+        return QR_ERR_SHAPE;
+    if (n == 0 || k == 0)
+        return QR_OK;
+    if (!w_bf16)
+        return QR_ERR_NULL;
+    if (misaligned(w_bf16, 16) || misaligned(q, 16) || misaligned(qT, 16) || misaligned(s, 4) ||
+        misaligned(sT, 4))
+        return QR_ERR_ALIGN;
+    const int64_t nblk = cdiv(n, 128) * cdiv(k, 128);
+    const Range rw = span(w_bf16, strided_bytes(n, k, ld_w, 2));
+    const Range outs[4] = {span(q, n * k), span(s, nblk * 4), span(qT, n * k), span(sT, nblk * 4)};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], rw))
+            return QR_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j]))
+                return QR_ERR_ALIAS;
+    }
+    const int mode = qr::QMODE_BLK | (qT ? qr::QMODE_BLKT : 0);
+    return launch_status(qr::launch_quant_tile(mode, static_cast<const uint16_t *>(w_bf16), n, k,
+                                               ld_w, q, s, qT, sT, (hipStream_t)stream));
+}
+
+qr_status qr_gemm_fp8_bsfprop(const uint8_t *a, const float *sa, const uint8_t *b,
+                              const float *sb, int64_t M, int64_t N, int64_t K, void *y,
+                              qr_out_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                              qr_stream stream)
+{
+    return run_gemm(qr::BSCALE_BLOCK, a, sa, b, sb, M, N, K, y, (int32_t)y_dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+qr_status qr_gemm_fp8_bsdgrad(const uint8_t *dy, const float *sdy, const uint8_t *wT,
+                              const float *swT, int64_t M, int64_t N, int64_t K, void *dx,
+                              qr_out_dtype dx_dtype, void *workspace, size_t workspace_bytes,
+                              qr_stream stream)
+{
+    // dX[M, K] = dY[M, N] . W[N, K]: the FProp form with contraction N and B = W^T [K, N]
+    return run_gemm(qr::BSCALE_BLOCK, dy, sdy, wT, swT, M, K, N, dx, (int32_t)dx_dtype,
+                    workspace, workspace_bytes, stream);
+}
+
+qr_status qr_gemm_fp8_bswgrad(const uint8_t *dyT, const float *sdyT, const uint8_t *xT,
+                              const float *sxT, int64_t M, int64_t N, int64_t K, void *dw,
+                              qr_out_dtype dw_dtype, void *workspace, size_t workspace_bytes,
+                              qr_stream stream)
+{
+    // dW[N, K] = dY^T[N, M] . X[M, K]: the FProp form with contraction M, A = dY^T, B = X^T,
+    // and per-row B scales
+    return run_gemm(qr::BSCALE_ROW, dyT, sdyT, xT, sxT, N, K, M, dw, (int32_t)dw_dtype,
+                    workspace, workspace_bytes, stream);
+}
+
+size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || K >= kMaxDim || M >= kMaxDim || N >= kMaxDim)
+        return 0;
+    switch (kind) {
+    case QR_GEMM_FPROP:
+        return K % 128 || M == 0 || N == 0 || K == 0 ? 0 : qr::plan_gemm(qr::BSCALE_BLOCK, M, N, K).ws_bytes;
+    case QR_GEMM_DGRAD:
+        return N % 128 || M == 0 || K == 0 || N == 0 ? 0 : qr::plan_gemm(qr::BSCALE_BLOCK, M, K, N).ws_bytes;
+    case QR_GEMM_WGRAD:
+        return M % 128 || N == 0 || K == 0 || M == 0 ? 0 : qr::plan_gemm(qr::BSCALE_ROW, N, K, M).ws_bytes;
+    default:
+        return 0;
+    }
+}
+
+qr_status qr_uaq_fold(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, const float *s,
+                      void *w_out_bf16, float *gain_inout, qr_stream stream)
+{
+    if (n < 0 || k < 0 || n >= kMaxDim || k >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (k % 8 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k))
+        return QR_ERR_SHAPE;
+    if (n == 0 || k == 0)
+        return QR_OK;
+    if (!w_bf16 || !s || !w_out_bf16)
+        return QR_ERR_NULL;
+    if (misaligned(w_bf16, 16) || misaligned(w_out_bf16, 16) || misaligned(s, 16) ||
+        misaligned(gain_inout, 4))
+        return QR_ERR_ALIGN;
+    const bool inplace = w_out_bf16 == w_bf16;
+    const int64_t ld_out = inplace ? ld_w : k;
+    const Range rw = span(w_bf16, strided_bytes(n, k, ld_w, 2));
+    const Range ro = span(w_out_bf16, strided_bytes(n, k, ld_out, 2));
+    const Range rs = span(s, k * 4), rg = span(gain_inout, gain_inout ? k * 4 : 0);
+    if ((!inplace && overlap(ro, rw)) || overlap(ro, rs) || overlap(ro, rg) || overlap(rg, rw) ||
+        overlap(rg, rs))
+        return QR_ERR_ALIAS;
+    return launch_status(qr::launch_uaq_fold(static_cast<const uint16_t *>(w_bf16), n, k, ld_w, s,
+                                             static_cast<uint16_t *>(w_out_bf16), ld_out,
+                                             gain_inout, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,480 @@
+// Block-scaled FP8 GEMM for gfx950:  C[m, n] = sum_g sa[m, g] * sb(n, g) * P_g[m, n],
+// P_g[m, n] = sum_{k in group g} e4m3(A[m, k]) * e4m3(B[n, k]),  groups of 128 along K.
+//
+// This is the FProp form of the Jet-RL notes (arXiv 2601.14243v1), section on the
+// fine-grained GEMM quantization scheme: the activation is quantized 1x128 along K
+// (row-major, one scale per row and group) and the weight 128x128 ("column-major" for
+// Y = X W^T, i.e. W[N, K] with K contiguous; one scale per block).  DGrad is the same form on
+// the transposed weight copy; WGrad is the same form on the two token-grouped transposed
+// operands, where the B scale is per row of B (BSCALE_ROW) instead of per block.
+//
+// Design for CDNA4 (gfx950):
+//   * One K step = one scale group of 128: every 16x16 output sub-tile takes exactly one
+//     v_mfma_scale_f32_16x16x128_f8f6f4 (E8M0 scales fixed at 2^0, so the hardware block
+//     scaling is neutral) into a fresh fp32 partial, which is then promoted into the fp32
+//     accumulator with the group's scale product (one FMA per output per group).
+//   * The MFMA takes the B rows as its first operand and the A rows as its second, so each
+//     lane's four results are four consecutive n of one m: the A scale is one value per
+//     lane per sub-tile, and for per-block B scales the whole wave shares one B scale.
+//   * A and B tiles (K-contiguous, 128 bytes per row per step) are staged global ->
+//     registers -> LDS, double-buffered, with the 16-byte chunk index XOR-swizzled by
+//     (row & 7) so that both the 16-byte stores and the fragment reads are bank-conflict
+//     free.  The next step's global loads are issued before the current step's MFMAs.
+//   * Work-group ids are remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
+//     takes a contiguous run of tiles, which share A rows in its L2.
+//   * Skinny M (decode) uses small tiles and a deterministic split over K: partial sums go
+//     to a caller workspace and a second kernel adds them in a fixed order.
+#include "qr_device.h"
+#include "qr_internal.h"
+
+namespace qr {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 128;
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int THREADS = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;       // wave tile
+    static constexpr int IM = TM / 16, JN = TN / 16;       // 16x16 sub-tiles per wave
+    static constexpr int CA = BM * 8 / THREADS;            // 16-byte A chunks per thread
+    static constexpr int CB = BN * 8 / THREADS;            // 16-byte B chunks per thread
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+    static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "chunk split");
+    static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns lie in one 128-block");
+};
+
+struct GemmArgs {
+    const uint8_t *A;
+    const float *sa;
+    const uint8_t *B;
+    const float *sb;
+    void *C;            // output, or the fp32 workspace [split][M][N] when split > 1
+    int64_t M, N, K;
+    int nk;             // K / 128
+    int tilesM, tilesN;
+    int split, kgps;    // number of K splits, groups per split
+};
+
+#define QR_LDS __attribute__((address_space(3)))
+
+// Buffer descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-class GPUs.
+constexpr int kBufFlags = 0x00020000;
+
+// s_waitcnt vmcnt(0) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
+__device__ __forceinline__ void wait_vm0()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <class T, int BSCALE, bool OUT_BF16>
+__global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
+{
+    constexpr int NW = T::WM * T::WN;
+    constexpr int SLA = T::BM / 8, SLB = T::BN / 8;              // 1 KB slabs per stage
+    constexpr int SLA_W = (SLA + NW - 1) / NW, SLB_W = (SLB + NW - 1) / NW;
+    constexpr int SCA = (T::BM + 63) / 64;                         // 64-scale slabs
+    // B scales per stage: BN per-row values, or the tile's per-block values (one slab).
+    constexpr int SCB = BSCALE == BSCALE_ROW ? (T::BN + 63) / 64 : 1;
+    constexpr int SCA_W = (SCA + NW - 1) / NW, SCB_W = (SCB + NW - 1) / NW;
+    constexpr int NSB = BSCALE == BSCALE_ROW ? T::BN : 1;
+
+    // Two stages in distinct LDS objects (not one array indexed by a variable): the
+    // compiler's alias analysis then sees that reads of one stage do not depend on the
+    // direct-to-LDS loads in flight into the other, and does not wait for them.
+    __shared__ __attribute__((aligned(1024))) uint8_t smA0[T::BM * kGroup];
+    __shared__ __attribute__((aligned(1024))) uint8_t smA1[T::BM * kGroup];
+    __shared__ __attribute__((aligned(1024))) uint8_t smB0[T::BN * kGroup];
+    __shared__ __attribute__((aligned(1024))) uint8_t smB1[T::BN * kGroup];
+    __shared__ __attribute__((aligned(256))) float sSA0[SCA * 64];
+    __shared__ __attribute__((aligned(256))) float sSA1[SCA * 64];
+    __shared__ __attribute__((aligned(256))) float sSB0[SCB * 64];
+    __shared__ __attribute__((aligned(256))) float sSB1[SCB * 64];
+    (void)NSB;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index: uniform across the wave, so say so (buffer offsets and LDS bases must be
+    // scalar; otherwise the compiler serializes them lane by lane)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    const int lq = lane >> 4, lr = lane & 15;
+
+    // ---- which tile and K range
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0)
+        bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    const int tiles = g.tilesM * g.tilesN;
+    const int split = bid / tiles;
+    const int tile = bid - split * tiles;
+    const int tm = tile / g.tilesN, tn = tile - tm * g.tilesN;
+    const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
+    const int gb = split * g.kgps;
+    const int ge = min(g.nk, gb + g.kgps);
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int nk = g.nk;
+
+    // ---- direct-to-LDS buffer loads.  Each operand tile gets a buffer descriptor whose
+    // range ends at the last valid row, so rows past M or N read as zeros (hardware range
+    // check on the per-lane offset, which carries the whole offset) and feed only outputs
+    // that are never stored.  A wave's load instruction fills
+    // one 1 KB slab = 8 rows of 128 bytes; lane l lands at byte 16*l, i.e. row l/8, physical
+    // chunk l%8, which holds logical chunk (l%8) ^ (row & 7).
+    const int64_t rowsA = M - m0 < T::BM ? M - m0 : T::BM;
+    const int64_t rowsB = N - n0 < T::BN ? N - n0 : T::BN;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.A + m0 * K), 0, (int)(rowsA * K), kBufFlags);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.B + n0 * K), 0, (int)(rowsB * K), kBufFlags);
+    const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.sa + m0 * nk), 0, (int)(rowsA * nk * 4), kBufFlags);
+    // per-row B scales: rows n0.. of sb; per-block B scales: block rows n0/128.. of sb
+    const int64_t nblkN = (N + kGroup - 1) / kGroup;
+    const int64_t sbRow0 = BSCALE == BSCALE_ROW ? n0 : n0 / kGroup;
+    const int64_t sbRows = BSCALE == BSCALE_ROW ? rowsB
+                           : ((n0 + rowsB + kGroup - 1) / kGroup) - n0 / kGroup;
+    const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.sb + sbRow0 * nk), 0, (int)(sbRows * nk * 4), kBufFlags);
+    const uint32_t voffAB = (uint32_t)((lane >> 3) * K + (((lane & 7) ^ (lane >> 3)) << 4));
+    const uint32_t voffS = (uint32_t)(lane * nk * 4);
+    (void)nblkN;
+
+    auto issue = [&](int kg, uint8_t *dA, uint8_t *dB, float *dSA, float *dSB) {
+        const uint32_t k0 = (uint32_t)kg * kGroup;
+#pragma unroll
+        for (int i = 0; i < SLA_W; ++i) {
+            const int slab = wave + i * NW;
+            if (SLA % NW == 0 || slab < SLA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rA, (QR_LDS void *)(dA + slab * 1024), 16,
+                    voffAB + (uint32_t)(slab * 8 * K) + k0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < SLB_W; ++i) {
+            const int slab = wave + i * NW;
+            if (SLB % NW == 0 || slab < SLB)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rB, (QR_LDS void *)(dB + slab * 1024), 16,
+                    voffAB + (uint32_t)(slab * 8 * K) + k0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < SCA_W; ++i) {
+            const int slab = wave + i * NW;
+            if (slab < SCA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rSA, (QR_LDS void *)(dSA + slab * 64), 4,
+                    voffS + (uint32_t)(slab * 64 * nk * 4 + kg * 4), 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < SCB_W; ++i) {
+            const int slab = wave + i * NW;
+            if (slab < SCB)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rSB, (QR_LDS void *)(dSB + slab * 64), 4,
+                    voffS + (uint32_t)(slab * 64 * nk * 4 + kg * 4), 0, 0, 0);
+        }
+    };
+
+    v4f acc[T::IM][T::JN];
+#pragma unroll
+    for (int i = 0; i < T::IM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::JN; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment of a 16-row sub-tile starting at (uniform) row r0: lane (lq, lr) takes 32
+    // bytes of row r0 + lr, the logical chunks 2*lq and 2*lq+1.  Sub-tiles start on a multiple
+    // of 16 rows, so the swizzle (row & 7) = (lr & 7) and the per-lane byte offsets are the
+    // same for every sub-tile: only an immediate r0 * 128 changes.
+    const int fragLo = lr * kGroup + (((2 * lq) ^ (lr & 7)) << 4);
+    const int fragHi = lr * kGroup + (((2 * lq + 1) ^ (lr & 7)) << 4);
+    auto frag = [&](const uint8_t *tileBase, int r0) -> v8i {
+        const uint8_t *p = tileBase + r0 * kGroup;
+        const uint4 lo = *reinterpret_cast<const uint4 *>(p + fragLo);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(p + fragHi);
+        v8i f;
+        f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+        f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+        return f;
+    };
+
+    auto compute = [&](int kg, const uint8_t *tA, const uint8_t *tB, const float *tSA,
+                       const float *tSB) {
+        float sav[T::IM];
+#pragma unroll
+        for (int i = 0; i < T::IM; ++i)
+            sav[i] = tSA[wm * T::TM + i * 16 + lr];
+        float sbw = 0.0f;
+        float sbv[T::JN][4];
+        if (BSCALE == BSCALE_ROW) {
+#pragma unroll
+            for (int j = 0; j < T::JN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sbv[j][r] = tSB[wn * T::TN + j * 16 + 4 * lq + r];
+        } else {
+            // this wave's 128-column block within the tile (tile starts on a block boundary
+            // or lies inside one block)
+            sbw = tSB[T::BN >= 128 ? (wn * T::TN) / 128 : 0];
+        }
+        v8i bf[T::JN];
+#pragma unroll
+        for (int j = 0; j < T::JN; ++j)
+            bf[j] = frag(tB, wn * T::TN + j * 16);
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        // Software pipeline over units of PJ MFMAs (one M sub-tile, PJ N sub-tiles): the
+        // MFMAs of unit u share a scheduling region with the promotion FMAs of unit u-1, so
+        // the MFMA pipe and the VALU work side by side and only two units of partials
+        // (2 * PJ * 4 registers) are live.
+        constexpr int PJ = T::JN >= 2 ? 2 : 1;
+        constexpr int UPI = T::JN / PJ;                 // units per M sub-tile
+        v4f pbuf[2][PJ];   // partials of units u (slot u&1) and u-1; no copies between them
+        auto promote = [&](int u) {
+            const int i = u / UPI, j0 = (u % UPI) * PJ;
+            const float ci = sav[i] * sbw;
+#pragma unroll
+            for (int jj = 0; jj < PJ; ++jj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float c = BSCALE == BSCALE_ROW ? sav[i] * sbv[j0 + jj][r] : ci;
+                    acc[i][j0 + jj][r] = __builtin_fmaf(pbuf[u & 1][jj][r], c, acc[i][j0 + jj][r]);
+                }
+        };
+        v8i af;
+#pragma unroll
+        for (int u = 0; u < T::IM * UPI; ++u) {
+            const int i = u / UPI, j0 = (u % UPI) * PJ;
+            if (j0 == 0)
+                af = frag(tA, wm * T::TM + i * 16);
+#pragma unroll
+            for (int jj = 0; jj < PJ; ++jj)
+                pbuf[u & 1][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf[j0 + jj], af, zero, 0, 0, 0, 127, 0, 127);
+            if (u > 0)
+                promote(u - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        promote(T::IM * UPI - 1);
+    };
+
+    // ---- main loop: one 128-wide scale group per step, two LDS stages (unrolled by two so
+    // that each stage is a compile-time LDS object).
+    if (gb < ge)
+        issue(gb, smA0, smB0, sSA0, sSB0);
+    wait_vm0();
+    __syncthreads();
+    for (int kg = gb; kg < ge; kg += 2) {
+        if (kg + 1 < ge)
+            issue(kg + 1, smA1, smB1, sSA1, sSB1);
+        compute(kg, smA0, smB0, sSA0, sSB0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm0();
+        __syncthreads();
+        if (kg + 1 >= ge)
+            break;
+        if (kg + 2 < ge)
+            issue(kg + 2, smA0, smB0, sSA0, sSB0);
+        compute(kg + 1, smA1, smB1, sSA1, sSB1);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm0();
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds C[m][n..n+3] for each sub-tile
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < T::IM; ++i) {
+        const int64_t m = m0 + wm * T::TM + i * 16 + lr;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int j = 0; j < T::JN; ++j) {
+            const int64_t n = n0 + wn * T::TN + j * 16 + 4 * lq;
+            const v4f a = acc[i][j];
+            if (g.split > 1 || !OUT_BF16) {
+                float *c = reinterpret_cast<float *>(g.C) + (int64_t)split * M * N + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    *reinterpret_cast<float4 *>(c) = make_float4(a[0], a[1], a[2], a[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            c[r] = a[r];
+                }
+            } else {
+                uint16_t *c = reinterpret_cast<uint16_t *>(g.C) + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    uint2 o;
+                    o.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+                    o.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+                    *reinterpret_cast<uint2 *>(c) = o;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            c[r] = (uint16_t)f32_to_bf16(a[r]);
+                }
+            }
+        }
+    }
+}
+
+// Sum the split-K partials in split order (deterministic) and convert.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ ws, int64_t MN,
+                                                       int split, void *out)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if ((MN & 3) == 0) {
+        const int64_t n4 = MN >> 2;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+            float4 s = reinterpret_cast<const float4 *>(ws)[i];
+            for (int p = 1; p < split; ++p) {
+                const float4 v = reinterpret_cast<const float4 *>(ws + p * MN)[i];
+                s.x += v.x;
+                s.y += v.y;
+                s.z += v.z;
+                s.w += v.w;
+            }
+            if (OUT_BF16) {
+                uint2 o;
+                o.x = f32_to_bf16(s.x) | (f32_to_bf16(s.y) << 16);
+                o.y = f32_to_bf16(s.z) | (f32_to_bf16(s.w) << 16);
+                reinterpret_cast<uint2 *>(out)[i] = o;
+            } else {
+                reinterpret_cast<float4 *>(out)[i] = s;
+            }
+        }
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+            float s = ws[i];
+            for (int p = 1; p < split; ++p)
+                s += ws[p * MN + i];
+            if (OUT_BF16)
+                reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)f32_to_bf16(s);
+            else
+                reinterpret_cast<float *>(out)[i] = s;
+        }
+    }
+}
+
+// Tile configurations, indexed by GemmPlan::cfg.
+using CfgBig2 = TileCfg<256, 128, 4, 2>;   // prefill / training: 8 waves, 64x64 per wave
+using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
+using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
+using CfgM256 = TileCfg<256, 64, 4, 1>;    // decode, M <= 256 (and small-M remainder)
+
+enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3 };
+
+void tile_dims(int cfg, int &bm, int &bn)
+{
+    switch (cfg) {
+    case CFG_BIG: bm = CfgBig2::BM; bn = CfgBig2::BN; break;
+    case CFG_M64: bm = CfgM64::BM; bn = CfgM64::BN; break;
+    case CFG_M128: bm = CfgM128::BM; bn = CfgM128::BN; break;
+    default: bm = CfgM256::BM; bn = CfgM256::BN; break;
+    }
+}
+
+template <class T, int BSCALE, bool OUT_BF16>
+hipError_t launch_cfg(const GemmArgs &a, int blocks, hipStream_t stream)
+{
+    k_gemm<T, BSCALE, OUT_BF16><<<blocks, T::THREADS, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hipStream_t s)
+{
+    if (bscale == BSCALE_ROW)
+        return out_bf16 ? launch_cfg<T, BSCALE_ROW, true>(a, blocks, s)
+                        : launch_cfg<T, BSCALE_ROW, false>(a, blocks, s);
+    return out_bf16 ? launch_cfg<T, BSCALE_BLOCK, true>(a, blocks, s)
+                    : launch_cfg<T, BSCALE_BLOCK, false>(a, blocks, s);
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
+{
+    (void)bscale;
+    GemmPlan p;
+    if (M > 256)
+        p.cfg = CFG_BIG;
+    else if (M <= 64)
+        p.cfg = CFG_M64;
+    else if (M <= 128)
+        p.cfg = CFG_M128;
+    else
+        p.cfg = CFG_M256;
+    int bm, bn;
+    tile_dims(p.cfg, bm, bn);
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const int64_t nk = K / kGroup;
+    int64_t split = 1;
+    if (p.cfg != CFG_BIG && tiles > 0 && tiles < 512 && nk > 0) {
+        split = (512 + tiles - 1) / tiles;
+        const int64_t max_split = nk / 4 > 1 ? nk / 4 : 1;   // keep >= 4 groups per split
+        if (split > max_split)
+            split = max_split;
+        if (split > 16)
+            split = 16;
+        if (split < 1)
+            split = 1;
+        const int64_t kgps = (nk + split - 1) / split;
+        split = (nk + kgps - 1) / kgps;
+    }
+    p.split = (int)split;
+    p.ws_bytes = split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float *sa,
+                       const uint8_t *B, const float *sb, int64_t M, int64_t N, int64_t K,
+                       void *C, void *ws, const GemmPlan &plan, hipStream_t stream)
+{
+    int bm, bn;
+    tile_dims(plan.cfg, bm, bn);
+    GemmArgs a;
+    a.A = A;
+    a.sa = sa;
+    a.B = B;
+    a.sb = sb;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.nk = (int)(K / kGroup);
+    a.tilesM = (int)((M + bm - 1) / bm);
+    a.tilesN = (int)((N + bn - 1) / bn);
+    a.split = plan.split;
+    a.kgps = (a.nk + plan.split - 1) / plan.split;
+    a.C = plan.split > 1 ? ws : C;
+    const int blocks = a.tilesM * a.tilesN * plan.split;
+    hipError_t e;
+    switch (plan.cfg) {
+    case CFG_BIG: e = launch_t<CfgBig2>(bscale, out_bf16, a, blocks, stream); break;
+    case CFG_M64: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
+    case CFG_M128: e = launch_t<CfgM128>(bscale, out_bf16, a, blocks, stream); break;
+    default: e = launch_t<CfgM256>(bscale, out_bf16, a, blocks, stream); break;
+    }
+    if (e != hipSuccess || plan.split <= 1)
+        return e;
+    const int64_t MN = M * N;
+    int64_t rb = ((MN & 3) == 0 ? MN / 4 : MN + 255) / 256;
+    if (rb > 8192)
+        rb = 8192;
+    if (rb < 1)
+        rb = 1;
+    if (out_bf16)
+        k_splitk_reduce<true><<<(unsigned)rb, 256, 0, stream>>>((const float *)ws, MN, plan.split, C);
+    else
+        k_splitk_reduce<false><<<(unsigned)rb, 256, 0, stream>>>((const float *)ws, MN, plan.split, C);
+    return hipGetLastError();
+}
+
+}  // namespace qr

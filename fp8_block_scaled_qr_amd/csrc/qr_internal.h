@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qr {
+
+// Quantizer tile modes (bit flags).
+enum : int {
+    QMODE_ROW = 1,    // 1x128 row groups, codes in input layout
+    QMODE_COL = 2,    // 128x1 column groups, codes and scales stored transposed
+    QMODE_BLK = 4,    // 128x128 blocks, codes in input layout
+    QMODE_BLKT = 8,   // 128x128 blocks, transposed copy of codes and scales
+};
+
+// One pass over x [rows, cols] (ld_x) in 128x128 tiles.
+//   ROW:  q [rows, cols], s [rows, ceil(cols/128)]
+//   COL:  qT [cols, rows], sT [cols, ceil(rows/128)]
+//   BLK:  q [rows, cols], s [ceil(rows/128), ceil(cols/128)]
+//   BLKT: qT [cols, rows], sT [ceil(cols/128), ceil(rows/128)]
+hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t cols,
+                             int64_t ld_x, uint8_t *q, float *s, uint8_t *qT, float *sT,
+                             hipStream_t stream);
+
+hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                           const float *s, uint16_t *w_out, int64_t ld_out, float *gain,
+                           hipStream_t stream);
+
+// B-operand scale layouts of the block-scaled GEMM C[m, n] = sum_k A[m, k] B[n, k].
+enum : int {
+    BSCALE_BLOCK = 0,  // sb [ceil(N/128), K/128]: one scale per 128x128 block of B
+    BSCALE_ROW = 1,    // sb [N, K/128]: one scale per row of B and 128-group of K
+};
+
+struct GemmPlan {
+    int cfg;        // tile configuration index
+    int split;      // number of K splits (1 = none)
+    size_t ws_bytes;
+};
+
+GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K);
+
+// A [M, K] codes, sa [M, K/128]; B [N, K] codes, sb per `bscale`; C [M, N] (out_bf16 ? bf16 : f32).
+hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float *sa,
+                       const uint8_t *B, const float *sb, int64_t M, int64_t N, int64_t K,
+                       void *C, void *ws, const GemmPlan &plan, hipStream_t stream);
+
+}  // namespace qr

@@ -1,0 +1,181 @@
+/*
+ * qr.h -- C ABI of the MI355X (gfx950) fine-grained FP8 quantize-and-multiply library.
+ *
+ * The library implements the linear-layer hot path that the quantized-rollout RL methods
+ * share: 1x128 per-group quantization of activations and gradients, 128x128 per-block
+ * quantization of weights, the block-scaled FP8 GEMM in its FProp, DGrad and WGrad forms,
+ * and the one-time UAQ invariant-scale fold.
+ *
+ * Sources (the pages this library follows):
+ *   [JET]  "Jet-RL: Enabling On-Policy FP8 Reinforcement Learning with Unified Training and
+ *          Rollout Precision Flow" (arXiv 2601.14243v1) paper notes, section "fine-grained GEMM
+ *          quantization scheme" (the paper's Figure 6): all three GEMMs of a linear layer run
+ *          in FP8; weights are quantized per 128x128 block, activations and gradients per
+ *          1x128 group; FProp takes the activation 1x128 row-major and the weight 128x128
+ *          "column-major"; DGrad reuses the FProp configuration; WGrad takes its first operand
+ *          1x128 and its second 128x1, with the two quantizations fused; gradients travel
+ *          between operators in BF16 and are quantized only inside the kernels.  Section
+ *          "system implementation": weights are quantized to FP8 in the parameter-update
+ *          phase.
+ *   [QURL] "QuRL: Efficient Reinforcement Learning with Quantized Rollout" (ICLR 2026) paper
+ *          notes, section "key design 1: update-aware quantization (UAQ)": WX = (W/s)(sX) with
+ *          s > 1 applied per column of W and per row of the preceding activation, folded into
+ *          the norm gain once before RL training.
+ *
+ * Numeric conventions (the pages say only "FP8"; these are this library's readings):
+ *   - FP8 is OCP E4M3: bias 7, largest finite 448, S.1111.111 is NaN, no infinities,
+ *     subnormals m*2^-9.  Codes are stored one byte per element.
+ *   - A group's scale is s = RN32(amax / 448) (one binary32 division, amax exact).  The code
+ *     of x is E4M3(RN32(x / s)), round to nearest even, saturating at +-448, keeping the sign
+ *     of zero.  amax == 0 gives s == 0 and signed-zero codes.  A trailing partial group takes
+ *     amax over the elements present.
+ *   - Dequantized value = code value * group scale.  GEMMs accumulate in fp32 with the scale
+ *     product applied once per 128-element contraction group; outputs are fp32 or bf16
+ *     (round to nearest even).
+ *   - Inputs must be finite.  Non-finite input is not detected on the GPU; the results are
+ *     then undefined, but every access stays in bounds.
+ *
+ * Conventions of every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned and allocated by the caller; the library
+ *     allocates nothing and keeps no state between calls.  Tensors are row-major; bf16
+ *     tensors are passed as their 16-bit patterns.  Outputs are dense (leading dimension =
+ *     their column count); inputs may carry a leading dimension ld (elements).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the call
+ *     returns without synchronizing.  Device faults surface at the caller's next
+ *     synchronization, as usual in HIP.
+ *   - Arguments are validated on the host before any HIP call; a failed check returns a
+ *     status and launches nothing.  A size of zero returns QR_OK and launches nothing.
+ *   - Results are bitwise deterministic for a given shape (no atomics on any output path).
+ *   - Calls are thread-safe; calls that write the same buffers concurrently race.
+ */
+#ifndef QR_H
+#define QR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qr_status;
+enum {
+    QR_OK = 0,
+    QR_ERR_NULL = 1,        /* a required pointer is NULL, or no output was requested     */
+    QR_ERR_SHAPE = 2,       /* negative size, or a size rule of the entry point violated   */
+    QR_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                            */
+    QR_ERR_ALIAS = 4,       /* an output overlaps an input or another output               */
+    QR_ERR_WORKSPACE = 5,   /* workspace smaller than qr_gemm_workspace_bytes() requires   */
+    QR_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch                    */
+    QR_ERR_ARG = 7          /* an enumerated argument is out of range                      */
+};
+
+typedef enum { QR_OUT_F32 = 0, QR_OUT_BF16 = 1 } qr_out_dtype;
+
+typedef enum { QR_GEMM_FPROP = 0, QR_GEMM_DGRAD = 1, QR_GEMM_WGRAD = 2 } qr_gemm_kind;
+
+typedef void *qr_stream; /* hipStream_t */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qr_status_string(qr_status status);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t qr_abi_version(void);
+
+/*
+ * Activation / gradient quantization [JET].
+ *
+ * x: bf16 [rows, cols], leading dimension ld_x (elements, >= cols).
+ * Row-wise 1x128 groups (128 consecutive elements of a row; FProp's and DGrad's A operand):
+ *     q_row [rows, cols] codes, s_row [rows, ceil(cols/128)] fp32 scales.
+ * Column-wise 128x1 groups (128 consecutive rows of one column; WGrad's operands), stored
+ * transposed so that each group is contiguous:
+ *     q_colT [cols, rows] codes, s_colT [cols, ceil(rows/128)] fp32 scales.
+ * Either output pair may be NULL (both members NULL), but not both pairs.  Requesting both
+ * is the fused quantize-transpose: x is read once.
+ *
+ * Size rules: rows >= 0, cols >= 0; cols % 8 == 0 and ld_x % 8 == 0; when the column-wise
+ * pair is requested also rows % 8 == 0.  x, q_row, q_colT 16-byte aligned; scale pointers
+ * 4-byte aligned.  Outputs must not overlap x or each other.
+ */
+qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t *q_row, float *s_row, uint8_t *q_colT, float *s_colT,
+                             qr_stream stream);
+
+/*
+ * Weight quantization, 128x128 blocks [JET]; run once per weight update.
+ *
+ * w: bf16 [n, k] (n = output features, k = input features), leading dimension ld_w.
+ *     q [n, k] codes, s [ceil(n/128), ceil(k/128)] fp32 scales (block (i, j) covers rows
+ *     128i.., columns 128j..).
+ * Optional transposed copy for DGrad (both NULL or both non-NULL):
+ *     qT [k, n] with qT[c, r] = q[r, c], sT [ceil(k/128), ceil(n/128)] with sT[j, i] = s[i, j].
+ *
+ * Size rules: n, k >= 0; n % 8 == 0, k % 8 == 0, ld_w % 8 == 0.  Alignment and aliasing as
+ * for qr_quant_act_1x128.
+ */
+qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w,
+                             uint8_t *q, float *s, uint8_t *qT, float *sT, qr_stream stream);
+
+/*
+ * FProp [JET]:  Y[m, n] = sum_k deq(A)[m, k] * deq(W)[n, k].
+ *   a  [M, K] codes with sa [M, K/128]            (1x128 groups along K, from q_row)
+ *   b  [N, K] codes with sb [ceil(N/128), K/128]   (the 128x128-quantized weight W[N, K])
+ *   y  [M, N], fp32 or bf16 per y_dtype.
+ * Size rules: M, N >= 0; K % 128 == 0.  a, b, y 16-byte aligned.
+ * workspace: device scratch of at least qr_gemm_workspace_bytes(QR_GEMM_FPROP, M, N, K)
+ * bytes (may be NULL when that is 0); its contents on entry do not matter.
+ */
+qr_status qr_gemm_fp8_bsfprop(const uint8_t *a, const float *sa, const uint8_t *b,
+                              const float *sb, int64_t M, int64_t N, int64_t K, void *y,
+                              qr_out_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                              qr_stream stream);
+
+/*
+ * DGrad [JET]:  dX[m, k] = sum_n deq(dY)[m, n] * deq(W)[n, k]  (the FProp form on W^T).
+ *   dy  [M, N] codes with sdy [M, N/128]                  (1x128 groups along N, from q_row)
+ *   wT  [K, N] codes with swT [ceil(K/128), N/128]        (the transposed copy qT/sT of
+ *                                                          qr_quant_w_128x128 for W[N, K])
+ *   dx  [M, K], fp32 or bf16.
+ * Size rules: M, K >= 0; N % 128 == 0.  Workspace as for FProp (kind QR_GEMM_DGRAD).
+ */
+qr_status qr_gemm_fp8_bsdgrad(const uint8_t *dy, const float *sdy, const uint8_t *wT,
+                              const float *swT, int64_t M, int64_t N, int64_t K, void *dx,
+                              qr_out_dtype dx_dtype, void *workspace, size_t workspace_bytes,
+                              qr_stream stream);
+
+/*
+ * WGrad [JET]:  dW[n, k] = sum_m deq(dY)[m, n] * deq(X)[m, k], contraction over M tokens,
+ * both operands grouped 128 along the tokens (dY^T 1x128, X 128x1):
+ *   dyT [N, M] codes with sdyT [N, M/128]   (q_colT / s_colT of qr_quant_act_1x128 on dY)
+ *   xT  [K, M] codes with sxT  [K, M/128]   (q_colT / s_colT of qr_quant_act_1x128 on X)
+ *   dw  [N, K], fp32 or bf16.
+ * Size rules: N, K >= 0; M % 128 == 0.  Workspace as for FProp (kind QR_GEMM_WGRAD).
+ */
+qr_status qr_gemm_fp8_bswgrad(const uint8_t *dyT, const float *sdyT, const uint8_t *xT,
+                              const float *sxT, int64_t M, int64_t N, int64_t K, void *dw,
+                              qr_out_dtype dw_dtype, void *workspace, size_t workspace_bytes,
+                              qr_stream stream);
+
+/* Workspace bytes the GEMM entry point of `kind` needs for these sizes (0 if none).  The
+ * sizes are the ones passed to that entry point.  Returns 0 for invalid arguments. */
+size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K);
+
+/*
+ * UAQ fold [QURL]:  w_out[n, c] = RN_bf16(w[n, c] / s[c])  (the exact quotient rounded once
+ * to bf16, nearest even) and, if gain_inout != NULL, gain_inout[c] = RN32(gain_inout[c] * s[c]).
+ *   w      bf16 [n, k], leading dimension ld_w; w_out may equal w (in place, same ld_w),
+ *          otherwise w_out is dense [n, k] and must not overlap w.
+ *   s      fp32 [k], every s[c] finite and > 0 (not checked on the GPU).
+ *   gain   fp32 [k] or NULL: the gain of the norm that feeds this layer.
+ * Run once, before training; the fold is NOT idempotent (a second call divides by s again).
+ * Size rules: n, k >= 0; k % 8 == 0, ld_w % 8 == 0; w, w_out 16-byte aligned.
+ */
+qr_status qr_uaq_fold(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, const float *s,
+                      void *w_out_bf16, float *gain_inout, qr_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QR_H */

@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header declares,
+and rejects invalid arguments with the documented status before any HIP call.  Only argument
+combinations that fail validation (or have a zero size, which launches nothing) are used, so
+no kernel is ever launched here; the pointers are fake and never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_block_scaled_qr_amd as qr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, LAUNCH, ARG = range(8)
+
+A = 1 << 40          # fake, 16-byte aligned device addresses far apart
+B = 2 << 40
+C = 3 << 40
+D = 4 << 40
+E = 5 << 40
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qr.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qr_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qr.load()
+
+
+def test_exports_match_header(L):
+    declared = header_functions()
+    assert len(declared) == 9, declared
+    out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
+    assert exported == declared
+    assert sorted(qr.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings_and_version(L):
+    assert qr.abi_version() == 1
+    for st in range(8):
+        assert qr.status_string(st)
+    assert "unknown" in qr.status_string(99)
+
+
+def act(L, x, rows, cols, ld, q, s, qT, sT):
+    return L.qr_quant_act_1x128(x, rows, cols, ld, q, s, qT, sT, None)
+
+
+def test_quant_act_validation(L):
+    assert act(L, A, -1, 128, 128, B, C, None, None) == SHAPE
+    assert act(L, A, 4, 100, 104, B, C, None, None) == SHAPE          # cols % 8
+    assert act(L, A, 4, 128, 100, B, C, None, None) == SHAPE          # ld < cols
+    assert act(L, A, 4, 128, 132, B, C, None, None) == SHAPE          # ld % 8
+    assert act(L, A, 12, 128, 128, None, None, B, C) == SHAPE         # column pass: rows % 8
+    assert act(L, A, 4, 128, 128, None, None, None, None) == NULL     # no output
+    assert act(L, A, 4, 128, 128, B, None, None, None) == NULL        # half a pair
+    assert act(L, None, 4, 128, 128, B, C, None, None) == NULL
+    assert act(L, A + 2, 8, 128, 128, B, C, None, None) == ALIGN
+    assert act(L, A, 8, 128, 128, B + 8, C, None, None) == ALIGN
+    assert act(L, A, 8, 128, 128, B, C + 2, None, None) == ALIGN
+    assert act(L, A, 8, 128, 128, A + 16, C, None, None) == ALIAS     # codes inside x
+    assert act(L, A, 8, 128, 128, B, B + 512, None, None) == ALIAS    # scales inside codes
+    assert act(L, A, 8, 128, 128, B, C, B + 512, D) == ALIAS          # colT over row codes
+    assert act(L, A, 0, 128, 128, B, C, None, None) == OK             # empty: nothing launched
+    assert act(L, A, 8, 0, 0, B, C, D, E) == OK
+    assert act(L, A, 128 * 65536, 8, 8, B, C, None, None) == SHAPE   # row tiles beyond grid
+
+
+def test_quant_w_validation(L):
+    f = L.qr_quant_w_128x128
+    assert f(A, 128, 128, 128, None, C, None, None, None) == NULL
+    assert f(A, 128, 128, 128, B, C, D, None, None) == NULL          # half of the T pair
+    assert f(A, 100, 128, 128, B, C, None, None, None) == SHAPE       # n % 8
+    assert f(A, 128, 124, 128, B, C, None, None, None) == SHAPE       # k % 8
+    assert f(A + 8, 128, 128, 128, B, C, None, None, None) == ALIGN
+    assert f(A, 128, 128, 128, B, A, None, None, None) == ALIAS
+    assert f(A, 128, 128, 128, B, C, B + 64, D, None) == ALIAS
+    assert f(A, 0, 128, 128, B, C, None, None, None) == OK
+
+
+def gemm(L, name, a, sa, b, sb, M, N, K, y, dt, ws, wsb):
+    return getattr(L, name)(a, sa, b, sb, M, N, K, y, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name", ["qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad",
+                                  "qr_gemm_fp8_bswgrad"])
+def test_gemm_validation(L, name):
+    # the contraction size is K for FProp, N for DGrad, M for WGrad
+    contraction = {"qr_gemm_fp8_bsfprop": 2, "qr_gemm_fp8_bsdgrad": 1, "qr_gemm_fp8_bswgrad": 0}[name]
+    dims = [512, 512, 512]
+    bad = list(dims)
+    bad[contraction] = 200
+    assert gemm(L, name, A, B, C, D, *bad, E, 1, None, 0) == SHAPE
+    assert gemm(L, name, A, B, C, D, -1, 512, 512, E, 1, None, 0) == SHAPE
+    assert gemm(L, name, A, B, C, D, *dims, E, 7, None, 0) == ARG
+    assert gemm(L, name, None, B, C, D, *dims, E, 1, None, 0) == NULL
+    assert gemm(L, name, A, B, C, D, *dims, None, 1, None, 0) == NULL
+    assert gemm(L, name, A + 4, B, C, D, *dims, E, 1, None, 0) == ALIGN
+    assert gemm(L, name, A, B + 2, C, D, *dims, E, 1, None, 0) == ALIGN
+    assert gemm(L, name, A, B, C, D, *dims, A + 64, 1, None, 0) == ALIAS    # output over A
+    assert gemm(L, name, A, B, C, D, *dims, C, 0, None, 0) == ALIAS         # output over B
+    z = list(dims)
+    z[[0, 1, 2][contraction - 1]] = 0                                         # an output dim 0
+    assert gemm(L, name, A, B, C, D, *z, E, 1, None, 0) == OK
+
+
+def test_gemm_workspace(L):
+    # skinny decode shapes split K and need a workspace; large shapes need none
+    nb = qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 4096)
+    assert nb > 0 and nb % (64 * 14336 * 4) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 8192, 4096, 4096) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 100) == 0     # invalid K
+    assert qr.qr_gemm_workspace_bytes(9, 64, 14336, 4096) == 0
+    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 64, 14336, 4096, E, 1, None, 0) == WORKSPACE
+    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 64, 14336, 4096, E, 1, 6 << 40, nb - 1) == WORKSPACE
+    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 64, 14336, 4096, E, 1, A, nb) == ALIAS
+    # DGrad / WGrad sizes are passed as given to their entry points
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_DGRAD, 64, 4096, 14336) > 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_WGRAD, 8192, 4096, 4096) == 0
+
+
+def test_uaq_validation(L):
+    f = L.qr_uaq_fold
+    assert f(A, 4, 100, 104, B, C, None, None) == SHAPE                # k % 8
+    assert f(A, 4, 128, 120, B, C, None, None) == SHAPE                # ld < k
+    assert f(None, 4, 128, 128, B, C, None, None) == NULL
+    assert f(A, 4, 128, 128, None, C, None, None) == NULL
+    assert f(A, 4, 128, 128, B + 4, C, None, None) == ALIGN            # s is read as float4
+    assert f(A, 4, 128, 128, B, A + 256, None, None) == ALIAS          # partial overlap
+    assert f(A, 4, 128, 128, B, C, B, None) == ALIAS                   # gain over s
+    assert f(A, 0, 128, 128, B, C, D, None) == OK

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP library through its C ABI against the reference oracle.
+
+Codes and scales must match bit for bit; GEMM outputs must satisfy
+|gpu - oracle| <= 2e-3 * sum_k |a_k b_k| per element against the unrounded fp64 oracle.
+Small cases compare every element; the full-size workloads compare the quantizers in full and
+the GEMMs on sampled outputs that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_qr_amd as qr
+import oracle
+import qr_synth
+from gpu_util import (assert_bitexact, assert_gemm_close, dev, dev_bf16, host, out_f64,
+                      sample_positions)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qr.load()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ================================================================= quantizers
+
+ACT_SHAPES = [(256, 512, "tiny_fprop X"), (77, 200, "ragged rows and partial group"),
+              (1, 8, "one row, 8 columns"), (300, 1096, "ragged both"),
+              (8192, 4096, "prefill_8b X full size")]
+
+
+@pytest.mark.parametrize("rows,cols,name", ACT_SHAPES)
+def test_quant_rows(rows, cols, name):
+    say("quant_rows", rows, cols, name)
+    x = qr_synth.normal_bf16(rows * 7 + cols, (rows, cols), 1.0, 99, max(1, cols // 100))
+    q, s, _, _ = qr.quant_act(dev_bf16(x), row=True, col=False)
+    rq, rs = oracle.quant_rows(x)
+    assert_bitexact(host(q), rq, "codes")
+    assert_bitexact(host(s), rs, "scales")
+
+
+DUAL_SHAPES = [(256, 512, "small"), (200, 136, "ragged rows and columns"), (8, 8, "minimal"),
+               (8192, 4096, "backward_8b dY full size")]
+
+
+@pytest.mark.parametrize("rows,cols,name", DUAL_SHAPES)
+def test_quant_dual_and_colT(rows, cols, name):
+    say("quant dual", rows, cols, name)
+    std = 1e-3 if rows == 8192 else 1.0
+    x = (qr_synth.backward_8b_dy() if rows == 8192 else
+         qr_synth.normal_bf16(rows + cols, (rows, cols), std, 5, 2))
+    xd = dev_bf16(x)
+    q, s, qT, sT = qr.quant_act(xd, row=True, col=True)
+    rq, rs = oracle.quant_rows(x)
+    rqT, rsT = oracle.quant_cols_T(x)
+    assert_bitexact(host(q), rq, "row codes")
+    assert_bitexact(host(s), rs, "row scales")
+    assert_bitexact(host(qT), rqT, "colT codes")
+    assert_bitexact(host(sT), rsT, "colT scales")
+    # column-only pass (X's WGrad operand) gives the same column outputs
+    _, _, qT2, sT2 = qr.quant_act(xd, row=False, col=True)
+    assert_bitexact(host(qT2), rqT, "colT-only codes")
+    assert_bitexact(host(sT2), rsT, "colT-only scales")
+
+
+W_SHAPES = [(512, 512, "tiny_fprop W"), (200, 136, "ragged blocks"),
+            (4096, 4096, "prefill_8b W"), (14336, 4096, "decode_8b W")]
+
+
+@pytest.mark.parametrize("n,k,name", W_SHAPES)
+def test_quant_w(n, k, name):
+    say("quant_w", n, k, name)
+    w = qr_synth.normal_bf16(n + 3 * k, (n, k), 0.02)
+    q, s, qT, sT = qr.quant_w(dev_bf16(w), transposed=True)
+    rq, rs = oracle.quant_blocks(w)
+    assert_bitexact(host(q), rq, "codes")
+    assert_bitexact(host(s), rs, "scales")
+    assert_bitexact(host(qT), np.ascontiguousarray(rq.T), "transposed codes")
+    assert_bitexact(host(sT), np.ascontiguousarray(rs.T), "transposed scales")
+
+
+def test_quant_strided_input():
+    say("quant strided ld")
+    big = qr_synth.normal_bf16(11, (96, 640), 1.0)
+    xd = dev_bf16(big)[:, 64:64 + 384]          # ld = 640, cols = 384
+    q, s, qT, sT = qr.quant_act(xd, row=True, col=True)
+    sub = np.ascontiguousarray(big[:, 64:448])
+    rq, rs = oracle.quant_rows(sub)
+    rqT, rsT = oracle.quant_cols_T(sub)
+    assert_bitexact(host(q), rq, "codes")
+    assert_bitexact(host(s), rs, "scales")
+    assert_bitexact(host(qT), rqT, "colT codes")
+    assert_bitexact(host(sT), rsT, "colT scales")
+
+
+def _groups_for_amax(amax_bits_list):
+    """Rows of 128 bf16: first element the group amax, then every bf16 x with |x| <= amax."""
+    allb = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    allv = qr_synth.bf16_bits_to_f32(allb)
+    finite = np.isfinite(allv)
+    rows = []
+    for ab in amax_bits_list:
+        a = qr_synth.bf16_bits_to_f32(np.array([ab], np.uint16))[0]
+        xs = allb[finite & (np.abs(allv) <= a)]
+        pad = (-xs.size) % 127
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        r = np.empty((xs.shape[0], 128), np.uint16)
+        r[:, 0] = ab
+        r[:, 1:] = xs
+        rows.append(r)
+    return np.concatenate(rows)
+
+
+def test_codes_every_bf16_for_sampled_scales():
+    """Every bf16 x against 1/97 of all finite bf16 amax values (subnormal, normal, huge) and
+    hand-picked ones: exercises the exact quotient, saturation, the sign of zero and every
+    E4M3 rounding boundary of the hardware conversion."""
+    say("exhaustive-x codes")
+    picks = list(range(1, 0x7F80, 97)) + [0x0001, 0x0080, 0x3F80, 0x43E0, 0x7F7F, 0x3B12]
+    x = _groups_for_amax(np.array(picks, np.uint16))
+    for r0 in range(0, x.shape[0], 1 << 19):
+        part = np.ascontiguousarray(x[r0:r0 + (1 << 19)])
+        q, s, _, _ = qr.quant_act(dev_bf16(part), row=True)
+        rq, rs = oracle.quant_rows(part)
+        assert_bitexact(host(s), rs, "scales")
+        assert_bitexact(host(q), rq, "codes")
+
+
+def test_quant_special_values():
+    say("special values")
+    x = np.zeros((16, 256), np.uint16)
+    x[1, :] = 0x8000                                   # all negative zero
+    x[2, :128] = 0x3F80                                # all equal
+    x[3, 5] = 0x0001                                   # subnormal amax, rest zero
+    x[3, 6] = 0x8001
+    x[4, :] = qr_synth.f32_to_bf16_bits(np.linspace(-448, 448, 256).astype(np.float32))
+    x[5, :] = qr_synth.f32_to_bf16_bits(np.full(256, 3.0e38, np.float32))
+    x[6, ::2] = 0x7F7F                                 # max finite bf16 and its negative
+    x[6, 1::2] = 0xFF7F
+    x[7, :] = qr_synth.f32_to_bf16_bits((np.arange(256) - 128).astype(np.float32) * 2.0 ** -130)
+    q, s, qT, sT = qr.quant_act(dev_bf16(x), row=True, col=True)
+    rq, rs = oracle.quant_rows(x)
+    rqT, rsT = oracle.quant_cols_T(x)
+    assert_bitexact(host(q), rq, "codes")
+    assert_bitexact(host(s), rs, "scales")
+    assert_bitexact(host(qT), rqT, "colT codes")
+    assert_bitexact(host(sT), rsT, "colT scales")
+    w = np.ascontiguousarray(np.tile(x, (8, 1))[:128])
+    qw, sw, _, _ = qr.quant_w(dev_bf16(w))
+    rqw, rsw = oracle.quant_blocks(w)
+    assert_bitexact(host(qw), rqw, "block codes")
+    assert_bitexact(host(sw), rsw, "block scales")
+
+
+# ================================================================= UAQ fold
+
+def test_uaq_fold_random_and_near_midpoints():
+    say("uaq fold")
+    rng = np.random.default_rng(5)
+    w = qr_synth.normal_bf16(61, (64, 256), 0.02)
+    s = rng.uniform(1.5, 4.0, 256).astype(np.float32)
+    # near-midpoint scales: s = RN32(|w| / mid) for a bf16 midpoint below |w| / 1.5
+    wv = qr_synth.bf16_bits_to_f32(w[0]).astype(np.float64)
+    for c in range(0, 256, 2):
+        tgt = abs(wv[c]) / rng.uniform(1.5, 4.0)
+        e = np.floor(np.log2(tgt))
+        ulp = 2.0 ** (e - 7)
+        s[c] = np.float32(abs(wv[c]) / ((np.floor(tgt / ulp) + 0.5) * ulp))
+    gain = rng.uniform(0.5, 2.0, 256).astype(np.float32)
+    wd, sd, gd = dev_bf16(w), dev(s), dev(gain.copy())
+    out = qr.uaq_fold(wd, sd, gd)
+    ro, rg = oracle.uaq_fold(w, s, gain)
+    assert_bitexact(host(out), ro, "folded weight")
+    assert_bitexact(host(gd), rg, "gain")
+    # in place, no gain
+    qr.uaq_fold(wd, sd, None, inplace=True)
+    assert_bitexact(host(wd), ro, "folded weight in place")
+
+
+# ================================================================= GEMMs
+
+def _fprop_case(lin, x, w, out_dtype, sample=None, name=""):
+    say("fprop", lin.M if lin else x.shape, name)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    qa, sa, _, _ = qr.quant_act(xd, row=True)
+    qw, sw, _, _ = qr.quant_w(wd)
+    y = qr.gemm_fprop(qa, sa, qw, sw, out_dtype=out_dtype)
+    ra, rsa = oracle.quant_rows(x)
+    rw, rsw = oracle.quant_blocks(w)
+    assert_bitexact(host(qa), ra, "A codes")
+    assert_bitexact(host(qw), rw, "W codes")
+    yg = out_f64(y)
+    bf = out_dtype == qr.QR_OUT_BF16
+    if sample is None:
+        Y, S = oracle.fprop(ra, rsa, rw, rsw)
+        return assert_gemm_close(yg, Y, S, name, bf)
+    mi, ni = sample
+    Y, S = oracle.fprop(ra, rsa, rw, rsw, sample=(mi, ni))
+    return assert_gemm_close(yg[mi, ni], Y, S, name, bf)
+
+
+def test_fprop_tiny_fp32_full():
+    lin = qr_synth.tiny_fprop()
+    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_F32, name="tiny_fprop"))
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 200, 384), (1, 128, 128), (300, 264, 256),
+                                   (129, 1000, 640), (64, 512, 1024), (256, 384, 2048),
+                                   (520, 136, 384)])
+@pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
+def test_fprop_shapes_full(M, N, K, out):
+    x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 7, max(1, K // 100))
+    w = qr_synth.normal_bf16(M * N + K, (N, K), 0.02)
+    print(_fprop_case(None, x, w, out, name=f"{M}x{N}x{K}"))
+
+
+def test_fprop_decode_8b_sampled():
+    lin = qr_synth.decode_8b()
+    smp = sample_positions(lin.M, lin.N, 4096, 1)
+    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, smp, "decode_8b"))
+
+
+def test_fprop_prefill_8b_sampled():
+    lin = qr_synth.prefill_8b()
+    smp = sample_positions(lin.M, lin.N, 4096, 2)
+    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, smp, "prefill_8b"))
+
+
+def test_fprop_empty_and_zero_k():
+    say("fprop empty / K=0")
+    a = torch.zeros((4, 0), dtype=torch.uint8, device="cuda")
+    y = torch.full((4, 8), 7.0, device="cuda")
+    qr.qr_gemm_fp8_bsfprop(a, torch.zeros(4, device="cuda"), a, torch.zeros(1, device="cuda"),
+                           4, 8, 0, y, qr.QR_OUT_F32)
+    assert float(y.abs().max()) == 0.0
+    qr.qr_gemm_fp8_bsfprop(None, None, None, None, 0, 8, 128, y, qr.QR_OUT_F32)   # M = 0
+    torch.cuda.synchronize()
+
+
+def _backward_operands():
+    lin = qr_synth.prefill_8b()
+    x, w, dy = lin.x(), lin.w(), qr_synth.backward_8b_dy()
+    return x, w, dy
+
+
+def test_backward_8b_dgrad_wgrad_sampled():
+    say("backward_8b")
+    x, w, dy = _backward_operands()
+    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    qdy, sdy, qdyT, sdyT = qr.quant_act(dyd, row=True, col=True)
+    _, _, qxT, sxT = qr.quant_act(xd, row=False, col=True)
+    _, _, qwT, swT = qr.quant_w(wd, transposed=True)
+    dx = qr.gemm_dgrad(qdy, sdy, qwT, swT)
+    dw = qr.gemm_wgrad(qdyT, sdyT, qxT, sxT)
+    rdy, rsdy = oracle.quant_rows(dy)
+    rdyT, rsdyT = oracle.quant_cols_T(dy)
+    rxT, rsxT = oracle.quant_cols_T(x)
+    rw, rsw = oracle.quant_blocks(w)
+    assert_bitexact(host(qwT), np.ascontiguousarray(rw.T), "W^T codes")
+    assert_bitexact(host(qxT), rxT, "X^T codes")
+    smp = sample_positions(8192, 4096, 4096, 3)
+    Y, S = oracle.dgrad(rdy, rsdy, rw, rsw, sample=smp)
+    print("dgrad", assert_gemm_close(out_f64(dx)[smp], Y, S, "dgrad", True))
+    smp = sample_positions(4096, 4096, 4096, 4)
+    Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT, sample=smp)
+    print("wgrad", assert_gemm_close(out_f64(dw)[smp], Y, S, "wgrad", True))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (384, 200, 384), (128, 77, 1024),
+                                   (1024, 136, 512)])
+def test_dgrad_wgrad_small_full(M, N, K):
+    """Full comparison on small backward shapes: M tokens, N output features, K inputs."""
+    say("dgrad/wgrad small", M, N, K)
+    x = qr_synth.normal_bf16(M + K, (M, K), 1.0, 3, 2)
+    dy = qr_synth.normal_bf16(M + N + 1, (M, N), 1e-3)
+    n_pad = ((N + 127) // 128) * 128 if N % 128 else N
+    # DGrad contracts over N: pad N to whole groups with zero gradient columns and weights
+    dy_p = np.zeros((M, n_pad), np.uint16)
+    dy_p[:, :N] = dy
+    w = np.zeros((n_pad, K), np.uint16)
+    w[:N] = qr_synth.normal_bf16(N * K, (N, K), 0.02)
+    qdy, sdy, qdyT, sdyT = qr.quant_act(dev_bf16(dy_p), row=True, col=True)
+    _, _, qxT, sxT = qr.quant_act(dev_bf16(x), row=False, col=True)
+    _, _, qwT, swT = qr.quant_w(dev_bf16(w), transposed=True)
+    for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
+        dx = qr.gemm_dgrad(qdy, sdy, qwT, swT, out_dtype=out)
+        rdy, rsdy = oracle.quant_rows(dy_p)
+        rw, rsw = oracle.quant_blocks(w)
+        Y, S = oracle.dgrad(rdy, rsdy, rw, rsw)
+        assert_gemm_close(out_f64(dx), Y, S, "dgrad", out == qr.QR_OUT_BF16)
+        dw = qr.gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=out)
+        rdyT, rsdyT = oracle.quant_cols_T(dy_p)
+        rxT, rsxT = oracle.quant_cols_T(x)
+        Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT)
+        assert_gemm_close(out_f64(dw), Y, S, "wgrad", out == qr.QR_OUT_BF16)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_decode_32b_set_sampled(idx):
+    lin = qr_synth.decode_32b_set()[idx]
+    say("decode_32b", lin.name, lin.M, lin.N, lin.K)
+    w, s, x = lin.w(), lin.uaq_s(), lin.x()
+    wd = dev_bf16(w)
+    wf = qr.uaq_fold(wd, dev(s))
+    rwf, _ = oracle.uaq_fold(w, s)
+    assert_bitexact(host(wf), rwf, "folded W")
+    del wd
+    smp = sample_positions(lin.M, lin.N, 4096, 10 + idx)
+    print(_fprop_case(lin, x, rwf, qr.QR_OUT_BF16, smp, lin.name))
+
+
+def test_gemm_deterministic():
+    say("determinism")
+    lin = qr_synth.decode_8b()
+    x, w = lin.x(), lin.w()
+    qa, sa, _, _ = qr.quant_act(dev_bf16(x), row=True)
+    qw, sw, _, _ = qr.quant_w(dev_bf16(w))
+    y1 = host(qr.gemm_fprop(qa, sa, qw, sw))
+    y2 = host(qr.gemm_fprop(qa, sa, qw, sw))
+    assert np.array_equal(y1, y2)

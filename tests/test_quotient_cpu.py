@@ -1,0 +1,31 @@
+"""The GPU quantizers' per-element quotient algorithm, replayed on the host for every
+(bf16 amax, bf16 x) pair (see quotient_check.c).  CPU only."""
+import os
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _has_fma():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return " fma " in f.read()
+    except OSError:
+        return False
+
+
+def test_quotient_matches_ieee_division_for_every_bf16_pair(tmp_path):
+    exe = str(tmp_path / "quotient_check")
+    cmd = ["gcc", "-O0", "-ffp-contract=off", "-fopenmp", os.path.join(HERE, "quotient_check.c"),
+           "-o", exe, "-lm"]
+    if _has_fma():
+        cmd.insert(3, "-mfma")
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    print(r.stdout)
+    fields = dict(zip(r.stdout.split()[0::2], map(int, r.stdout.split()[1::2])))
+    assert fields["pairs"] == 1065402240          # every finite (amax, x) with |x| <= amax
+    assert fields["mismatches"] == 0, r.stdout
+    assert r.returncode == 0
