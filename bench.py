@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X FP8 quantize-and-multiply path (one GPU).
+
+One step is one pass of the whole linear-layer path over one batch of seeded synthetic
+input, at the 8B-layer shapes (hidden 4096, 8192 tokens; decode FFN 14336 at batch 64):
+
+  uaq_fold        W [4096, 4096] / s (per input column), gain * s        (one-time op; timed)
+  quant_w         128x128 blocks of the folded W, plus the transposed copy for DGrad
+  quant_x         1x128 groups of X [8192, 4096]  (X is the norm output carrying s)
+  fprop           Y = X W^T            8192 x 4096 x 4096, bf16 out
+  quant_dy_dual   1x128 rows and 128x1 columns (transposed) of dY [8192, 4096], one read
+  quant_x_col     128x1 columns (transposed) of X
+  dgrad           dX = dY W            8192 x 4096 x 4096, bf16 out
+  wgrad           dW = dY^T X          4096 x 4096 x 8192, bf16 out
+  quant_x_dec     1x128 groups of the decode activation X [64, 4096]
+  fprop_decode    Y = X W^T            64 x 14336 x 4096 on the pre-quantized weight, bf16 out
+
+Every op's launches are bracketed with HIP events on the stream they run on.  The JSON line
+reports the step's GEMM throughput (all GEMM flops / step time) as `value`, each op's time
+with its roofline fraction, the roofline of the dominant kernel, and the CPU oracle timed on
+a bounded token slice of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak) + quantize GB/s (% HBM)"
+
+T, H, F, MD = 8192, 4096, 14336, 64     # tokens, hidden, decode FFN width, decode batch
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(m, n, k):
+    return 2.0 * m * n * k
+
+
+def op_table():
+    """Algorithmic work of each op: ('mfma', flops) or ('hbm', bytes), minimum traffic."""
+    g = 128
+    return {
+        # read W bf16 + s + gain, write W' bf16 + gain
+        "uaq_fold": ("hbm", H * H * 2 * 2 + H * 4 * 3),
+        # read bf16, write codes twice + scales twice
+        "quant_w": ("hbm", H * H * 2 + 2 * H * H + 2 * (H // g) ** 2 * 4),
+        "quant_x": ("hbm", T * H * 2 + T * H + T * (H // g) * 4),
+        "fprop": ("mfma", gemm_flops(T, H, H)),
+        "quant_dy_dual": ("hbm", T * H * 2 + 2 * T * H + 2 * T * (H // g) * 4),
+        "quant_x_col": ("hbm", T * H * 2 + T * H + H * (T // g) * 4),
+        "dgrad": ("mfma", gemm_flops(T, H, H)),
+        "wgrad": ("mfma", gemm_flops(H, H, T)),
+        "quant_x_dec": ("hbm", MD * H * 2 + MD * H + MD * (H // g) * 4),
+        # decode is bound by streaming the weight: codes + block scales + A + Y
+        "fprop_decode": ("hbm", F * H + (F // g) * (H // g) * 4 + MD * H + MD * (H // g) * 4
+                         + MD * F * 2),
+    }
+
+
+def decode_flops():
+    return gemm_flops(MD, F, H)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "quant.hip", "qr_device.h", "api.cpp"):
+        with open(os.path.join(ROOT, "fp8_block_scaled_qr_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel)
+    if not e or e.get("source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ GPU part
+
+class Step:
+    def __init__(self, torch, qr):
+        import qr_synth
+        self.torch, self.qr = torch, qr
+        dev = "cuda:0"
+        t0 = time.time()
+        s = qr_synth.uniform_f32(3011, H, 1.5, 4.0)
+        x = qr_synth.normal_bf16(3001, (T, H), 1.0, 3003, qr_synth.n_outliers(H), col_scale=s)
+        w = qr_synth.normal_bf16(3002, (H, H), 0.02)
+        dy = qr_synth.backward_8b_dy()
+        dec = qr_synth.decode_8b()
+        xd, wd = dec.x(), dec.w()
+        log(f"inputs generated in {time.time() - t0:.1f}s")
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        u8, f32 = torch.uint8, torch.float32
+        self.X, self.W, self.dY, self.Xd = bf(x), bf(w), bf(dy), bf(xd)
+        self.s = torch.from_numpy(s).to(dev)
+        self.gain = torch.ones(H, dtype=f32, device=dev)
+        e = lambda *sh, dt=u8: torch.empty(sh, dtype=dt, device=dev)
+        g = 128
+        self.Wf = torch.empty_like(self.W)
+        self.qW, self.sW, self.qWT, self.sWT = e(H, H), e(H // g, H // g, dt=f32), e(H, H), e(H // g, H // g, dt=f32)
+        self.qX, self.sX = e(T, H), e(T, H // g, dt=f32)
+        self.Y = e(T, H, dt=torch.bfloat16)
+        self.qdY, self.sdY, self.qdYT, self.sdYT = e(T, H), e(T, H // g, dt=f32), e(H, T), e(H, T // g, dt=f32)
+        self.qXT, self.sXT = e(H, T), e(H, T // g, dt=f32)
+        self.dX, self.dW = e(T, H, dt=torch.bfloat16), e(H, H, dt=torch.bfloat16)
+        self.qXd, self.sXd = e(MD, H), e(MD, H // g, dt=f32)
+        self.Yd = e(MD, F, dt=torch.bfloat16)
+        # the decode weight is quantized once, outside the step (weights change per update)
+        Wd = bf(wd)
+        self.qWd, self.sWd = e(F, H), e(F // g, H // g, dt=f32)
+        qr.qr_quant_w_128x128(Wd, F, H, H, self.qWd, self.sWd, None, None)
+        del Wd
+        self.ws = {}
+        for kind, (M, N, K) in (("fprop", (T, H, H)), ("dgrad", (T, H, H)), ("wgrad", (T, H, H)),
+                                ("decode", (MD, F, H))):
+            code = {"fprop": 0, "dgrad": 1, "wgrad": 2, "decode": 0}[kind]
+            nb = qr.qr_gemm_workspace_bytes(code, M, N, K)
+            self.ws[kind] = (e(nb) if nb else None, nb)
+        torch.cuda.synchronize()
+
+    def ops(self):
+        qr, BF = self.qr, self.qr.QR_OUT_BF16
+        return [
+            ("uaq_fold", lambda: qr.qr_uaq_fold(self.W, H, H, H, self.s, self.Wf, self.gain)),
+            ("quant_w", lambda: qr.qr_quant_w_128x128(self.Wf, H, H, H, self.qW, self.sW, self.qWT, self.sWT)),
+            ("quant_x", lambda: qr.qr_quant_act_1x128(self.X, T, H, H, self.qX, self.sX, None, None)),
+            ("fprop", lambda: qr.qr_gemm_fp8_bsfprop(self.qX, self.sX, self.qW, self.sW, T, H, H, self.Y, BF,
+                                                     *self.ws["fprop"])),
+            ("quant_dy_dual", lambda: qr.qr_quant_act_1x128(self.dY, T, H, H, self.qdY, self.sdY, self.qdYT,
+                                                            self.sdYT)),
+            ("quant_x_col", lambda: qr.qr_quant_act_1x128(self.X, T, H, H, None, None, self.qXT, self.sXT)),
+            ("dgrad", lambda: qr.qr_gemm_fp8_bsdgrad(self.qdY, self.sdY, self.qWT, self.sWT, T, H, H, self.dX, BF,
+                                                     *self.ws["dgrad"])),
+            ("wgrad", lambda: qr.qr_gemm_fp8_bswgrad(self.qdYT, self.sdYT, self.qXT, self.sXT, T, H, H, self.dW, BF,
+                                                     *self.ws["wgrad"])),
+            ("quant_x_dec", lambda: qr.qr_quant_act_1x128(self.Xd, MD, H, H, self.qXd, self.sXd, None, None)),
+            ("fprop_decode", lambda: qr.qr_gemm_fp8_bsfprop(self.qXd, self.sXd, self.qWd, self.sWd, MD, F, H,
+                                                            self.Yd, BF, *self.ws["decode"])),
+        ]
+
+
+def run_gpu(args):
+    import torch
+    import fp8_block_scaled_qr_amd as qr
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (MI355X)")
+    qr.load()
+    torch.cuda.set_device(0)
+    st = Step(torch, qr)
+    ops = st.ops()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for _, f in ops:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        for (name, f), (a, b) in zip(ops, ev[k]):
+            a.record(stream)
+            f()
+            b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(end) / args.steps
+    per_op = {}
+    for i, (name, _) in enumerate(ops):
+        per_op[name] = float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]))
+    return step_ms, wall, per_op
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def run_cpu_baseline(tokens):
+    """The oracle (plain C, fp64 products) on a token slice of the same step: the fold and
+    quantization of the full weight, the activation/gradient quantizers and all four GEMMs
+    restricted to `tokens` tokens (WGrad contracts over them; the decode GEMM keeps 64 rows
+    x 1/8 of the FFN outputs)."""
+    import oracle
+    import qr_synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    s = qr_synth.uniform_f32(3011, H, 1.5, 4.0)
+    x = qr_synth.normal_bf16(3001, (T, H), 1.0, 3003, qr_synth.n_outliers(H), col_scale=s)[:tokens]
+    w = qr_synth.normal_bf16(3002, (H, H), 0.02)
+    dy = qr_synth.backward_8b_dy()[:tokens]
+    dec = qr_synth.decode_8b()
+    xd, wd = dec.x(), dec.w()[: F // 8]
+    oracle.lib()
+    t0 = time.perf_counter()
+    wf, _ = oracle.uaq_fold(w, s, np.ones(H, np.float32))
+    qw, sw = oracle.quant_blocks(wf)
+    qx, sx = oracle.quant_rows(x)
+    oracle.fprop(qx, sx, qw, sw)
+    qd, sd = oracle.quant_rows(dy)
+    qdT, sdT = oracle.quant_cols_T(dy)
+    qxT, sxT = oracle.quant_cols_T(x)
+    oracle.dgrad(qd, sd, qw, sw)
+    oracle.wgrad(qdT, sdT, qxT, sxT)
+    qxd, sxd = oracle.quant_rows(xd)
+    qwd, swd = oracle.quant_blocks(wd)
+    oracle.fprop(qxd, sxd, qwd, swd)
+    dt = time.perf_counter() - t0
+    flops = 3 * gemm_flops(tokens, H, H) + gemm_flops(MD, F // 8, H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": (f"the full step's ops on a {tokens}-token slice (fold + 128x128 quantize of "
+                       f"the full 4096x4096 W, 1x128/128x1 quantizers of X and dY[:{tokens}], "
+                       f"FProp/DGrad/WGrad over {tokens} tokens, decode FProp 64 x {F // 8} x {H} "
+                       f"incl. quantizing that weight slice); value = the slice's GEMM flops / "
+                       f"oracle wall time")}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    step_ms, wall, per_op = run_gpu(args)
+    table = op_table()
+    kernels = {}
+    for name, ms in per_op.items():
+        bound, work = table[name]
+        if bound == "mfma":
+            ach = work / (ms * 1e-3) / 1e12
+            kernels[name] = {"us": round(ms * 1e3, 2), "bound": "mfma", "achieved": round(ach, 1),
+                             "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4)}
+        else:
+            ach = work / (ms * 1e-3) / 1e9
+            kernels[name] = {"us": round(ms * 1e3, 2), "bound": "hbm", "achieved": round(ach, 1),
+                             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    gemm_total = 3 * gemm_flops(T, H, H) + decode_flops()
+    value = gemm_total / (step_ms * 1e-3) / 1e12
+    dom = max(per_op, key=lambda k: per_op[k])
+    kd = kernels[dom]
+    roof = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"],
+            "peak": PEAK_FP8_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS,
+            "unit": kd["unit"], "frac": kd["frac"], "avg_launch_us": kd["us"],
+            "traffic": measured_traffic(dom)}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded; 8B-layer shapes)",
+        "config": {"workload": ("8B-layer FP8 step: UAQ fold + 128x128 W quantize (4096x4096), "
+                                "1x128 X quantize + FProp 8192x4096x4096, fused dual dY "
+                                "quantize-transpose + X 128x1, DGrad and WGrad (8192 tokens), "
+                                "decode FProp 64x14336x4096"),
+                   "tokens": T, "hidden": H, "decode_batch": MD, "decode_ffn": F,
+                   "gemm_gflop_per_step": round(gemm_total / 1e9, 2)},
+        "roofline": roof,
+        "kernels": kernels,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = run_cpu_baseline(args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,6 +44,8 @@ struct TileCfg {
     static constexpr int IM = TM / 16, JN = TN / 16;       // 16x16 sub-tiles per wave
     static constexpr int CA = BM * 8 / THREADS;            // 16-byte A chunks per thread
     static constexpr int CB = BN * 8 / THREADS;            // 16-byte B chunks per thread
+    static_assert((BM / 8) % (WM * WN) == 0 && (BN / 8) % (WM * WN) == 0,
+                  "whole 16-row x 4-chunk load units per wave");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
     static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "chunk split");
     static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns lie in one 128-block");
@@ -61,45 +63,38 @@ struct GemmArgs {
     int split, kgps;    // number of K splits, groups per split
 };
 
-#define QR_LDS __attribute__((address_space(3)))
-
 // Buffer descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-class GPUs.
 constexpr int kBufFlags = 0x00020000;
 
-// s_waitcnt vmcnt(0) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
-__device__ __forceinline__ void wait_vm0()
+// Workgroup barrier for the LDS stage ring, without the memory fence of __syncthreads():
+// that fence would also wait for the next steps' global loads still in flight.  Ordering is
+// explicit: each wave waits for its own LDS accesses (lgkmcnt(0)) so that the stage it wrote
+// is complete and no wave refills a stage another wave still reads; the empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void stage_barrier()
 {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained (gfx9)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <class T, int BSCALE, bool OUT_BF16>
 __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 {
-    constexpr int NW = T::WM * T::WN;
-    constexpr int SLA = T::BM / 8, SLB = T::BN / 8;              // 1 KB slabs per stage
-    constexpr int SLA_W = (SLA + NW - 1) / NW, SLB_W = (SLB + NW - 1) / NW;
-    constexpr int SCA = (T::BM + 63) / 64;                         // 64-scale slabs
-    // B scales per stage: BN per-row values, or the tile's per-block values (one slab).
-    constexpr int SCB = BSCALE == BSCALE_ROW ? (T::BN + 63) / 64 : 1;
-    constexpr int SCA_W = (SCA + NW - 1) / NW, SCB_W = (SCB + NW - 1) / NW;
-    constexpr int NSB = BSCALE == BSCALE_ROW ? T::BN : 1;
+    // Scales staged per step: BM row scales of A, then BN row scales (per-row B scales) or
+    // the tile's per-block B scales.
+    constexpr int NSB = BSCALE == BSCALE_ROW ? T::BN : (T::BN >= kGroup ? T::BN / kGroup : 1);
+    static_assert(T::BM + NSB <= T::THREADS, "one scale per thread per step");
 
-    // Two stages in distinct LDS objects (not one array indexed by a variable): the
-    // compiler's alias analysis then sees that reads of one stage do not depend on the
-    // direct-to-LDS loads in flight into the other, and does not wait for them.
-    __shared__ __attribute__((aligned(1024))) uint8_t smA0[T::BM * kGroup];
-    __shared__ __attribute__((aligned(1024))) uint8_t smA1[T::BM * kGroup];
-    __shared__ __attribute__((aligned(1024))) uint8_t smB0[T::BN * kGroup];
-    __shared__ __attribute__((aligned(1024))) uint8_t smB1[T::BN * kGroup];
-    __shared__ __attribute__((aligned(256))) float sSA0[SCA * 64];
-    __shared__ __attribute__((aligned(256))) float sSA1[SCA * 64];
-    __shared__ __attribute__((aligned(256))) float sSB0[SCB * 64];
-    __shared__ __attribute__((aligned(256))) float sSB1[SCB * 64];
-    (void)NSB;
+    // Two LDS stages per operand.  One scale slot per thread and stage: [0, BM) A row scales,
+    // [BM, BM + NSB) B scales, the rest unused.
+    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][T::BM * kGroup];
+    __shared__ __attribute__((aligned(1024))) uint8_t smB[2][T::BN * kGroup];
+    __shared__ __attribute__((aligned(16))) float sS[2][T::THREADS];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave index: uniform across the wave, so say so (buffer offsets and LDS bases must be
-    // scalar; otherwise the compiler serializes them lane by lane)
+    // wave index: uniform across the wave, so say so (scalar offsets stay scalar)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / T::WN, wn = wave % T::WN;
     const int lq = lane >> 4, lr = lane & 15;
@@ -119,12 +114,24 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const int64_t M = g.M, N = g.N, K = g.K;
     const int nk = g.nk;
 
-    // ---- direct-to-LDS buffer loads.  Each operand tile gets a buffer descriptor whose
-    // range ends at the last valid row, so rows past M or N read as zeros (hardware range
-    // check on the per-lane offset, which carries the whole offset) and feed only outputs
-    // that are never stored.  A wave's load instruction fills
-    // one 1 KB slab = 8 rows of 128 bytes; lane l lands at byte 16*l, i.e. row l/8, physical
-    // chunk l%8, which holds logical chunk (l%8) ^ (row & 7).
+    // ---- LDS layout, fragment-major: a 16-row sub-tile (16 rows x 128 bytes) is stored as
+    // the two 1 KB halves of its MFMA operand fragment.  Lane l of the fragment holds row
+    // l % 16, bytes 32 * (l / 16) .. +32; half h keeps bytes 16h .. 16h+15 of that, at
+    // offset h * 1024 + 16 * l.  A fragment read is then two linear 1 KB reads (the fastest
+    // LDS read pattern on gfx950: ~1.3x a conflict-free swizzled row-major layout), and the
+    // scatter moves to the 16-byte stores, whose rate does not depend on the pattern.
+    // Row r, 16-byte chunk c goes to sub-tile r / 16, half c % 2, lane (r % 16) + 16 * (c / 2).
+    auto lds_off = [](int row, int c) -> int {
+        return (row >> 4) * 2048 + (c & 1) * 1024 + (((row & 15) + 16 * (c >> 1)) << 4);
+    };
+    //
+    // ---- global loads: buffer loads into registers.  Each operand tile gets a buffer
+    // descriptor whose range ends at its last valid row, so rows past M or N read as zeros
+    // (hardware range check on the per-lane offset, which carries the whole offset) and
+    // feed only outputs that are never stored.  Thread t loads 16-byte chunks
+    // c = t + i * THREADS: row c / 8, logical chunk c % 8, so 8 consecutive threads read one
+    // 128-byte row segment.  (Direct-to-LDS loads measured about 3x slower than this on gfx950
+    // for this access pattern.)
     const int64_t rowsA = M - m0 < T::BM ? M - m0 : T::BM;
     const int64_t rowsB = N - n0 < T::BN ? N - n0 : T::BN;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
@@ -134,49 +141,61 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(g.sa + m0 * nk), 0, (int)(rowsA * nk * 4), kBufFlags);
     // per-row B scales: rows n0.. of sb; per-block B scales: block rows n0/128.. of sb
-    const int64_t nblkN = (N + kGroup - 1) / kGroup;
     const int64_t sbRow0 = BSCALE == BSCALE_ROW ? n0 : n0 / kGroup;
     const int64_t sbRows = BSCALE == BSCALE_ROW ? rowsB
                            : ((n0 + rowsB + kGroup - 1) / kGroup) - n0 / kGroup;
     const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(g.sb + sbRow0 * nk), 0, (int)(sbRows * nk * 4), kBufFlags);
-    const uint32_t voffAB = (uint32_t)((lane >> 3) * K + (((lane & 7) ^ (lane >> 3)) << 4));
-    const uint32_t voffS = (uint32_t)(lane * nk * 4);
-    (void)nblkN;
 
-    auto issue = [&](int kg, uint8_t *dA, uint8_t *dB, float *dSA, float *dSB) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 ra[T::CA], rb[T::CB];
+    float rs = 0.0f;
+    // scale loaders: threads [0, BM) load A's row scales (whole waves, BM % 64 == 0), the
+    // others B scales (index clamped into [0, NSB): the extra lanes fill unused slots).  The
+    // descriptor choice is wave-uniform, so every lane loads without branching.
+    static_assert(T::BM % 64 == 0, "A-scale loaders are whole waves");
+    const bool wavesA = wave < T::BM / 64;
+    const __amdgpu_buffer_rsrc_t rS = wavesA ? rSA : rSB;
+    const int sidx = wavesA ? tid : min(tid - T::BM, NSB - 1);
+    const uint32_t soff = (uint32_t)(sidx * nk * 4);
+
+    // Per-step data movement in slots: slot j < CA + CB is one 16-byte chunk per lane of A or
+    // B, slot CA + CB is the thread's scale.  One slot of a wave covers 16 rows x 4 chunks:
+    // wave instruction u (u = wave + j * waves) takes rows 16 * (u / 2) + lane % 16 and
+    // chunks 4 * (u % 2) + lane / 16, so each row reads 64 contiguous bytes from memory and
+    // each 16-lane group stores 16 different rows, i.e. 16 distinct LDS bank groups in the
+    // fragment-major layout.  load_slot fills the slot's register from global memory for
+    // step kg; store_slot writes it to the LDS stage (dA, dB, dS).
+    constexpr int NSLOT = T::CA + T::CB + 1;
+    constexpr int NW = T::WM * T::WN;
+    const int lrow = lane & 15, lchunk = lane >> 4;
+    auto slot_row = [&](int u) { return 16 * (u >> 1) + lrow; };
+    auto slot_chunk = [&](int u) { return 4 * (u & 1) + lchunk; };
+    // Branch-free on purpose: straight-line code lets the scheduler interleave the slots with
+    // the MFMAs and lets the compiler track each load's wait exactly.
+    auto load_slot = [&](int j, int kg) {
         const uint32_t k0 = (uint32_t)kg * kGroup;
-#pragma unroll
-        for (int i = 0; i < SLA_W; ++i) {
-            const int slab = wave + i * NW;
-            if (SLA % NW == 0 || slab < SLA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rA, (QR_LDS void *)(dA + slab * 1024), 16,
-                    voffAB + (uint32_t)(slab * 8 * K) + k0, 0, 0, 0);
+        if (j < T::CA) {
+            const int u = wave + j * NW;
+            ra[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rA, (uint32_t)(slot_row(u) * K + (slot_chunk(u) << 4)) + k0, 0, 0);
+        } else if (j < T::CA + T::CB) {
+            const int u = wave + (j - T::CA) * NW;
+            rb[j - T::CA] = __builtin_amdgcn_raw_buffer_load_b128(
+                rB, (uint32_t)(slot_row(u) * K + (slot_chunk(u) << 4)) + k0, 0, 0);
+        } else {
+            rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, soff + kg * 4, 0, 0));
         }
-#pragma unroll
-        for (int i = 0; i < SLB_W; ++i) {
-            const int slab = wave + i * NW;
-            if (SLB % NW == 0 || slab < SLB)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rB, (QR_LDS void *)(dB + slab * 1024), 16,
-                    voffAB + (uint32_t)(slab * 8 * K) + k0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < SCA_W; ++i) {
-            const int slab = wave + i * NW;
-            if (slab < SCA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rSA, (QR_LDS void *)(dSA + slab * 64), 4,
-                    voffS + (uint32_t)(slab * 64 * nk * 4 + kg * 4), 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < SCB_W; ++i) {
-            const int slab = wave + i * NW;
-            if (slab < SCB)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rSB, (QR_LDS void *)(dSB + slab * 64), 4,
-                    voffS + (uint32_t)(slab * 64 * nk * 4 + kg * 4), 0, 0, 0);
+    };
+    auto store_slot = [&](int j, uint8_t *dA, uint8_t *dB, float *dS) {
+        if (j < T::CA) {
+            const int u = wave + j * NW;
+            *reinterpret_cast<u32x4 *>(dA + lds_off(slot_row(u), slot_chunk(u))) = ra[j];
+        } else if (j < T::CA + T::CB) {
+            const int u = wave + (j - T::CA) * NW;
+            *reinterpret_cast<u32x4 *>(dB + lds_off(slot_row(u), slot_chunk(u))) = rb[j - T::CA];
+        } else {
+            dS[tid] = rs;
         }
     };
 
@@ -187,24 +206,24 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         for (int j = 0; j < T::JN; ++j)
             acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Fragment of a 16-row sub-tile starting at (uniform) row r0: lane (lq, lr) takes 32
-    // bytes of row r0 + lr, the logical chunks 2*lq and 2*lq+1.  Sub-tiles start on a multiple
-    // of 16 rows, so the swizzle (row & 7) = (lr & 7) and the per-lane byte offsets are the
-    // same for every sub-tile: only an immediate r0 * 128 changes.
-    const int fragLo = lr * kGroup + (((2 * lq) ^ (lr & 7)) << 4);
-    const int fragHi = lr * kGroup + (((2 * lq + 1) ^ (lr & 7)) << 4);
+    // Operand fragment of the 16-row sub-tile starting at (uniform) row r0.
     auto frag = [&](const uint8_t *tileBase, int r0) -> v8i {
-        const uint8_t *p = tileBase + r0 * kGroup;
-        const uint4 lo = *reinterpret_cast<const uint4 *>(p + fragLo);
-        const uint4 hi = *reinterpret_cast<const uint4 *>(p + fragHi);
+        const uint8_t *p = tileBase + (r0 >> 4) * 2048 + lane * 16;
+        const uint4 lo = *reinterpret_cast<const uint4 *>(p);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(p + 1024);
         v8i f;
         f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
         f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
         return f;
     };
 
-    auto compute = [&](int kg, const uint8_t *tA, const uint8_t *tB, const float *tSA,
-                       const float *tSB) {
+    // compute(stage) also moves data: between its MFMAs it writes the registers (step k+1,
+    // loaded one step earlier) into the other stage and then refills each register with step
+    // k+2, so LDS stores and global loads overlap the MFMA pipe instead of bunching up at
+    // the barrier.
+    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS, uint8_t *nA,
+                       uint8_t *nB, float *nS, int kld) {
+        const float *tSA = tS, *tSB = tS + T::BM;
         float sav[T::IM];
 #pragma unroll
         for (int i = 0; i < T::IM; ++i)
@@ -218,72 +237,86 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
                 for (int r = 0; r < 4; ++r)
                     sbv[j][r] = tSB[wn * T::TN + j * 16 + 4 * lq + r];
         } else {
-            // this wave's 128-column block within the tile (tile starts on a block boundary
-            // or lies inside one block)
-            sbw = tSB[T::BN >= 128 ? (wn * T::TN) / 128 : 0];
+            // this wave's 128-column block within the tile (the tile starts on a block
+            // boundary or lies inside one block)
+            sbw = tSB[T::BN >= kGroup ? (wn * T::TN) / kGroup : 0];
         }
         v8i bf[T::JN];
 #pragma unroll
         for (int j = 0; j < T::JN; ++j)
             bf[j] = frag(tB, wn * T::TN + j * 16);
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        // Software pipeline over units of PJ MFMAs (one M sub-tile, PJ N sub-tiles): the
-        // MFMAs of unit u share a scheduling region with the promotion FMAs of unit u-1, so
-        // the MFMA pipe and the VALU work side by side and only two units of partials
-        // (2 * PJ * 4 registers) are live.
-        constexpr int PJ = T::JN >= 2 ? 2 : 1;
-        constexpr int UPI = T::JN / PJ;                 // units per M sub-tile
-        v4f pbuf[2][PJ];   // partials of units u (slot u&1) and u-1; no copies between them
+        // Software pipeline over single MFMAs (one M sub-tile x one N sub-tile): the MFMA of
+        // unit u shares a scheduling region with the promotion FMAs of unit u-1, so the MFMA
+        // pipe and the VALU work side by side and only two partials are live.
+        v4f pbuf[2];
         auto promote = [&](int u) {
-            const int i = u / UPI, j0 = (u % UPI) * PJ;
+            const int i = u / T::JN, j = u % T::JN;
             const float ci = sav[i] * sbw;
 #pragma unroll
-            for (int jj = 0; jj < PJ; ++jj)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float c = BSCALE == BSCALE_ROW ? sav[i] * sbv[j0 + jj][r] : ci;
-                    acc[i][j0 + jj][r] = __builtin_fmaf(pbuf[u & 1][jj][r], c, acc[i][j0 + jj][r]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float c = BSCALE == BSCALE_ROW ? sav[i] * sbv[j][r] : ci;
+                acc[i][j][r] = __builtin_fmaf(pbuf[u & 1][r], c, acc[i][j][r]);
+            }
         };
-        v8i af;
+        // A fragments double-buffered: sub-tile i+1's fragment is read from LDS while
+        // sub-tile i's MFMAs run, so the LDS latency stays hidden.
+        v8i afb[2];
+        afb[0] = frag(tA, wm * T::TM);
 #pragma unroll
-        for (int u = 0; u < T::IM * UPI; ++u) {
-            const int i = u / UPI, j0 = (u % UPI) * PJ;
-            if (j0 == 0)
-                af = frag(tA, wm * T::TM + i * 16);
-#pragma unroll
-            for (int jj = 0; jj < PJ; ++jj)
-                pbuf[u & 1][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bf[j0 + jj], af, zero, 0, 0, 0, 127, 0, 127);
+        for (int u = 0; u < T::IM * T::JN; ++u) {
+            const int i = u / T::JN, j = u % T::JN;
+            if (j == 0 && i + 1 < T::IM)
+                afb[(i + 1) & 1] = frag(tA, wm * T::TM + (i + 1) * 16);
+            pbuf[u & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], afb[i & 1], zero,
+                                                                          0, 0, 0, 127, 0, 127);
             if (u > 0)
                 promote(u - 1);
+            // data movement, spread over the units: store slot u, then reload it
+            if (u < NSLOT) {
+                store_slot(u, nA, nB, nS);
+                load_slot(u, kld);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        promote(T::IM * UPI - 1);
+        promote(T::IM * T::JN - 1);
+#pragma unroll
+        for (int j = T::IM * T::JN; j < NSLOT; ++j) {
+            store_slot(j, nA, nB, nS);
+            load_slot(j, kld);
+        }
     };
 
-    // ---- main loop: one 128-wide scale group per step, two LDS stages (unrolled by two so
-    // that each stage is a compile-time LDS object).
-    if (gb < ge)
-        issue(gb, smA0, smB0, sSA0, sSB0);
-    wait_vm0();
-    __syncthreads();
-    for (int kg = gb; kg < ge; kg += 2) {
-        if (kg + 1 < ge)
-            issue(kg + 1, smA1, smB1, sSA1, sSB1);
-        compute(kg, smA0, smB0, sSA0, sSB0);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm0();
-        __syncthreads();
-        if (kg + 1 >= ge)
-            break;
-        if (kg + 2 < ge)
-            issue(kg + 2, smA0, smB0, sSA0, sSB0);
-        compute(kg + 1, smA1, smB1, sSA1, sSB1);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm0();
-        __syncthreads();
+    // ---- main loop: one 128-wide scale group per step, two LDS stages and one register
+    // stage.  Step k computes from LDS stage k%2 while it stores step k+1 (already in
+    // registers) into the other stage and loads step k+2 into the registers; the loads stay
+    // in flight across the (fence-free) barrier.  Near the end of the K range the stores and
+    // loads still run, unconditionally: loads re-read the last group (the index is clamped)
+    // and stores fill a stage that is never read again.  The loop is not unrolled: one copy
+    // of the step keeps every accumulator in the same registers from step to step.
+    const int glast = ge - 1;
+    if (gb < ge) {
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j)
+            load_slot(j, gb);
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j)
+            store_slot(j, smA[0], smB[0], sS[0]);
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j)
+            load_slot(j, min(gb + 1, glast));
     }
+    stage_barrier();
+#pragma nounroll
+    for (int kg = gb; kg < ge; ++kg) {
+        const int st = (kg - gb) & 1;
+        compute(smA[st], smB[st], sS[st], smA[st ^ 1], smB[st ^ 1], sS[st ^ 1],
+                min(kg + 2, glast));
+        stage_barrier();
+    }
+    // the loads issued for steps past the end are discarded; let them land before the
+    // registers are reused and the wave ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // ---- epilogue: lane holds C[m][n..n+3] for each sub-tile
     const bool vec_ok = (N & 3) == 0;
@@ -367,7 +400,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 using CfgBig2 = TileCfg<256, 128, 4, 2>;   // prefill / training: 8 waves, 64x64 per wave
 using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
 using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
-using CfgM256 = TileCfg<256, 64, 4, 1>;    // decode, M <= 256 (and small-M remainder)
+using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
 
 enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3 };
 
