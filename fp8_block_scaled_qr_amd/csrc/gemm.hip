@@ -398,16 +398,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 
 // Tile configurations, indexed by GemmPlan::cfg.
 using CfgBig2 = TileCfg<256, 128, 4, 2>;   // prefill / training: 8 waves, 64x64 per wave
+using CfgBig4 = TileCfg<256, 256, 2, 4>;   // prefill / training: 8 waves, 128x64 per wave
 using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
 using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
 using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
 
-enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3 };
+enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4 };
 
 void tile_dims(int cfg, int &bm, int &bn)
 {
     switch (cfg) {
     case CFG_BIG: bm = CfgBig2::BM; bn = CfgBig2::BN; break;
+    case CFG_BIG4: bm = CfgBig4::BM; bn = CfgBig4::BN; break;
     case CFG_M64: bm = CfgM64::BM; bn = CfgM64::BN; break;
     case CFG_M128: bm = CfgM128::BM; bn = CfgM128::BN; break;
     default: bm = CfgM256::BM; bn = CfgM256::BN; break;
@@ -435,10 +437,12 @@ hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hi
 
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
 {
-    (void)bscale;
     GemmPlan p;
+    // Large M: 256x256 tiles (8 waves of 128x64) where the per-block B scale keeps the wave's
+    // promotion to one scale product per row; the per-row B scales of WGrad need more
+    // registers, so WGrad keeps 256x128 tiles (8 waves of 64x64).
     if (M > 256)
-        p.cfg = CFG_BIG;
+        p.cfg = bscale == BSCALE_BLOCK ? CFG_BIG4 : CFG_BIG;
     else if (M <= 64)
         p.cfg = CFG_M64;
     else if (M <= 128)
@@ -450,7 +454,7 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t nk = K / kGroup;
     int64_t split = 1;
-    if (p.cfg != CFG_BIG && tiles > 0 && tiles < 512 && nk > 0) {
+    if (p.cfg != CFG_BIG && p.cfg != CFG_BIG4 && tiles > 0 && tiles < 512 && nk > 0) {
         split = (512 + tiles - 1) / tiles;
         const int64_t max_split = nk / 4 > 1 ? nk / 4 : 1;   // keep >= 4 groups per split
         if (split > max_split)
@@ -491,6 +495,7 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     hipError_t e;
     switch (plan.cfg) {
     case CFG_BIG: e = launch_t<CfgBig2>(bscale, out_bf16, a, blocks, stream); break;
+    case CFG_BIG4: e = launch_t<CfgBig4>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M64: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M128: e = launch_t<CfgM128>(bscale, out_bf16, a, blocks, stream); break;
     default: e = launch_t<CfgM256>(bscale, out_bf16, a, blocks, stream); break;
