@@ -41,6 +41,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Products of the sizes must stay far below 2^62; every tensor handled here is < 2^40 bytes.
 constexpr int64_t kMaxDim = int64_t(1) << 31;
+// Quantizer inputs: a 128-row tile must span less than 2^31 bytes (32-bit buffer offsets).
+constexpr int64_t kMaxLd = int64_t(1) << 22;
 
 qr_status launch_status(hipError_t e) { return e == hipSuccess ? QR_OK : QR_ERR_LAUNCH; }
 
@@ -129,7 +131,8 @@ qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int
     const bool row = q_row != nullptr, col = q_colT != nullptr;
     if (!row && !col)
         return QR_ERR_NULL;
-    if (cols % 8 != 0 || ld_x % 8 != 0 || (rows > 0 && ld_x < cols) || (col && rows % 8 != 0))
+    if (cols % 8 != 0 || ld_x % 8 != 0 || (rows > 0 && ld_x < cols) || (col && rows % 8 != 0) ||
+        ld_x >= kMaxLd)
         return QR_ERR_SHAPE;
     if (cdiv(rows, 128) > 65535)
         return QR_ERR_SHAPE;
@@ -163,7 +166,7 @@ qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t l
         return QR_ERR_SHAPE;
     if (!q || !s || (qT == nullptr) != (sT == nullptr))
         return QR_ERR_NULL;
-    if (n % 8 != 0 || k % 8 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k))
+    if (n % 8 != 0 || k % 8 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k) || ld_w >= kMaxLd)
         return QR_ERR_SHAPE;
     if (cdiv(n, 128) > 65535)
         return QR_ERR_SHAPE;

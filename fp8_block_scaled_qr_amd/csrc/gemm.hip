@@ -65,6 +65,7 @@ struct GemmArgs {
 
 // Buffer descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-class GPUs.
 constexpr int kBufFlags = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past every descriptor's extent
 
 // Workgroup barrier for the LDS stage ring, without the memory fence of __syncthreads():
 // that fence would also wait for the next steps' global loads still in flight.  Ordering is
@@ -396,6 +397,191 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
     }
 }
 
+// ---------------------------------------------------------------- skinny M (decode)
+//
+// C[M, N] = A[M, K] B[N, K]^T for M <= 16 * MT (decode batches up to 64) with per-block B
+// scales.  The work is streaming B once from HBM, so the kernel is built around that stream:
+//   * A workgroup has NW waves; wave w owns 16 rows of B (n0 + 16 w ..) over the whole K, so
+//     no split-K partials are written.  Its B rows go from global memory straight into the
+//     MFMA operand registers (lane l: row l % 16, bytes 32 (l / 16) .. +32 of the group),
+//     through a ring of D groups: group g + D is requested as soon as group g is consumed,
+//     keeping D * 2 KB per wave in flight.
+//   * The A group (16 MT rows x 128 bytes) and its row scales are shared by the waves
+//     through LDS, double-buffered with one barrier per group; the next group's A is loaded
+//     into registers before the current group's MFMAs and written to LDS after them.
+//   * Per group and 16-row sub-tile of A: one 16x16x128 MFMA and four promotion FMAs.
+//   * Every load is a range-checked buffer load (zeros past the end), issued without a
+//     branch, so the compiler's wait counts stay exact and the ring stays in flight.
+template <int MT, int NW, int D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * NW) void k_gemm_skinny(GemmArgs g)
+{
+    constexpr int THREADS = 64 * NW;
+    constexpr int AROWS = 16 * MT;
+    constexpr int ACHUNKS = AROWS * 8;                       // 16-byte chunks per A group
+    constexpr int AREG = (ACHUNKS + THREADS - 1) / THREADS;  // per thread
+    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][AROWS * kGroup];
+    __shared__ float smS[2][AROWS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane >> 4, lr = lane & 15;
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int nk = g.nk;
+    const int64_t nw0 = (int64_t)blockIdx.x * (16 * NW) + 16 * wave;   // this wave's first B row
+
+    // B: this wave's 16 rows
+    int64_t browsv = N - nw0;
+    browsv = browsv < 0 ? 0 : (browsv > 16 ? 16 : browsv);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.B + (nw0 < N ? nw0 : 0) * K), 0, (int)(browsv * K), kBufFlags);
+    const uint32_t boff = (uint32_t)(lr * K + 32 * lq);
+    // per-block B scale row of this wave (clamped inside sb; a wave past N has zero B rows)
+    const int64_t nblk = (nw0 < N ? nw0 : N - 1) / kGroup;
+    const float *sbw = g.sb + nblk * nk;
+    // A: rows 0 .. M-1 (rows up to 16 MT - 1 read as zeros)
+    const int64_t arows = M < AROWS ? M : AROWS;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)g.A, 0, (int)(arows * K), kBufFlags);
+    const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)g.sa, 0, (int)(arows * nk * 4), kBufFlags);
+
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    // A chunk c of a group: row c / 8, 16-byte chunk c % 8; thread t takes chunks
+    // (t + i * THREADS) mod ACHUNKS (duplicates write identical bytes to the same place)
+    auto a_chunk = [&](int i) { return (tid + i * THREADS) % ACHUNKS; };
+    auto lds_off = [](int row, int c) -> int {
+        return (row >> 4) * 2048 + (c & 1) * 1024 + (((row & 15) + 16 * (c >> 1)) << 4);
+    };
+    u32x4 ra[AREG];
+    float rsa = 0.0f;
+    auto load_a = [&](int grp) {
+        const bool ok = grp < nk;
+#pragma unroll
+        for (int i = 0; i < AREG; ++i) {
+            const int c = a_chunk(i);
+            const uint32_t off = ok ? (uint32_t)((c >> 3) * K + (int64_t)grp * kGroup + ((c & 7) << 4))
+                                    : kOutOfRange;
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+        }
+        const uint32_t soff = ok ? (uint32_t)(((tid % AROWS) * nk + grp) * 4) : kOutOfRange;
+        rsa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rSA, soff, 0, 0));
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < AREG; ++i) {
+            const int c = a_chunk(i);
+            *reinterpret_cast<u32x4 *>(&smA[buf][lds_off(c >> 3, c & 7)]) = ra[i];
+        }
+        smS[buf][tid % AROWS] = rsa;
+    };
+
+    // B ring: slot j holds group g (g % D == j) as two 16-byte halves
+    u32x4 rbr[D][2];
+    auto load_b = [&](int j, int grp) {
+        const uint32_t off = grp < nk ? boff + (uint32_t)grp * kGroup : kOutOfRange;
+        rbr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+        rbr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rB, off + 16, 0, 0);
+    };
+
+    v4f acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+    // one group: MFMAs from LDS stage `buf` and ring slot j, then refill slot j with group
+    // grp + D, then move the next A group (already in registers) into the other stage
+    auto step = [&](int j, int grp, int buf) {
+        load_a(grp + 1);
+        const float sb = sbw[grp < nk ? grp : nk - 1];   // past nk: B is zero anyway
+        v8i bf;
+        bf[0] = (int)rbr[j][0][0]; bf[1] = (int)rbr[j][0][1];
+        bf[2] = (int)rbr[j][0][2]; bf[3] = (int)rbr[j][0][3];
+        bf[4] = (int)rbr[j][1][0]; bf[5] = (int)rbr[j][1][1];
+        bf[6] = (int)rbr[j][1][2]; bf[7] = (int)rbr[j][1][3];
+        v4f p[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const uint8_t *q = &smA[buf][t * 2048 + lane * 16];
+            const uint4 lo = *reinterpret_cast<const uint4 *>(q);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(q + 1024);
+            v8i af;
+            af[0] = (int)lo.x; af[1] = (int)lo.y; af[2] = (int)lo.z; af[3] = (int)lo.w;
+            af[4] = (int)hi.x; af[5] = (int)hi.y; af[6] = (int)hi.z; af[7] = (int)hi.w;
+            p[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, zero, 0, 0, 0, 127, 0,
+                                                                    127);
+        }
+        // the MFMAs read ring slot j before it is refilled (the empty volatile asm pins them
+        // ahead of the refill; left free, they drift to the end of the unrolled loop, which
+        // keeps every ring slot twice in registers)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            asm volatile("" : "+v"(p[t]));
+        load_b(j, grp + D);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const float c = smS[buf][t * 16 + lr] * sb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[t][r] = __builtin_fmaf(p[t][r], c, acc[t][r]);
+        }
+        store_a(buf ^ 1);
+        stage_barrier();
+    };
+
+    // prologue: A group 0 into stage 0, B groups 0 .. D-1 into the ring
+    load_a(0);
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        load_b(j, j);
+    store_a(0);
+    stage_barrier();
+    // main loop: D groups per iteration (the ring slot of each is then a constant); groups
+    // past nk read zeros and add nothing
+#pragma nounroll
+    for (int g0 = 0; g0 < nk; g0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            step(j, g0 + j, j & 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): ring loads past the end land first
+
+    // epilogue: lane holds C[m][n..n+3], m = 16 t + lane % 16, n = nw0 + 4 (lane / 16)
+    const int64_t n = nw0 + 4 * lq;
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int64_t m = t * 16 + lr;
+        if (m >= M || n >= N)
+            continue;
+        const v4f a = acc[t];
+        if (!OUT_BF16) {
+            float *c = reinterpret_cast<float *>(g.C) + m * N + n;
+            if (vec_ok && n + 3 < N) {
+                *reinterpret_cast<float4 *>(c) = make_float4(a[0], a[1], a[2], a[3]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        c[r] = a[r];
+            }
+        } else {
+            uint16_t *c = reinterpret_cast<uint16_t *>(g.C) + m * N + n;
+            if (vec_ok && n + 3 < N) {
+                uint2 o;
+                o.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+                o.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+                *reinterpret_cast<uint2 *>(c) = o;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        c[r] = (uint16_t)f32_to_bf16(a[r]);
+            }
+        }
+    }
+}
+
 // Tile configurations, indexed by GemmPlan::cfg.
 using CfgBig2 = TileCfg<256, 128, 4, 2>;   // prefill / training: 8 waves, 64x64 per wave
 using CfgBig4 = TileCfg<256, 256, 2, 4>;   // prefill / training: 8 waves, 128x64 per wave
@@ -403,13 +589,34 @@ using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
 using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
 using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
 
-enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4 };
+enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_SKINNY = 5 };
+
+#ifndef QR_SKINNY_NW
+#define QR_SKINNY_NW 4
+#endif
+#ifndef QR_SKINNY_D
+#define QR_SKINNY_D 8
+#endif
+constexpr int kSkinnyNW = QR_SKINNY_NW;   // waves per workgroup (16 B rows each)
+constexpr int kSkinnyD = QR_SKINNY_D;     // B groups in flight per wave
+
+template <int MT>
+hipError_t launch_skinny(bool out_bf16, const GemmArgs &a, hipStream_t stream)
+{
+    const int64_t blocks = (a.N + 16 * kSkinnyNW - 1) / (16 * kSkinnyNW);
+    if (out_bf16)
+        k_gemm_skinny<MT, kSkinnyNW, kSkinnyD, true><<<(unsigned)blocks, 64 * kSkinnyNW, 0, stream>>>(a);
+    else
+        k_gemm_skinny<MT, kSkinnyNW, kSkinnyD, false><<<(unsigned)blocks, 64 * kSkinnyNW, 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 void tile_dims(int cfg, int &bm, int &bn)
 {
     switch (cfg) {
     case CFG_BIG: bm = CfgBig2::BM; bn = CfgBig2::BN; break;
     case CFG_BIG4: bm = CfgBig4::BM; bn = CfgBig4::BN; break;
+    case CFG_SKINNY: bm = 64; bn = 16 * kSkinnyNW; break;
     case CFG_M64: bm = CfgM64::BM; bn = CfgM64::BN; break;
     case CFG_M128: bm = CfgM128::BM; bn = CfgM128::BN; break;
     default: bm = CfgM256::BM; bn = CfgM256::BN; break;
@@ -443,6 +650,8 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     // registers, so WGrad keeps 256x128 tiles (8 waves of 64x64).
     if (M > 256)
         p.cfg = bscale == BSCALE_BLOCK ? CFG_BIG4 : CFG_BIG;
+    else if (M <= 64 && bscale == BSCALE_BLOCK)
+        p.cfg = CFG_SKINNY;   // decode: stream B once, no split
     else if (M <= 64)
         p.cfg = CFG_M64;
     else if (M <= 128)
@@ -454,7 +663,8 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t nk = K / kGroup;
     int64_t split = 1;
-    if (p.cfg != CFG_BIG && p.cfg != CFG_BIG4 && tiles > 0 && tiles < 512 && nk > 0) {
+    if (p.cfg != CFG_BIG && p.cfg != CFG_BIG4 && p.cfg != CFG_SKINNY && tiles > 0 && tiles < 512 &&
+        nk > 0) {
         split = (512 + tiles - 1) / tiles;
         const int64_t max_split = nk / 4 > 1 ? nk / 4 : 1;   // keep >= 4 groups per split
         if (split > max_split)
@@ -491,6 +701,10 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     a.split = plan.split;
     a.kgps = (a.nk + plan.split - 1) / plan.split;
     a.C = plan.split > 1 ? ws : C;
+    if (plan.cfg == CFG_SKINNY)
+        return M <= 16 ? launch_skinny<1>(out_bf16, a, stream)
+               : M <= 32 ? launch_skinny<2>(out_bf16, a, stream)
+                         : launch_skinny<4>(out_bf16, a, stream);
     const int blocks = a.tilesM * a.tilesN * plan.split;
     hipError_t e;
     switch (plan.cfg) {

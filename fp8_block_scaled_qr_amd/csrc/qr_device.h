@@ -39,62 +39,90 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v)
     return v;
 }
 
-// Group scale s = RN32(amax / 448) and the reciprocal r = RN32(1 / s) used by quot().
+// A group's scale s = RN32(amax / 448) and what the quotient needs: sq = s * m and
+// r = RN32(1 / sq), where m = 2^64 for the tiny scales 0 < s < 2^-100 (whose reciprocal could
+// overflow and whose residual could underflow) and m = 1 otherwise.  s == 0 (amax == 0) gives
+// r = 0.
 struct Scale {
-    float s, r;
-    bool slow;  // s == 0 or tiny: use the IEEE division path
+    float s;    // the group's scale (the value stored)
+    float sq;   // s * m
+    float r;    // RN32(1 / sq), 0 when s == 0
+    float m;    // 1 or 2^64
 };
 
-__device__ __forceinline__ Scale make_scale(uint32_t amax_bits15)
+constexpr float kTinyScale = 0x1p-100f;
+constexpr float kTinyLift = 0x1p64f;
+
+__device__ __forceinline__ Scale scale_of(float s)
 {
     Scale sc;
-    float amax = __uint_as_float(amax_bits15 << 16);
-    sc.s = __fdiv_rn(amax, kE4M3Max);
-    sc.r = __fdiv_rn(1.0f, sc.s);
-    sc.slow = !(sc.s >= 0x1p-100f);
+    sc.s = s;
+    sc.m = (s > 0.0f && s < kTinyScale) ? kTinyLift : 1.0f;
+    sc.sq = s * sc.m;
+    sc.r = sc.sq == 0.0f ? 0.0f : __fdiv_rn(1.0f, sc.sq);
     return sc;
 }
 
+__device__ __forceinline__ Scale make_scale(uint32_t amax_bits15)
+{
+    return scale_of(__fdiv_rn(__uint_as_float(amax_bits15 << 16), kE4M3Max));
+}
+
+__device__ __forceinline__ bool tiny_scale(const Scale &sc) { return sc.m != 1.0f; }
+
 // x / s as the E4M3 encoder needs it: equal to RN32(x / s) bit for bit wherever |x / s| >
 // 2^-10, and with the same sign and magnitude <= 2^-10 elsewhere (all of which encode to the
-// signed zero).  Fast path (P. Markstein, "Computation of elementary functions on the IBM
+// signed zero).  Method (P. Markstein, "Computation of elementary functions on the IBM
 // RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990): with r = RN(1/s) and
 // q = RN(x*r), the residual x - q*s is exact in one FMA and RN(q + residual*r) is the
 // correctly rounded quotient, except where that residual underflows (x tiny, far inside the
 // zero code).  The residual is formed as q*s - x and subtracted so that x = -0 yields -0.
-// Groups whose scale is zero or below 2^-100 (where 1/s may overflow) take the IEEE
-// division.  A host replay of these exact operations over every pair of bf16 amax and bf16
-// x confirms both properties.
+// quot() is valid for groups with m == 1 (including s == 0); quot_lifted() for every group:
+// it first multiplies x by m, which is exact, so x*m / (s*m) is the same quotient.  A host
+// replay of these exact operations over every pair of bf16 amax and bf16 x confirms both
+// properties.
 __device__ __forceinline__ float quot(float x, const Scale &sc)
 {
-    if (sc.slow)
-        return sc.s == 0.0f ? x : __fdiv_rn(x, sc.s);
     float q = x * sc.r;
-    float e = __builtin_fmaf(q, sc.s, -x);
+    float e = __builtin_fmaf(q, sc.sq, -x);
     return __builtin_fmaf(-e, sc.r, q);
 }
 
-// Four values -> four E4M3 codes (byte i = value i): clamp to +-448 (saturation), then the
-// hardware round-to-nearest-even conversion.
+__device__ __forceinline__ float quot_lifted(float x, const Scale &sc)
+{
+    return quot(x * sc.m, sc);
+}
+
+// Four quotients -> four E4M3 codes (byte i = value i) by the hardware conversion, which
+// rounds to nearest even and turns magnitudes above 464 (the midpoint between 448 and the
+// next step) into NaN.  A quotient x / s of a finite group never exceeds 448 by more than
+// the scale's rounding error (at most ~0.34 %, reached only when amax / 448 is an fp32
+// subnormal), so every quotient lies below 464 and the conversion saturates it to +-448 as
+// required without a clamp; the conversion's rounding of [448, 464) to 448 is checked on
+// the device by the parity tests.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
 {
-    a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
-    b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
-    c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
-    d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
 
 // Codes of the 8 bf16 values packed in v (element i in half i%2 of dword i/2), one scale.
+// LIFT selects quot_lifted (needed when the group's scale may be tiny).
+template <bool LIFT>
+__device__ __forceinline__ float quot_t(float x, const Scale &sc)
+{
+    return LIFT ? quot_lifted(x, sc) : quot(x, sc);
+}
+
+template <bool LIFT>
 __device__ __forceinline__ uint2 encode8(const uint4 &v, const Scale &sc)
 {
     uint2 o;
-    o.x = e4m3x4(quot(bf16_lo(v.x), sc), quot(bf16_hi(v.x), sc), quot(bf16_lo(v.y), sc),
-                 quot(bf16_hi(v.y), sc));
-    o.y = e4m3x4(quot(bf16_lo(v.z), sc), quot(bf16_hi(v.z), sc), quot(bf16_lo(v.w), sc),
-                 quot(bf16_hi(v.w), sc));
+    o.x = e4m3x4(quot_t<LIFT>(bf16_lo(v.x), sc), quot_t<LIFT>(bf16_hi(v.x), sc),
+                 quot_t<LIFT>(bf16_lo(v.y), sc), quot_t<LIFT>(bf16_hi(v.y), sc));
+    o.y = e4m3x4(quot_t<LIFT>(bf16_lo(v.z), sc), quot_t<LIFT>(bf16_hi(v.z), sc),
+                 quot_t<LIFT>(bf16_lo(v.w), sc), quot_t<LIFT>(bf16_hi(v.w), sc));
     return o;
 }
 

@@ -15,6 +15,8 @@
 // LDS, so the two divisions per group are not repeated by every lane.  Codes leave as 8-byte
 // stores: in the input layout for row groups and blocks, and as 8 consecutive rows of one
 // column for the transposed layouts (the column's group is contiguous there).
+#include <type_traits>
+
 #include "qr_device.h"
 #include "qr_internal.h"
 
@@ -23,6 +25,10 @@ namespace qr {
 namespace {
 
 constexpr int kTile = 128;
+#ifndef QR_QUANT_WG_PER_CU
+#define QR_QUANT_WG_PER_CU 4
+#endif
+constexpr int kQuantWgPerCu = QR_QUANT_WG_PER_CU;   // resident workgroups per CU in the persistent grid
 
 __device__ __forceinline__ uint32_t absmax8(const uint4 &v)
 {
@@ -35,13 +41,19 @@ __device__ __forceinline__ uint32_t half_bits(const uint4 &v, int i)
     return ((i & 1) ? (w >> 16) : w) & 0x7FFFu;
 }
 
-__device__ __forceinline__ Scale scale_from(float s, float r)
+__device__ __forceinline__ Scale unpack_scale(const float4 &p)
 {
     Scale sc;
-    sc.s = s;
-    sc.r = r;
-    sc.slow = !(s >= 0x1p-100f);
+    sc.s = 0.0f;   // not needed by the encoder
+    sc.sq = p.x;
+    sc.r = p.y;
+    sc.m = p.z;
     return sc;
+}
+
+__device__ __forceinline__ float4 pack_scale(const Scale &sc)
+{
+    return make_float4(sc.sq, sc.r, sc.m, 0.0f);
 }
 
 // 8x8 byte transpose: in[j] holds row j (byte i = column i); out[i] holds column i
@@ -68,6 +80,45 @@ __device__ __forceinline__ void transpose8x8(const uint2 in[8], uint2 out[8])
     transpose4x4(in[4].y, in[5].y, in[6].y, in[7].y, out[4].y, out[5].y, out[6].y, out[7].y);
 }
 
+// Barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its global
+// loads, so the next tile's prefetch stays in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kBufFlags = 0x00020000;     // raw buffer, range-checked per lane
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// The tile's eight 16-byte loads per thread as range-checked buffer loads: a row past `rows`
+// lies past the descriptor's extent and a column octet past `cols` takes an offset outside it,
+// so both read zeros without a branch (a branch around each load would make the compiler
+// wait for every outstanding load, the prefetch included, before the first use).
+__device__ __forceinline__ void load_tile(const uint16_t *__restrict__ x, int64_t rows,
+                                          int64_t ldx, int64_t r0, int64_t col, bool colok,
+                                          int oq, uint4 v[8])
+{
+    int64_t extent = (rows - r0) * ldx * 2;
+    if (extent > 0x7FFFFFF0)
+        extent = 0x7FFFFFF0;
+    if (extent < 0)
+        extent = 0;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + r0 * ldx), 0, (int)extent, kBufFlags);
+    const uint32_t base = (uint32_t)(8 * oq * ldx + col) * 2u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t off = colok ? base + (uint32_t)(j * ldx * 2) : kOutOfRange;
+        v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    }
+}
+
+// Persistent: workgroup b handles tiles b, b + gridDim.x, ... (row-major over the tile grid)
+// and prefetches the next tile's 32 KB into registers while it reduces, encodes and stores
+// the current one, so reads and writes of the whole grid overlap.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ldx,
@@ -85,143 +136,193 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
     __shared__ uint32_t red_col[4][kTile];
     __shared__ uint32_t red_row[kTile];
     __shared__ uint32_t red_blk[4];
-    __shared__ float row_s[kTile], row_r[kTile], col_s[kTile], col_r[kTile];
-    __shared__ float blk_sr[2];
+    __shared__ float4 row_sc[kTile], col_sc[kTile];
+    __shared__ float4 blk_sc;
+    __shared__ uint32_t tiny_flag[2];   // per iteration parity: some group of the tile is tiny
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int oq = t >> 4;   // row octet within the tile
     const int oc = t & 15;   // column octet within the tile
-    const int64_t bi = blockIdx.y, bj = blockIdx.x;
-    const int64_t r0 = bi * kTile, c0 = bj * kTile;
-    const int64_t col = c0 + 8 * oc;
     const int64_t ngr = (rows + kTile - 1) / kTile, ngc = (cols + kTile - 1) / kTile;
-    const bool colok = col < cols;
 
-    uint4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t r = r0 + 8 * oq + j;
-        v[j] = make_uint4(0, 0, 0, 0);
-        if (colok && r < rows)
-            v[j] = *reinterpret_cast<const uint4 *>(x + r * ldx + col);
-    }
+    auto process = [&](int64_t bi, int64_t bj, int par, uint4 (&v)[8]) {
+        const int64_t r0 = bi * kTile, c0 = bj * kTile;
+        const int64_t col = c0 + 8 * oc;
+        const bool colok = col < cols;
 
-    // ---- maxima
-    if (ROW) {
+        // ---- maxima
+        if (t == 0)
+            tiny_flag[par] = 0;   // last read two iterations ago, before two barriers
+        if (ROW) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t m = row16_max(absmax8(v[j]));
-            if (oc == 0)
-                red_row[8 * oq + j] = m;
+            for (int j = 0; j < 8; ++j) {
+                uint32_t m = row16_max(absmax8(v[j]));
+                if (oc == 0)
+                    red_row[8 * oq + j] = m;
+            }
         }
-    }
-    if (COL) {
+        if (COL) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 8; ++i) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    m = umax(m, half_bits(v[j], i));
+                m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
+                m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
+                if (lane < 16)
+                    red_col[wave][8 * oc + i] = m;
+            }
+        }
+        if (ANYBLK) {
             uint32_t m = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                m = umax(m, half_bits(v[j], i));
+                m = umax(m, absmax8(v[j]));
+            m = row16_max(m);
             m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
             m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
-            if (lane < 16)
-                red_col[wave][8 * oc + i] = m;
+            if (lane == 0)
+                red_blk[wave] = m;
         }
-    }
-    if (ANYBLK) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            m = umax(m, absmax8(v[j]));
-        m = row16_max(m);
-        m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
-        m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
-        if (lane == 0)
-            red_blk[wave] = m;
-    }
-    __syncthreads();
+        lds_barrier();
 
-    // ---- scales: one thread per row, per column, per block
-    if (ROW && t < kTile) {
-        Scale sc = make_scale(red_row[t]);
-        row_s[t] = sc.s;
-        row_r[t] = sc.r;
-        if (r0 + t < rows)
-            s[(r0 + t) * ngc + bj] = sc.s;
-    }
-    if (COL && (ROW ? t >= kTile : t < kTile)) {
-        const int c = ROW ? t - kTile : t;
-        uint32_t m = umax(umax(red_col[0][c], red_col[1][c]), umax(red_col[2][c], red_col[3][c]));
-        Scale sc = make_scale(m);
-        col_s[c] = sc.s;
-        col_r[c] = sc.r;
-        if (c0 + c < cols)
-            sT[(c0 + c) * ngr + bi] = sc.s;
-    }
-    if (ANYBLK && t == 0) {
-        uint32_t m = umax(umax(red_blk[0], red_blk[1]), umax(red_blk[2], red_blk[3]));
-        Scale sc = make_scale(m);
-        blk_sr[0] = sc.s;
-        blk_sr[1] = sc.r;
-        if (BLK)
-            s[bi * ngc + bj] = sc.s;
-        if (BLKT)
-            sT[bj * ngr + bi] = sc.s;
-    }
-    __syncthreads();
+        // ---- scales: one thread per row, per column, per block
+        if (ROW && t < kTile) {
+            const Scale sc = make_scale(red_row[t]);
+            row_sc[t] = pack_scale(sc);
+            if (tiny_scale(sc))
+                tiny_flag[par] = 1;
+            if (r0 + t < rows)
+                s[(r0 + t) * ngc + bj] = sc.s;
+        }
+        if (COL && (ROW ? t >= kTile : t < kTile)) {
+            const int c = ROW ? t - kTile : t;
+            const uint32_t m = umax(umax(red_col[0][c], red_col[1][c]),
+                                    umax(red_col[2][c], red_col[3][c]));
+            const Scale sc = make_scale(m);
+            col_sc[c] = pack_scale(sc);
+            if (tiny_scale(sc))
+                tiny_flag[par] = 1;
+            if (c0 + c < cols)
+                sT[(c0 + c) * ngr + bi] = sc.s;
+        }
+        if (ANYBLK && t == 0) {
+            const uint32_t m = umax(umax(red_blk[0], red_blk[1]), umax(red_blk[2], red_blk[3]));
+            const Scale sc = make_scale(m);
+            blk_sc = pack_scale(sc);
+            if (tiny_scale(sc))
+                tiny_flag[par] = 1;
+            if (BLK)
+                s[bi * ngc + bj] = sc.s;
+            if (BLKT)
+                sT[bj * ngr + bi] = sc.s;
+        }
+        lds_barrier();
 
-    // ---- codes
-    if (ROW) {
+        // ---- codes (the lifted quotient only for tiles that hold a tiny scale)
+        auto encode = [&](auto lift_tag) {
+            constexpr bool LIFT = decltype(lift_tag)::value;
+            if (ROW) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int rr = 8 * oq + j;
-            const int64_t r = r0 + rr;
-            uint2 c8 = encode8(v[j], scale_from(row_s[rr], row_r[rr]));
-            if (colok && r < rows)
-                *reinterpret_cast<uint2 *>(q + r * cols + col) = c8;
-        }
-    }
-    if (ANYBLK) {
-        const Scale sc = scale_from(blk_sr[0], blk_sr[1]);
-        uint2 c8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            c8[j] = encode8(v[j], sc);
-        if (BLK) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t r = r0 + 8 * oq + j;
-                if (colok && r < rows)
-                    *reinterpret_cast<uint2 *>(q + r * cols + col) = c8[j];
+                for (int j = 0; j < 8; ++j) {
+                    const int rr = 8 * oq + j;
+                    const int64_t r = r0 + rr;
+                    const uint2 c8 = encode8<LIFT>(v[j], unpack_scale(row_sc[rr]));
+                    if (colok && r < rows)
+                        *reinterpret_cast<uint2 *>(q + r * cols + col) = c8;
+                }
             }
-        }
-        if (BLKT) {
-            uint2 ct[8];
-            transpose8x8(c8, ct);
-            const int64_t r = r0 + 8 * oq;   // rows % 8 == 0: the octet is all in or all out
-            if (colok && r < rows) {
+            if (ANYBLK) {
+                const Scale sc = unpack_scale(blk_sc);
+                uint2 c8[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<uint2 *>(qT + (col + i) * rows + r) = ct[i];
+                for (int j = 0; j < 8; ++j)
+                    c8[j] = encode8<LIFT>(v[j], sc);
+                if (BLK) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int64_t r = r0 + 8 * oq + j;
+                        if (colok && r < rows)
+                            *reinterpret_cast<uint2 *>(q + r * cols + col) = c8[j];
+                    }
+                }
+                if (BLKT) {
+                    uint2 ct[8];
+                    transpose8x8(c8, ct);
+                    const int64_t r = r0 + 8 * oq;   // rows % 8 == 0: the octet is all in or out
+                    if (colok && r < rows) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            *reinterpret_cast<uint2 *>(qT + (col + i) * rows + r) = ct[i];
+                    }
+                }
             }
-        }
-    }
-    if (COL) {
-        const int64_t r = r0 + 8 * oq;       // rows % 8 == 0: the octet is all in or all out
-        const bool ok = colok && r < rows;
+            if (COL) {
+                const int64_t r = r0 + 8 * oq;       // rows % 8 == 0: the octet is all in or out
+                const bool ok = colok && r < rows;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = 8 * oc + i;
-            const Scale sc = scale_from(col_s[c], col_r[c]);
-            uint2 c8;
-            c8.x = e4m3x4(quot(bf16_elem(v[0], i), sc), quot(bf16_elem(v[1], i), sc),
-                          quot(bf16_elem(v[2], i), sc), quot(bf16_elem(v[3], i), sc));
-            c8.y = e4m3x4(quot(bf16_elem(v[4], i), sc), quot(bf16_elem(v[5], i), sc),
-                          quot(bf16_elem(v[6], i), sc), quot(bf16_elem(v[7], i), sc));
-            if (ok)
-                *reinterpret_cast<uint2 *>(qT + (col + i) * rows + r) = c8;
+                for (int i = 0; i < 8; ++i) {
+                    const Scale sc = unpack_scale(col_sc[8 * oc + i]);
+                    uint2 c8;
+                    c8.x = e4m3x4(quot_t<LIFT>(bf16_elem(v[0], i), sc),
+                                  quot_t<LIFT>(bf16_elem(v[1], i), sc),
+                                  quot_t<LIFT>(bf16_elem(v[2], i), sc),
+                                  quot_t<LIFT>(bf16_elem(v[3], i), sc));
+                    c8.y = e4m3x4(quot_t<LIFT>(bf16_elem(v[4], i), sc),
+                                  quot_t<LIFT>(bf16_elem(v[5], i), sc),
+                                  quot_t<LIFT>(bf16_elem(v[6], i), sc),
+                                  quot_t<LIFT>(bf16_elem(v[7], i), sc));
+                    if (ok)
+                        *reinterpret_cast<uint2 *>(qT + (col + i) * rows + r) = c8;
+                }
+            }
+        };
+        if (__builtin_amdgcn_readfirstlane(tiny_flag[par]))
+            encode(std::true_type{});
+        else
+            encode(std::false_type{});
+    };
+
+    // Two register buffers in turn, so that the loads of one tile are always in flight while
+    // the other is processed (a copy between them at the end of each iteration would make the
+    // compiler wait for the new loads before the old data is used).
+    // Tile (bi, bj) is walked incrementally (no 64-bit division in the loop).  A tile past
+    // the end gets an empty descriptor (its loads return zeros without touching memory), so
+    // the loads are issued unconditionally and the compiler's wait counts stay exact.
+    auto prefetch = [&](int64_t bi, int64_t bj, uint4 (&v)[8]) {
+        const bool valid = bi < ngr;
+        const int64_t c = bj * kTile + 8 * oc;
+        load_tile(x, valid ? rows : 0, ldx, valid ? bi * kTile : 0, c, c < cols, oq, v);
+    };
+    const int64_t step = gridDim.x;
+    const int64_t dbi = step / ngc, dbj = step - dbi * ngc;
+    auto advance = [&](int64_t &bi, int64_t &bj) {
+        bi += dbi;
+        bj += dbj;
+        if (bj >= ngc) {
+            bj -= ngc;
+            ++bi;
         }
+    };
+    uint4 va[8], vb[8];
+    int64_t bi = (int64_t)blockIdx.x / ngc, bj = (int64_t)blockIdx.x - bi * ngc;
+    int64_t ni = bi, nj = bj;
+    prefetch(bi, bj, va);
+    while (bi < ngr) {
+        advance(ni, nj);
+        prefetch(ni, nj, vb);
+        process(bi, bj, 0, va);
+        bi = ni;
+        bj = nj;
+        if (bi >= ngr)
+            break;
+        advance(ni, nj);
+        prefetch(ni, nj, va);
+        process(bi, bj, 1, vb);
+        bi = ni;
+        bj = nj;
     }
 }
 
@@ -275,6 +376,34 @@ __global__ __launch_bounds__(256) void k_uaq_fold(const uint16_t *w, int64_t n, 
 
 }  // namespace
 
+// Workgroups of a persistent grid for kernel `fn`: the CU count times the workgroups that fit
+// on a CU at once (capped), so the whole grid is resident and each workgroup loops.
+static int64_t persistent_grid(const void *fn)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    if (per_cu > kQuantWgPerCu)
+        per_cu = kQuantWgPerCu;
+    return (int64_t)cus * per_cu;
+}
+
+template <int MODE>
+static hipError_t launch_mode(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t *q, float *s, uint8_t *qT, float *sT, int64_t ntiles,
+                              hipStream_t stream)
+{
+    const int64_t limit = persistent_grid(reinterpret_cast<const void *>(&k_quant_tile<MODE>));
+    const dim3 grid((unsigned)(ntiles < limit ? ntiles : limit));
+    k_quant_tile<MODE><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s, qT, sT);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t *q, float *s, uint8_t *qT, float *sT,
                              hipStream_t stream)
@@ -282,29 +411,21 @@ hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t 
     const int64_t ngr = (rows + kTile - 1) / kTile, ngc = (cols + kTile - 1) / kTile;
     if (ngr == 0 || ngc == 0)
         return hipSuccess;
-    dim3 grid((unsigned)ngc, (unsigned)ngr);
+    const int64_t nt = ngr * ngc;
     switch (mode) {
     case QMODE_ROW:
-        k_quant_tile<QMODE_ROW><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s, qT, sT);
-        break;
+        return launch_mode<QMODE_ROW>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
     case QMODE_COL:
-        k_quant_tile<QMODE_COL><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s, qT, sT);
-        break;
+        return launch_mode<QMODE_COL>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
     case QMODE_ROW | QMODE_COL:
-        k_quant_tile<QMODE_ROW | QMODE_COL><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s,
-                                                                      qT, sT);
-        break;
+        return launch_mode<QMODE_ROW | QMODE_COL>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
     case QMODE_BLK:
-        k_quant_tile<QMODE_BLK><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s, qT, sT);
-        break;
+        return launch_mode<QMODE_BLK>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
     case QMODE_BLK | QMODE_BLKT:
-        k_quant_tile<QMODE_BLK | QMODE_BLKT><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s,
-                                                                       qT, sT);
-        break;
+        return launch_mode<QMODE_BLK | QMODE_BLKT>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
     default:
         return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,

@@ -94,8 +94,8 @@ int32_t qr_abi_version(void);
  * Either output pair may be NULL (both members NULL), but not both pairs.  Requesting both
  * is the fused quantize-transpose: x is read once.
  *
- * Size rules: rows >= 0, cols >= 0; cols % 8 == 0 and ld_x % 8 == 0; when the column-wise
- * pair is requested also rows % 8 == 0.  x, q_row, q_colT 16-byte aligned; scale pointers
+ * Size rules: rows >= 0, cols >= 0; cols % 8 == 0, ld_x % 8 == 0 and ld_x < 2^22; when the
+ * column-wise pair is requested also rows % 8 == 0.  x, q_row, q_colT 16-byte aligned; scale pointers
  * 4-byte aligned.  Outputs must not overlap x or each other.
  */
 qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
@@ -111,7 +111,7 @@ qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int
  * Optional transposed copy for DGrad (both NULL or both non-NULL):
  *     qT [k, n] with qT[c, r] = q[r, c], sT [ceil(k/128), ceil(n/128)] with sT[j, i] = s[i, j].
  *
- * Size rules: n, k >= 0; n % 8 == 0, k % 8 == 0, ld_w % 8 == 0.  Alignment and aliasing as
+ * Size rules: n, k >= 0; n % 8 == 0, k % 8 == 0, ld_w % 8 == 0, ld_w < 2^22.  Alignment and aliasing as
  * for qr_quant_act_1x128.
  */
 qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w,

@@ -5,7 +5,10 @@
  * 128-element group computes s = RN32(amax / 448) and r = RN32(1 / s) once, and each element
  * then takes three operations (P. Markstein, IBM J. Res. Dev. 34(1), 1990):
  *     q = RN(x * r);  e = RN(q * s - x) [one FMA];  v = RN(-e * r + q) [one FMA]
- * with groups whose s is 0 or below 2^-100 using the IEEE division instead.  This program
+ * Groups with 0 < s < 2^-100 first scale both x and s by m = 2^64 (exact: a power of two
+ * applied to a bf16 x and to s, nothing overflows), i.e. they run the same three operations
+ * on x*m with sq = s*m and r = RN32(1 / sq).  A group with s == 0 (amax == 0, every x is +-0)
+ * uses r = 0, which yields the signed zero of x.  This program
  * replays exactly those binary32 operations for EVERY pair (amax, x) of finite bf16 values
  * with |x| <= amax and compares v with the IEEE binary32 division x / s:
  *   - where |x / s| > 2^-10 (the code is not +-0), v must equal x / s bit for bit;
@@ -47,22 +50,19 @@ int main(void)
     for (uint32_t ab = 0; ab < 0x7F80u; ++ab) {          /* every finite amax >= 0 */
         const float amax = bf16(ab);
         const float s = amax / 448.0f;
-        const float r = 1.0f / s;
-        const int slow = !(s >= 0x1p-100f);
+        const float m = (s > 0.0f && s < 0x1p-100f) ? 0x1p64f : 1.0f;
+        const float sq = s * m;
+        const float r = sq == 0.0f ? 0.0f : 1.0f / sq;
         for (uint32_t xb = 0; xb < 0x10000u; ++xb) {
             if ((xb & 0x7F80u) == 0x7F80u)
                 continue;                                 /* Inf / NaN */
             if ((xb & 0x7FFFu) > ab)
                 continue;                                 /* |x| > amax: not in this group */
             const float x = bf16(xb);
-            float v;
-            if (slow) {
-                v = s == 0.0f ? x : x / s;
-            } else {
-                const float q = x * r;
-                const float e = fmaf(q, s, -x);
-                v = fmaf(-e, r, q);
-            }
+            const float xm = x * m;
+            const float q = xm * r;
+            const float e = fmaf(q, sq, -xm);
+            const float v = fmaf(-e, r, q);
             const float ref = s == 0.0f ? x : x / s;
             ++pairs;
             int ok;

@@ -113,17 +113,19 @@ def test_gemm_validation(L, name):
 
 
 def test_gemm_workspace(L):
-    # skinny decode shapes split K and need a workspace; large shapes need none
-    nb = qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 4096)
-    assert nb > 0 and nb % (64 * 14336 * 4) == 0
+    # mid-size M (65..256) splits K over a few tiles and needs a workspace; decode batches up
+    # to 64 rows stream the weight without a split; large shapes need none
+    nb = qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 200, 14336, 4096)
+    assert nb > 0 and nb % (200 * 14336 * 4) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 4096) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 8192, 4096, 4096) == 0
-    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 100) == 0     # invalid K
-    assert qr.qr_gemm_workspace_bytes(9, 64, 14336, 4096) == 0
-    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 64, 14336, 4096, E, 1, None, 0) == WORKSPACE
-    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 64, 14336, 4096, E, 1, 6 << 40, nb - 1) == WORKSPACE
-    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 64, 14336, 4096, E, 1, A, nb) == ALIAS
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 200, 14336, 100) == 0    # invalid K
+    assert qr.qr_gemm_workspace_bytes(9, 200, 14336, 4096) == 0
+    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 200, 14336, 4096, E, 1, None, 0) == WORKSPACE
+    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 200, 14336, 4096, E, 1, 6 << 40, nb - 1) == WORKSPACE
+    assert gemm(L, "qr_gemm_fp8_bsfprop", A, B, C, D, 200, 14336, 4096, E, 1, A, nb) == ALIAS
     # DGrad / WGrad sizes are passed as given to their entry points
-    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_DGRAD, 64, 4096, 14336) > 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_DGRAD, 200, 4096, 14336) > 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_WGRAD, 8192, 4096, 4096) == 0
 
 

@@ -212,7 +212,11 @@ def test_fprop_tiny_fp32_full():
 
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (1, 128, 128), (300, 264, 256),
                                    (129, 1000, 640), (64, 512, 1024), (256, 384, 2048),
-                                   (520, 136, 384)])
+                                   (520, 136, 384),
+                                   # decode batches (M <= 64): ragged N, group counts that
+                                   # are not a multiple of the kernel's 8-group ring
+                                   (5, 200, 1152), (17, 1000, 384), (33, 72, 640),
+                                   (64, 264, 1280), (16, 8, 128)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_fprop_shapes_full(M, N, K, out):
     x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 7, max(1, K // 100))
@@ -299,6 +303,22 @@ def test_dgrad_wgrad_small_full(M, N, K):
         rxT, rsxT = oracle.quant_cols_T(x)
         Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT)
         assert_gemm_close(out_f64(dw), Y, S, "wgrad", out == qr.QR_OUT_BF16)
+
+
+@pytest.mark.parametrize("M,N,K", [(48, 384, 520), (8, 128, 1000)])
+def test_dgrad_decode_batch_full(M, N, K):
+    """DGrad with a small token count takes the skinny-M kernel; full comparison."""
+    say("dgrad small M", M, N, K)
+    dy = qr_synth.normal_bf16(M + N + 5, (M, N), 1e-3)
+    w = qr_synth.normal_bf16(N * K + 5, (N, K), 0.02)
+    qdy, sdy, _, _ = qr.quant_act(dev_bf16(dy), row=True)
+    _, _, qwT, swT = qr.quant_w(dev_bf16(w), transposed=True)
+    rdy, rsdy = oracle.quant_rows(dy)
+    rw, rsw = oracle.quant_blocks(w)
+    for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
+        dx = qr.gemm_dgrad(qdy, sdy, qwT, swT, out_dtype=out)
+        Y, S = oracle.dgrad(rdy, rsdy, rw, rsw)
+        assert_gemm_close(out_f64(dx), Y, S, "dgrad", out == qr.QR_OUT_BF16)
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 3])
