@@ -397,90 +397,154 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
     }
 }
 
+// Raw buffer loads issued through inline asm, for a register ring whose waits are counted by
+// hand: the compiler does not see these as memory operations, so it inserts no waits of its
+// own for them (its waits around a loop back edge drain the whole ring).  The caller waits
+// with vm_wait<N>() before the first use, where N is the number of loads issued after the
+// one needed (loads retire in order).  The descriptor is four SGPRs: base address, stride 0,
+// extent in bytes, raw-buffer flags; offsets at or past the extent read zeros.
+typedef int v4i_sgpr __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i_sgpr make_rsrc_sgpr(const void *base, uint32_t extent)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4i_sgpr r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)extent);
+    r[3] = kBufFlags;
+    return r;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t asm_load_b128(const v4i_sgpr &rsrc, uint32_t off)
+{
+    u32x4_t v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+__device__ __forceinline__ float asm_load_b32(const v4i_sgpr &rsrc, uint32_t off)
+{
+    float v;
+    asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+// Every register an asm load writes must stay live (be named by a later asm statement) until
+// the vm_wait that covers the load: the compiler does not know the write is still pending
+// and would otherwise reuse the register.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------- skinny M (decode)
 //
 // C[M, N] = A[M, K] B[N, K]^T for M <= 16 * MT (decode batches up to 64) with per-block B
 // scales.  The work is streaming B once from HBM, so the kernel is built around that stream:
 //   * A workgroup has NW waves; wave w owns 16 rows of B (n0 + 16 w ..) over the whole K, so
 //     no split-K partials are written.  Its B rows go from global memory straight into the
-//     MFMA operand registers (lane l: row l % 16, bytes 32 (l / 16) .. +32 of the group),
-//     through a ring of D groups: group g + D is requested as soon as group g is consumed,
-//     keeping D * 2 KB per wave in flight.
-//   * The A group (16 MT rows x 128 bytes) and its row scales are shared by the waves
-//     through LDS, double-buffered with one barrier per group; the next group's A is loaded
-//     into registers before the current group's MFMAs and written to LDS after them.
-//   * Per group and 16-row sub-tile of A: one 16x16x128 MFMA and four promotion FMAs.
-//   * Every load is a range-checked buffer load (zeros past the end), issued without a
-//     branch, so the compiler's wait counts stay exact and the ring stays in flight.
-template <int MT, int NW, int D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * NW) void k_gemm_skinny(GemmArgs g)
+//     MFMA operand registers (lane l: row l % 16, bytes 32 (l / 16) .. +32 of the group).
+//   * The A group (16 MT rows x 128 bytes) and its row scales are shared through LDS: each
+//     thread carries a slice of them.
+//   * Both travel in one ring of D groups per wave: slot j holds group g (g % D == j) -- the
+//     wave's B fragment and the thread's A slice -- and is refilled with group g + D as soon
+//     as group g is consumed.  Loads retire in order, so a wave only ever waits for its
+//     oldest loads and keeps D groups in flight (a separate, later A load would make every
+//     wait drain the whole ring).
+//   * Per group: the A slices go to an LDS stage (two stages, one barrier per group), then
+//     one 16x16x128 MFMA and four promotion FMAs per 16-row sub-tile of A.
+//   * Every load is a range-checked buffer load (zeros past the last row) at a clamped
+//     group index; the ring's loads and waits are explicit (asm_load_b128, vm_wait).
+template <int MT, int NW, int KS, int D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
 {
-    constexpr int THREADS = 64 * NW;
+    constexpr int THREADS = 64 * NW * KS;
+    constexpr int KTHREADS = 64 * NW;                         // threads of one K split
     constexpr int AROWS = 16 * MT;
-    constexpr int ACHUNKS = AROWS * 8;                       // 16-byte chunks per A group
-    constexpr int AREG = (ACHUNKS + THREADS - 1) / THREADS;  // per thread
-    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][AROWS * kGroup];
-    __shared__ float smS[2][AROWS];
+    constexpr int ACHUNKS = AROWS * 8;                        // 16-byte chunks per A group
+    constexpr int AREG = (ACHUNKS + KTHREADS - 1) / KTHREADS; // per thread
+    constexpr int ABYTES = AROWS * kGroup;
+    static_assert(KS == 1 || (KS - 1) * NW * MT * 64 * 16 <= 2 * KS * ABYTES,
+                  "the K-split partials fit in the A stages");
+    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][KS][ABYTES];
+    __shared__ float smS[2][KS][AROWS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % NW, ks = wave / NW;   // B rows of the wave, its K split
+    const int ktid = tid - ks * KTHREADS;       // thread index within the K split
     const int lq = lane >> 4, lr = lane & 15;
     const int64_t M = g.M, N = g.N, K = g.K;
     const int nk = g.nk;
-    const int64_t nw0 = (int64_t)blockIdx.x * (16 * NW) + 16 * wave;   // this wave's first B row
+    const int64_t nw0 = (int64_t)blockIdx.x * (16 * NW) + 16 * wn;   // this wave's first B row
+    // this wave's groups: [gbeg, gend); every split takes gps steps (uniform barriers)
+    const int gps = (nk + KS - 1) / KS;
+    const int gbeg = ks * gps, gend = min(nk, gbeg + gps);
 
     // B: this wave's 16 rows
     int64_t browsv = N - nw0;
     browsv = browsv < 0 ? 0 : (browsv > 16 ? 16 : browsv);
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.B + (nw0 < N ? nw0 : 0) * K), 0, (int)(browsv * K), kBufFlags);
+    const v4i_sgpr rB = make_rsrc_sgpr(g.B + (nw0 < N ? nw0 : 0) * K, (uint32_t)(browsv * K));
     const uint32_t boff = (uint32_t)(lr * K + 32 * lq);
     // per-block B scale row of this wave (clamped inside sb; a wave past N has zero B rows)
     const int64_t nblk = (nw0 < N ? nw0 : N - 1) / kGroup;
-    const float *sbw = g.sb + nblk * nk;
+    const v4i_sgpr rSB = make_rsrc_sgpr(g.sb + nblk * nk, (uint32_t)(nk * 4));
     // A: rows 0 .. M-1 (rows up to 16 MT - 1 read as zeros)
     const int64_t arows = M < AROWS ? M : AROWS;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)g.A, 0, (int)(arows * K), kBufFlags);
-    const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)g.sa, 0, (int)(arows * nk * 4), kBufFlags);
+    const v4i_sgpr rA = make_rsrc_sgpr(g.A, (uint32_t)(arows * K));
+    const v4i_sgpr rSA = make_rsrc_sgpr(g.sa, (uint32_t)(arows * nk * 4));
 
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    // A chunk c of a group: row c / 8, 16-byte chunk c % 8; thread t takes chunks
-    // (t + i * THREADS) mod ACHUNKS (duplicates write identical bytes to the same place)
-    auto a_chunk = [&](int i) { return (tid + i * THREADS) % ACHUNKS; };
+    typedef u32x4_t u32x4;
+    // A chunk c of a group: row c / 8, 16-byte chunk c % 8; thread t of the split takes
+    // chunks (t + i * KTHREADS) mod ACHUNKS (duplicates write identical bytes to one place)
+    auto a_chunk = [&](int i) { return (ktid + i * KTHREADS) % ACHUNKS; };
     auto lds_off = [](int row, int c) -> int {
         return (row >> 4) * 2048 + (c & 1) * 1024 + (((row & 15) + 16 * (c >> 1)) << 4);
     };
-    u32x4 ra[AREG];
-    float rsa = 0.0f;
-    auto load_a = [&](int grp) {
-        const bool ok = grp < nk;
-#pragma unroll
-        for (int i = 0; i < AREG; ++i) {
-            const int c = a_chunk(i);
-            const uint32_t off = ok ? (uint32_t)((c >> 3) * K + (int64_t)grp * kGroup + ((c & 7) << 4))
-                                    : kOutOfRange;
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
-        }
-        const uint32_t soff = ok ? (uint32_t)(((tid % AROWS) * nk + grp) * 4) : kOutOfRange;
-        rsa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rSA, soff, 0, 0));
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < AREG; ++i) {
-            const int c = a_chunk(i);
-            *reinterpret_cast<u32x4 *>(&smA[buf][lds_off(c >> 3, c & 7)]) = ra[i];
-        }
-        smS[buf][tid % AROWS] = rsa;
-    };
 
-    // B ring: slot j holds group g (g % D == j) as two 16-byte halves
-    u32x4 rbr[D][2];
-    auto load_b = [&](int j, int grp) {
-        const uint32_t off = grp < nk ? boff + (uint32_t)grp * kGroup : kOutOfRange;
-        rbr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
-        rbr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rB, off + 16, 0, 0);
+    // the ring
+    u32x4 rbr[D][2];      // B fragment halves
+    u32x4 rar[D][AREG];   // this thread's A chunks
+    float rsr[D];         // this thread's A row scale
+    float rsb[D];         // the wave's B block scale (same address in every lane)
+    // Steps past the split's range re-read a valid group (clamped index: no select on the
+    // address, which the compiler would turn into branches around the loads); their B scale
+    // reads as zero.
+    const int glast = nk > 0 ? nk - 1 : 0;
+    constexpr int LPS = 2 + AREG + 2;   // loads per ring slot
+    auto load_slot = [&](int j, int step_idx) {
+        const int grp = gbeg + step_idx;
+        const int gc = min(grp, glast);
+        const uint32_t off = boff + (uint32_t)gc * kGroup;
+        rbr[j][0] = asm_load_b128(rB, off);
+        rbr[j][1] = asm_load_b128(rB, off + 16);
+#pragma unroll
+        for (int i = 0; i < AREG; ++i) {
+            const int c = a_chunk(i);
+            const uint32_t aoff = (uint32_t)((c >> 3) * K + (int64_t)gc * kGroup + ((c & 7) << 4));
+            rar[j][i] = asm_load_b128(rA, aoff);
+        }
+        const uint32_t soff = (uint32_t)(((ktid % AROWS) * nk + gc) * 4);
+        rsr[j] = asm_load_b32(rSA, soff);
+        rsb[j] = asm_load_b32(rSB, (uint32_t)(grp < gend ? grp * 4 : nk * 4));
+    };
+    // slot j's loads are the oldest in flight: (D - 1) slots were loaded after them
+    auto wait_slot = [&](int j) {
+        vm_wait<(D - 1) * LPS>();
+        // the loaded registers are defined only now
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            asm volatile("" : "+v"(rbr[j][h]));
+#pragma unroll
+        for (int i = 0; i < AREG; ++i)
+            asm volatile("" : "+v"(rar[j][i]));
+        asm volatile("" : "+v"(rsr[j]));
+        asm volatile("" : "+v"(rsb[j]));
     };
 
     v4f acc[MT];
@@ -489,11 +553,25 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_skinny(GemmArgs g)
         acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    // one group: MFMAs from LDS stage `buf` and ring slot j, then refill slot j with group
-    // grp + D, then move the next A group (already in registers) into the other stage
-    auto step = [&](int j, int grp, int buf) {
-        load_a(grp + 1);
-        const float sb = sbw[grp < nk ? grp : nk - 1];   // past nk: B is zero anyway
+    // one group from ring slot j: A slices -> LDS stage buf, barrier, MFMAs, refill slot j
+    // with the group D steps later, promotion
+    auto step = [&](int j, int step_idx, int buf) {
+        wait_slot(j);
+        uint8_t *sA = smA[buf][ks];
+#pragma unroll
+        for (int i = 0; i < AREG; ++i) {
+            const int c = a_chunk(i);
+            *reinterpret_cast<u32x4 *>(&sA[lds_off(c >> 3, c & 7)]) = rar[j][i];
+        }
+        smS[buf][ks][ktid % AROWS] = rsr[j];
+        stage_barrier();
+        // scale products first: no value of slot j may stay live across its refill (the
+        // compiler would keep old and new in different registers and rotate them at the back
+        // edge, copying registers whose loads are still in flight)
+        float cs[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            cs[t] = smS[buf][ks][t * 16 + lr] * rsb[j];
         v8i bf;
         bf[0] = (int)rbr[j][0][0]; bf[1] = (int)rbr[j][0][1];
         bf[2] = (int)rbr[j][0][2]; bf[3] = (int)rbr[j][0][3];
@@ -502,7 +580,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_skinny(GemmArgs g)
         v4f p[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const uint8_t *q = &smA[buf][t * 2048 + lane * 16];
+            const uint8_t *q = &sA[t * 2048 + lane * 16];
             const uint4 lo = *reinterpret_cast<const uint4 *>(q);
             const uint4 hi = *reinterpret_cast<const uint4 *>(q + 1024);
             v8i af;
@@ -517,34 +595,64 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_skinny(GemmArgs g)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
             asm volatile("" : "+v"(p[t]));
-        load_b(j, grp + D);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            asm volatile("" : "+v"(cs[t]));
+        load_slot(j, step_idx + D);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const float c = smS[buf][t * 16 + lr] * sb;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                acc[t][r] = __builtin_fmaf(p[t][r], c, acc[t][r]);
+                acc[t][r] = __builtin_fmaf(p[t][r], cs[t], acc[t][r]);
         }
-        store_a(buf ^ 1);
-        stage_barrier();
     };
 
-    // prologue: A group 0 into stage 0, B groups 0 .. D-1 into the ring
-    load_a(0);
+    // prologue: the first D steps into the ring
 #pragma unroll
     for (int j = 0; j < D; ++j)
-        load_b(j, j);
-    store_a(0);
-    stage_barrier();
-    // main loop: D groups per iteration (the ring slot of each is then a constant); groups
-    // past nk read zeros and add nothing
+        load_slot(j, j);
+    // main loop: D steps per iteration (the ring slot of each is then a constant); steps
+    // outside the split's groups add nothing (zero B scale)
 #pragma nounroll
-    for (int g0 = 0; g0 < nk; g0 += D) {
+    for (int s0 = 0; s0 < gps; s0 += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j)
-            step(j, g0 + j, j & 1);
+            step(j, s0 + j, j & 1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): ring loads past the end land first
+    // The last refills are never read, so without a use the compiler would hand their
+    // registers to the epilogue while the loads are still landing: wait for all of them,
+    // then name every ring register, so that they stay reserved until here.
+    vm_wait<0>();
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        asm volatile("" : "+v"(rbr[j][0]), "+v"(rbr[j][1]));
+#pragma unroll
+        for (int i = 0; i < AREG; ++i)
+            asm volatile("" : "+v"(rar[j][i]));
+        asm volatile("" : "+v"(rsr[j]), "+v"(rsb[j]));
+    }
+
+    // the K splits' partial sums meet in LDS (reusing the A stages) and split 0 adds them in
+    // split order, so the result does not depend on timing
+    if (KS > 1) {
+        v4f *red = reinterpret_cast<v4f *>(&smA[0][0][0]);
+        stage_barrier();   // every wave is done with the A stages
+        if (ks > 0) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                red[(((ks - 1) * NW + wn) * MT + t) * 64 + lane] = acc[t];
+        }
+        stage_barrier();
+        if (ks > 0)
+            return;
+#pragma unroll
+        for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v4f o = red[(((k2 - 1) * NW + wn) * MT + t) * 64 + lane];
+                acc[t] += o;
+            }
+    }
 
     // epilogue: lane holds C[m][n..n+3], m = 16 t + lane % 16, n = nw0 + 4 (lane / 16)
     const int64_t n = nw0 + 4 * lq;
@@ -595,19 +703,24 @@ enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_S
 #define QR_SKINNY_NW 4
 #endif
 #ifndef QR_SKINNY_D
-#define QR_SKINNY_D 8
+#define QR_SKINNY_D 4
 #endif
-constexpr int kSkinnyNW = QR_SKINNY_NW;   // waves per workgroup (16 B rows each)
-constexpr int kSkinnyD = QR_SKINNY_D;     // B groups in flight per wave
+#ifndef QR_SKINNY_KS
+#define QR_SKINNY_KS 1
+#endif
+constexpr int kSkinnyNW = QR_SKINNY_NW;   // wave columns per workgroup (16 B rows each)
+constexpr int kSkinnyKS = QR_SKINNY_KS;   // K splits per workgroup (wave rows)
+constexpr int kSkinnyD = QR_SKINNY_D;     // groups in flight per wave
 
 template <int MT>
 hipError_t launch_skinny(bool out_bf16, const GemmArgs &a, hipStream_t stream)
 {
     const int64_t blocks = (a.N + 16 * kSkinnyNW - 1) / (16 * kSkinnyNW);
+    constexpr int threads = 64 * kSkinnyNW * kSkinnyKS;
     if (out_bf16)
-        k_gemm_skinny<MT, kSkinnyNW, kSkinnyD, true><<<(unsigned)blocks, 64 * kSkinnyNW, 0, stream>>>(a);
+        k_gemm_skinny<MT, kSkinnyNW, kSkinnyKS, kSkinnyD, true><<<(unsigned)blocks, threads, 0, stream>>>(a);
     else
-        k_gemm_skinny<MT, kSkinnyNW, kSkinnyD, false><<<(unsigned)blocks, 64 * kSkinnyNW, 0, stream>>>(a);
+        k_gemm_skinny<MT, kSkinnyNW, kSkinnyKS, kSkinnyD, false><<<(unsigned)blocks, threads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
