@@ -45,7 +45,7 @@ struct TileCfg {
     static constexpr int CA = BM * 8 / THREADS;            // 16-byte A chunks per thread
     static constexpr int CB = BN * 8 / THREADS;            // 16-byte B chunks per thread
     static_assert((BM / 8) % (WM * WN) == 0 && (BN / 8) % (WM * WN) == 0,
-                  "whole 16-row x 4-chunk load units per wave");
+                  "whole 8-row x 8-chunk load units per wave");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
     static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "chunk split");
     static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns lie in one 128-block");
@@ -117,14 +117,19 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 
     // ---- LDS layout, fragment-major: a 16-row sub-tile (16 rows x 128 bytes) is stored as
     // the two 1 KB halves of its MFMA operand fragment.  Lane l of the fragment holds row
-    // l % 16, bytes 32 * (l / 16) .. +32; half h keeps bytes 16h .. 16h+15 of that, at
-    // offset h * 1024 + 16 * l.  A fragment read is then two linear 1 KB reads (the fastest
-    // LDS read pattern on gfx950: ~1.3x a conflict-free swizzled row-major layout), and the
-    // scatter moves to the 16-byte stores, whose rate does not depend on the pattern.
-    // Row r, 16-byte chunk c goes to sub-tile r / 16, half c % 2, lane (r % 16) + 16 * (c / 2).
+    // l % 16, bytes 32 * (l / 16) .. +32; half h keeps bytes 16h .. 16h+15 of that.  Within
+    // a half, the 16-byte slot of (row r, chunk c) is ((r % 16) ^ (2c % 16)) + 16 * (c / 2):
+    // every 16 lanes of a fragment read then cover one 256-byte span (all banks once), and so
+    // do every 16 lanes of a store instruction, which writes 2 rows x 8 chunks (the global
+    // loads read whole 128-byte lines: 8 rows x 128 bytes per wave instruction).
     auto lds_off = [](int row, int c) -> int {
-        return (row >> 4) * 2048 + (c & 1) * 1024 + (((row & 15) + 16 * (c >> 1)) << 4);
+        return (row >> 4) * 2048 + (c & 1) * 1024 +
+               ((((row & 15) ^ ((2 * c) & 15)) + 16 * (c >> 1)) << 4);
     };
+    // this lane's byte offsets of its two fragment halves within a sub-tile
+    const int fq = lane >> 4;
+    const int frag_lo = ((((lane & 15) ^ ((4 * fq) & 15)) + 16 * fq) << 4);
+    const int frag_hi = 1024 + ((((lane & 15) ^ ((4 * fq + 2) & 15)) + 16 * fq) << 4);
     //
     // ---- global loads: buffer loads into registers.  Each operand tile gets a buffer
     // descriptor whose range ends at its last valid row, so rows past M or N read as zeros
@@ -161,17 +166,17 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const uint32_t soff = (uint32_t)(sidx * nk * 4);
 
     // Per-step data movement in slots: slot j < CA + CB is one 16-byte chunk per lane of A or
-    // B, slot CA + CB is the thread's scale.  One slot of a wave covers 16 rows x 4 chunks:
-    // wave instruction u (u = wave + j * waves) takes rows 16 * (u / 2) + lane % 16 and
-    // chunks 4 * (u % 2) + lane / 16, so each row reads 64 contiguous bytes from memory and
-    // each 16-lane group stores 16 different rows, i.e. 16 distinct LDS bank groups in the
-    // fragment-major layout.  load_slot fills the slot's register from global memory for
-    // step kg; store_slot writes it to the LDS stage (dA, dB, dS).
+    // B, slot CA + CB is the thread's scale.  One slot of a wave covers 8 rows x 8 chunks:
+    // wave instruction u (u = wave + j * waves) takes rows 8 u + lane / 8 and chunk lane % 8,
+    // so it reads 8 whole 128-byte lines from memory, and each 16-lane group stores 2 rows x
+    // 8 chunks, 16 distinct LDS bank groups in the swizzled layout.  load_slot fills the
+    // slot's register from global memory for step kg; store_slot writes it to the LDS stage
+    // (dA, dB, dS).
     constexpr int NSLOT = T::CA + T::CB + 1;
     constexpr int NW = T::WM * T::WN;
-    const int lrow = lane & 15, lchunk = lane >> 4;
-    auto slot_row = [&](int u) { return 16 * (u >> 1) + lrow; };
-    auto slot_chunk = [&](int u) { return 4 * (u & 1) + lchunk; };
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    auto slot_row = [&](int u) { return 8 * u + lrow; };
+    auto slot_chunk = [&](int u) { (void)u; return lchunk; };
     // Branch-free on purpose: straight-line code lets the scheduler interleave the slots with
     // the MFMAs and lets the compiler track each load's wait exactly.
     auto load_slot = [&](int j, int kg) {
@@ -209,9 +214,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 
     // Operand fragment of the 16-row sub-tile starting at (uniform) row r0.
     auto frag = [&](const uint8_t *tileBase, int r0) -> v8i {
-        const uint8_t *p = tileBase + (r0 >> 4) * 2048 + lane * 16;
-        const uint4 lo = *reinterpret_cast<const uint4 *>(p);
-        const uint4 hi = *reinterpret_cast<const uint4 *>(p + 1024);
+        const uint8_t *p = tileBase + (r0 >> 4) * 2048;
+        const uint4 lo = *reinterpret_cast<const uint4 *>(p + frag_lo);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(p + frag_hi);
         v8i f;
         f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
         f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
