@@ -118,18 +118,19 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     // ---- LDS layout, fragment-major: a 16-row sub-tile (16 rows x 128 bytes) is stored as
     // the two 1 KB halves of its MFMA operand fragment.  Lane l of the fragment holds row
     // l % 16, bytes 32 * (l / 16) .. +32; half h keeps bytes 16h .. 16h+15 of that.  Within
-    // a half, the 16-byte slot of (row r, chunk c) is ((r % 16) ^ (2c % 16)) + 16 * (c / 2):
-    // every 16 lanes of a fragment read then cover one 256-byte span (all banks once), and so
-    // do every 16 lanes of a store instruction, which writes 2 rows x 8 chunks (the global
-    // loads read whole 128-byte lines: 8 rows x 128 bytes per wave instruction).
+    // a half, the 16-byte slot of (row r, chunk c) is ((r % 16) ^ sw(c)) + 16 * (c / 2) with
+    // sw(c) = c + 8 (c % 2): every 8 and every 16 consecutive lanes of a fragment read or of
+    // a store instruction (which writes 2 rows x 8 chunks; the global loads read whole
+    // 128-byte lines, 8 rows x 128 bytes per wave instruction) then touch distinct 16-byte
+    // bank groups of a 128- and of a 256-byte span.
     auto lds_off = [](int row, int c) -> int {
-        return (row >> 4) * 2048 + (c & 1) * 1024 +
-               ((((row & 15) ^ ((2 * c) & 15)) + 16 * (c >> 1)) << 4);
+        const int sw = (c + 8 * (c & 1)) & 15;
+        return (row >> 4) * 2048 + (c & 1) * 1024 + ((((row & 15) ^ sw) + 16 * (c >> 1)) << 4);
     };
-    // this lane's byte offsets of its two fragment halves within a sub-tile
+    // this lane's byte offsets of its two fragment halves within a sub-tile (chunks 2q, 2q+1)
     const int fq = lane >> 4;
-    const int frag_lo = ((((lane & 15) ^ ((4 * fq) & 15)) + 16 * fq) << 4);
-    const int frag_hi = 1024 + ((((lane & 15) ^ ((4 * fq + 2) & 15)) + 16 * fq) << 4);
+    const int frag_lo = ((((lane & 15) ^ ((2 * fq) & 15)) + 16 * fq) << 4);
+    const int frag_hi = 1024 + ((((lane & 15) ^ ((2 * fq + 9) & 15)) + 16 * fq) << 4);
     //
     // ---- global loads: buffer loads into registers.  Each operand tile gets a buffer
     // descriptor whose range ends at its last valid row, so rows past M or N read as zeros
