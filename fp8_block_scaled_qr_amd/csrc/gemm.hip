@@ -67,6 +67,12 @@ struct GemmArgs {
 constexpr int kBufFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past every descriptor's extent
 
+// The promotion of a unit's partial sum runs QR_PROMOTE_LAG MFMAs after the MFMA that made it,
+// so the VALU never waits on the MFMA result.
+#ifndef QR_PROMOTE_LAG
+#define QR_PROMOTE_LAG 3
+#endif
+
 // Workgroup barrier for the LDS stage ring, without the memory fence of __syncthreads():
 // that fence would also wait for the next steps' global loads still in flight.  Ordering is
 // explicit: each wave waits for its own LDS accesses (lgkmcnt(0)) so that the stage it wrote
@@ -256,14 +262,15 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         // Software pipeline over single MFMAs (one M sub-tile x one N sub-tile): the MFMA of
         // unit u shares a scheduling region with the promotion FMAs of unit u-1, so the MFMA
         // pipe and the VALU work side by side and only two partials are live.
-        v4f pbuf[2];
+        constexpr int NP = QR_PROMOTE_LAG + 1;   // partial buffers
+        v4f pbuf[NP];
         auto promote = [&](int u) {
             const int i = u / T::JN, j = u % T::JN;
             const float ci = sav[i] * sbw;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float c = BSCALE == BSCALE_ROW ? sav[i] * sbv[j][r] : ci;
-                acc[i][j][r] = __builtin_fmaf(pbuf[u & 1][r], c, acc[i][j][r]);
+                acc[i][j][r] = __builtin_fmaf(pbuf[u % NP][r], c, acc[i][j][r]);
             }
         };
         // A fragments double-buffered: sub-tile i+1's fragment is read from LDS while
@@ -275,10 +282,10 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             const int i = u / T::JN, j = u % T::JN;
             if (j == 0 && i + 1 < T::IM)
                 afb[(i + 1) & 1] = frag(tA, wm * T::TM + (i + 1) * 16);
-            pbuf[u & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], afb[i & 1], zero,
-                                                                          0, 0, 0, 127, 0, 127);
-            if (u > 0)
-                promote(u - 1);
+            pbuf[u % NP] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], afb[i & 1], zero,
+                                                                           0, 0, 0, 127, 0, 127);
+            if (u >= QR_PROMOTE_LAG)
+                promote(u - QR_PROMOTE_LAG);
             // data movement, spread over the units: store slot u, then reload it
             if (u < NSLOT) {
                 store_slot(u, nA, nB, nS);
@@ -286,7 +293,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        promote(T::IM * T::JN - 1);
+#pragma unroll
+        for (int u = T::IM * T::JN - QR_PROMOTE_LAG; u < T::IM * T::JN; ++u)
+            promote(u);
 #pragma unroll
         for (int j = T::IM * T::JN; j < NSLOT; ++j) {
             store_slot(j, nA, nB, nS);
