@@ -73,6 +73,75 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past every descript
 #define QR_PROMOTE_LAG 3
 #endif
 
+// Raw buffer loads issued through inline asm, for a register ring whose waits are counted by
+// hand: the compiler does not see these as memory operations, so it inserts no waits of its
+// own for them (its waits around a loop back edge drain the whole ring).  The caller waits
+// with vm_wait<N>() before the first use, where N is the number of loads issued after the
+// one needed (loads retire in order).  The descriptor is four SGPRs: base address, stride 0,
+// extent in bytes, raw-buffer flags; offsets at or past the extent read zeros.
+typedef int v4i_sgpr __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i_sgpr make_rsrc_sgpr(const void *base, uint32_t extent)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4i_sgpr r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)extent);
+    r[3] = kBufFlags;
+    return r;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t asm_load_b128(const v4i_sgpr &rsrc, uint32_t off)
+{
+    u32x4_t v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+__device__ __forceinline__ float asm_load_b32(const v4i_sgpr &rsrc, uint32_t off)
+{
+    float v;
+    asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+// Every register an asm load writes must stay live (be named by a later asm statement) until
+// the vm_wait that covers the load: the compiler does not know the write is still pending
+// and would otherwise reuse the register.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Direct-to-LDS loads issued through inline asm: the buffer load writes lane i's 16 (or 4)
+// bytes to LDS address M0 + 16 i (4 i).  The compiler does not see them as memory
+// operations, so it adds no waits for them (it cannot tell that they fill the other LDS
+// stage and would otherwise wait for them before every read of the current one); the caller
+// waits with vm_wait before the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const v4i_sgpr &rsrc, uint32_t lds_addr, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const v4i_sgpr &rsrc, uint32_t lds_addr, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object (uniform).
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
 // Workgroup barrier for the LDS stage ring, without the memory fence of __syncthreads():
 // that fence would also wait for the next steps' global loads still in flight.  Ordering is
 // explicit: each wave waits for its own LDS accesses (lgkmcnt(0)) so that the stage it wrote
@@ -89,16 +158,21 @@ __device__ __forceinline__ void stage_barrier()
 template <class T, int BSCALE, bool OUT_BF16>
 __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 {
-    // Scales staged per step: BM row scales of A, then BN row scales (per-row B scales) or
-    // the tile's per-block B scales.
+    // Scales staged per step: BM row scales of A, then the B scales (BN row scales, or the
+    // tile's per-block scales; a scale load fills 64 slots, extras duplicate the last one).
     constexpr int NSB = BSCALE == BSCALE_ROW ? T::BN : (T::BN >= kGroup ? T::BN / kGroup : 1);
-    static_assert(T::BM + NSB <= T::THREADS, "one scale per thread per step");
+    constexpr int NW = T::WM * T::WN;
+    constexpr int NSA_I = T::BM / 64;                               // A-scale loads per step
+    constexpr int NSB_I = BSCALE == BSCALE_ROW ? T::BN / 64 : 1;    // B-scale loads per step
+    constexpr int SB_SLOTS = NSB_I * 64;
+    static_assert(NSA_I + NSB_I <= NW, "one scale load per wave and step at most");
+    constexpr int DA = T::BM / 8 / NW, DB = T::BN / 8 / NW;         // 1 KB tile loads per wave
+    static_assert(DA * 8 * NW == T::BM && DB * 8 * NW == T::BN, "whole 1 KB loads per wave");
 
-    // Two LDS stages per operand.  One scale slot per thread and stage: [0, BM) A row scales,
-    // [BM, BM + NSB) B scales, the rest unused.
+    // Two LDS stages per operand; the global loads write them directly (no register staging).
     __shared__ __attribute__((aligned(1024))) uint8_t smA[2][T::BM * kGroup];
     __shared__ __attribute__((aligned(1024))) uint8_t smB[2][T::BN * kGroup];
-    __shared__ __attribute__((aligned(16))) float sS[2][T::THREADS];
+    __shared__ __attribute__((aligned(256))) float sS[2][T::BM + SB_SLOTS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index: uniform across the wave, so say so (scalar offsets stay scalar)
@@ -121,95 +195,61 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const int64_t M = g.M, N = g.N, K = g.K;
     const int nk = g.nk;
 
-    // ---- LDS layout, fragment-major: a 16-row sub-tile (16 rows x 128 bytes) is stored as
-    // the two 1 KB halves of its MFMA operand fragment.  Lane l of the fragment holds row
-    // l % 16, bytes 32 * (l / 16) .. +32; half h keeps bytes 16h .. 16h+15 of that.  Within
-    // a half, the 16-byte slot of (row r, chunk c) is ((r % 16) ^ sw(c)) + 16 * (c / 2) with
-    // sw(c) = c + 8 (c % 2): every 8 and every 16 consecutive lanes of a fragment read or of
-    // a store instruction (which writes 2 rows x 8 chunks; the global loads read whole
-    // 128-byte lines, 8 rows x 128 bytes per wave instruction) then touch distinct 16-byte
-    // bank groups of a 128- and of a 256-byte span.
-    auto lds_off = [](int row, int c) -> int {
-        const int sw = (c + 8 * (c & 1)) & 15;
-        return (row >> 4) * 2048 + (c & 1) * 1024 + ((((row & 15) ^ sw) + 16 * (c >> 1)) << 4);
-    };
-    // this lane's byte offsets of its two fragment halves within a sub-tile (chunks 2q, 2q+1)
-    const int fq = lane >> 4;
-    const int frag_lo = ((((lane & 15) ^ ((2 * fq) & 15)) + 16 * fq) << 4);
-    const int frag_hi = 1024 + ((((lane & 15) ^ ((2 * fq + 9) & 15)) + 16 * fq) << 4);
-    //
-    // ---- global loads: buffer loads into registers.  Each operand tile gets a buffer
-    // descriptor whose range ends at its last valid row, so rows past M or N read as zeros
-    // (hardware range check on the per-lane offset, which carries the whole offset) and
-    // feed only outputs that are never stored.  Thread t loads 16-byte chunks
-    // c = t + i * THREADS: row c / 8, logical chunk c % 8, so 8 consecutive threads read one
-    // 128-byte row segment.  (Direct-to-LDS loads measured about 3x slower than this on gfx950
-    // for this access pattern.)
+    // ---- LDS layout: row-major, 128 bytes per row, with the 16-byte chunk c of row r stored
+    // in slot c ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2).  A global load instruction fills one
+    // contiguous 1 KB block, 8 rows x 128 bytes: lane i writes slot i % 8 of row i / 8, so it
+    // reads chunk (i % 8) ^ f(row) -- each row is one whole 128-byte line from memory.  An
+    // MFMA operand fragment (lane l: row l % 16, chunks 2 (l / 16) and 2 (l / 16) + 1) is
+    // then read with every 8 and every 16 consecutive lanes on distinct 16-byte bank groups
+    // (measured as fast as a linear read on gfx950).
+    auto swz = [](int row) { return (row & 7) ^ ((row >> 3) & 1); };
+    const int frow = lane & 15, fq = lane >> 4;
+    const int frag_lo = frow * 128 + (((2 * fq) ^ swz(frow)) << 4);
+    const int frag_hi = frow * 128 + (((2 * fq + 1) ^ swz(frow)) << 4);
+
+    // ---- global loads, straight into LDS.  Each operand tile has a buffer descriptor whose
+    // range ends at its last valid row, so rows past M or N load zeros.
     const int64_t rowsA = M - m0 < T::BM ? M - m0 : T::BM;
     const int64_t rowsB = N - n0 < T::BN ? N - n0 : T::BN;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.A + m0 * K), 0, (int)(rowsA * K), kBufFlags);
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.B + n0 * K), 0, (int)(rowsB * K), kBufFlags);
-    const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.sa + m0 * nk), 0, (int)(rowsA * nk * 4), kBufFlags);
+    const v4i_sgpr rA = make_rsrc_sgpr(g.A + m0 * K, (uint32_t)(rowsA * K));
+    const v4i_sgpr rB = make_rsrc_sgpr(g.B + n0 * K, (uint32_t)(rowsB * K));
+    const v4i_sgpr rSA = make_rsrc_sgpr(g.sa + m0 * nk, (uint32_t)(rowsA * nk * 4));
     // per-row B scales: rows n0.. of sb; per-block B scales: block rows n0/128.. of sb
     const int64_t sbRow0 = BSCALE == BSCALE_ROW ? n0 : n0 / kGroup;
     const int64_t sbRows = BSCALE == BSCALE_ROW ? rowsB
                            : ((n0 + rowsB + kGroup - 1) / kGroup) - n0 / kGroup;
-    const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.sb + sbRow0 * nk), 0, (int)(sbRows * nk * 4), kBufFlags);
-
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 ra[T::CA], rb[T::CB];
-    float rs = 0.0f;
-    // scale loaders: threads [0, BM) load A's row scales (whole waves, BM % 64 == 0), the
-    // others B scales (index clamped into [0, NSB): the extra lanes fill unused slots).  The
-    // descriptor choice is wave-uniform, so every lane loads without branching.
-    static_assert(T::BM % 64 == 0, "A-scale loaders are whole waves");
-    const bool wavesA = wave < T::BM / 64;
-    const __amdgpu_buffer_rsrc_t rS = wavesA ? rSA : rSB;
-    const int sidx = wavesA ? tid : min(tid - T::BM, NSB - 1);
-    const uint32_t soff = (uint32_t)(sidx * nk * 4);
-
-    // Per-step data movement in slots: slot j < CA + CB is one 16-byte chunk per lane of A or
-    // B, slot CA + CB is the thread's scale.  One slot of a wave covers 8 rows x 8 chunks:
-    // wave instruction u (u = wave + j * waves) takes rows 8 u + lane / 8 and chunk lane % 8,
-    // so it reads 8 whole 128-byte lines from memory, and each 16-lane group stores 2 rows x
-    // 8 chunks, 16 distinct LDS bank groups in the swizzled layout.  load_slot fills the
-    // slot's register from global memory for step kg; store_slot writes it to the LDS stage
-    // (dA, dB, dS).
-    constexpr int NSLOT = T::CA + T::CB + 1;
-    constexpr int NW = T::WM * T::WN;
-    const int lrow = lane >> 3, lchunk = lane & 7;
-    auto slot_row = [&](int u) { return 8 * u + lrow; };
-    auto slot_chunk = [&](int u) { (void)u; return lchunk; };
-    // Branch-free on purpose: straight-line code lets the scheduler interleave the slots with
-    // the MFMAs and lets the compiler track each load's wait exactly.
-    auto load_slot = [&](int j, int kg) {
-        const uint32_t k0 = (uint32_t)kg * kGroup;
-        if (j < T::CA) {
-            const int u = wave + j * NW;
-            ra[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                rA, (uint32_t)(slot_row(u) * K + (slot_chunk(u) << 4)) + k0, 0, 0);
-        } else if (j < T::CA + T::CB) {
-            const int u = wave + (j - T::CA) * NW;
-            rb[j - T::CA] = __builtin_amdgcn_raw_buffer_load_b128(
-                rB, (uint32_t)(slot_row(u) * K + (slot_chunk(u) << 4)) + k0, 0, 0);
-        } else {
-            rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, soff + kg * 4, 0, 0));
-        }
+    const v4i_sgpr rSB = make_rsrc_sgpr(g.sb + sbRow0 * nk, (uint32_t)(sbRows * nk * 4));
+    // tile loads: wave w issues loads t = w + j * NW (rows 8 t .. 8 t + 7)
+    const int lrow = lane >> 3, lslot = lane & 7;
+    auto tile_voff = [&](int t) -> uint32_t {
+        const int row = 8 * t + lrow;
+        return (uint32_t)(row * K + ((lslot ^ swz(row)) << 4));
     };
-    auto store_slot = [&](int j, uint8_t *dA, uint8_t *dB, float *dS) {
-        if (j < T::CA) {
-            const int u = wave + j * NW;
-            *reinterpret_cast<u32x4 *>(dA + lds_off(slot_row(u), slot_chunk(u))) = ra[j];
-        } else if (j < T::CA + T::CB) {
-            const int u = wave + (j - T::CA) * NW;
-            *reinterpret_cast<u32x4 *>(dB + lds_off(slot_row(u), slot_chunk(u))) = rb[j - T::CA];
-        } else {
-            dS[tid] = rs;
+    // scale loads: wave w < NSA_I loads A row scales 64 w .. 64 w + 63, wave NSA_I + s loads
+    // B scale slots 64 s .. (rows or blocks, clamped to the last valid index)
+    const bool sA_wave = wave < NSA_I, sB_wave = !sA_wave && wave < NSA_I + NSB_I;
+    const int sidx = sA_wave ? 64 * wave + lane : min(64 * (wave - NSA_I) + lane, NSB - 1);
+    const uint32_t soff = (uint32_t)(sidx * nk * 4);
+    const int sdst = sA_wave ? 64 * wave : T::BM + 64 * (wave - NSA_I);
+
+    const uint32_t ldsA = lds_addr_of(&smA[0][0]), ldsB = lds_addr_of(&smB[0][0]);
+    const uint32_t ldsS = lds_addr_of(&sS[0][0]);
+    const v4i_sgpr rS = sA_wave ? rSA : rSB;
+    auto issue_step = [&](int kg, int st) {
+        const uint32_t k0 = (uint32_t)kg * kGroup;
+#pragma unroll
+        for (int j = 0; j < DA; ++j) {
+            const int t = wave + j * NW;
+            dma16(rA, ldsA + (uint32_t)(st * T::BM * kGroup + t * 1024), tile_voff(t) + k0);
         }
+#pragma unroll
+        for (int j = 0; j < DB; ++j) {
+            const int t = wave + j * NW;
+            dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
+        }
+        if (sA_wave || sB_wave)
+            dma4(rS, ldsS + (uint32_t)((st * (T::BM + SB_SLOTS) + sdst) * 4),
+                 soff + (uint32_t)kg * 4);
     };
 
     v4f acc[T::IM][T::JN];
@@ -221,7 +261,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 
     // Operand fragment of the 16-row sub-tile starting at (uniform) row r0.
     auto frag = [&](const uint8_t *tileBase, int r0) -> v8i {
-        const uint8_t *p = tileBase + (r0 >> 4) * 2048;
+        const uint8_t *p = tileBase + r0 * 128;
         const uint4 lo = *reinterpret_cast<const uint4 *>(p + frag_lo);
         const uint4 hi = *reinterpret_cast<const uint4 *>(p + frag_hi);
         v8i f;
@@ -230,12 +270,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         return f;
     };
 
-    // compute(stage) also moves data: between its MFMAs it writes the registers (step k+1,
-    // loaded one step earlier) into the other stage and then refills each register with step
-    // k+2, so LDS stores and global loads overlap the MFMA pipe instead of bunching up at
-    // the barrier.
-    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS, uint8_t *nA,
-                       uint8_t *nB, float *nS, int kld) {
+    // compute(stage): the MFMAs of one K step from an LDS stage, with the promotions
+    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS) {
         const float *tSA = tS, *tSB = tS + T::BM;
         float sav[T::IM];
 #pragma unroll
@@ -259,9 +295,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         for (int j = 0; j < T::JN; ++j)
             bf[j] = frag(tB, wn * T::TN + j * 16);
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        // Software pipeline over single MFMAs (one M sub-tile x one N sub-tile): the MFMA of
-        // unit u shares a scheduling region with the promotion FMAs of unit u-1, so the MFMA
-        // pipe and the VALU work side by side and only two partials are live.
+        // Software pipeline over single MFMAs (one M sub-tile x one N sub-tile): the partial
+        // of unit u is promoted QR_PROMOTE_LAG units later, so the VALU never waits on it.
         constexpr int NP = QR_PROMOTE_LAG + 1;   // partial buffers
         v4f pbuf[NP];
         auto promote = [&](int u) {
@@ -286,53 +321,31 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
                                                                            0, 0, 0, 127, 0, 127);
             if (u >= QR_PROMOTE_LAG)
                 promote(u - QR_PROMOTE_LAG);
-            // data movement, spread over the units: store slot u, then reload it
-            if (u < NSLOT) {
-                store_slot(u, nA, nB, nS);
-                load_slot(u, kld);
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int u = T::IM * T::JN - QR_PROMOTE_LAG; u < T::IM * T::JN; ++u)
             promote(u);
-#pragma unroll
-        for (int j = T::IM * T::JN; j < NSLOT; ++j) {
-            store_slot(j, nA, nB, nS);
-            load_slot(j, kld);
-        }
     };
 
-    // ---- main loop: one 128-wide scale group per step, two LDS stages and one register
-    // stage.  Step k computes from LDS stage k%2 while it stores step k+1 (already in
-    // registers) into the other stage and loads step k+2 into the registers; the loads stay
-    // in flight across the (fence-free) barrier.  Near the end of the K range the stores and
-    // loads still run, unconditionally: loads re-read the last group (the index is clamped)
-    // and stores fill a stage that is never read again.  The loop is not unrolled: one copy
-    // of the step keeps every accumulator in the same registers from step to step.
+    // ---- main loop: one 128-wide scale group per step, two LDS stages.  Step k first issues
+    // the loads of step k+1 into the other stage (free: every wave finished reading it before
+    // the last barrier), then computes from its own stage; before the barrier each wave waits
+    // for its own loads, so after it the next stage is complete.  Past the end of the K range
+    // the loads re-read the last group (clamped) into a stage that is never read.
     const int glast = ge - 1;
-    if (gb < ge) {
-#pragma unroll
-        for (int j = 0; j < NSLOT; ++j)
-            load_slot(j, gb);
-#pragma unroll
-        for (int j = 0; j < NSLOT; ++j)
-            store_slot(j, smA[0], smB[0], sS[0]);
-#pragma unroll
-        for (int j = 0; j < NSLOT; ++j)
-            load_slot(j, min(gb + 1, glast));
-    }
+    if (gb < ge)
+        issue_step(gb, 0);
+    vm_wait<0>();
     stage_barrier();
 #pragma nounroll
     for (int kg = gb; kg < ge; ++kg) {
         const int st = (kg - gb) & 1;
-        compute(smA[st], smB[st], sS[st], smA[st ^ 1], smB[st ^ 1], sS[st ^ 1],
-                min(kg + 2, glast));
+        issue_step(min(kg + 1, glast), st ^ 1);
+        compute(smA[st], smB[st], sS[st]);
+        vm_wait<0>();   // this wave's loads of step k+1
         stage_barrier();
     }
-    // the loads issued for steps past the end are discarded; let them land before the
-    // registers are reused and the wave ends
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // ---- epilogue: lane holds C[m][n..n+3] for each sub-tile
     const bool vec_ok = (N & 3) == 0;
@@ -410,51 +423,6 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
                 reinterpret_cast<float *>(out)[i] = s;
         }
     }
-}
-
-// Raw buffer loads issued through inline asm, for a register ring whose waits are counted by
-// hand: the compiler does not see these as memory operations, so it inserts no waits of its
-// own for them (its waits around a loop back edge drain the whole ring).  The caller waits
-// with vm_wait<N>() before the first use, where N is the number of loads issued after the
-// one needed (loads retire in order).  The descriptor is four SGPRs: base address, stride 0,
-// extent in bytes, raw-buffer flags; offsets at or past the extent read zeros.
-typedef int v4i_sgpr __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ v4i_sgpr make_rsrc_sgpr(const void *base, uint32_t extent)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    v4i_sgpr r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)extent);
-    r[3] = kBufFlags;
-    return r;
-}
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x4_t asm_load_b128(const v4i_sgpr &rsrc, uint32_t off)
-{
-    u32x4_t v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
-    return v;
-}
-
-__device__ __forceinline__ float asm_load_b32(const v4i_sgpr &rsrc, uint32_t off)
-{
-    float v;
-    asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
-    return v;
-}
-
-// Every register an asm load writes must stay live (be named by a later asm statement) until
-// the vm_wait that covers the load: the compiler does not know the write is still pending
-// and would otherwise reuse the register.
-template <int N>
-__device__ __forceinline__ void vm_wait()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // ---------------------------------------------------------------- skinny M (decode)
@@ -706,13 +674,12 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
 }
 
 // Tile configurations, indexed by GemmPlan::cfg.
-using CfgBig2 = TileCfg<256, 128, 4, 2>;   // prefill / training: 8 waves, 64x64 per wave
 using CfgBig4 = TileCfg<256, 256, 2, 4>;   // prefill / training: 8 waves, 128x64 per wave
 using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
 using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
 using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
 
-enum { CFG_BIG = 0, CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_SKINNY = 5 };
+enum { CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_SKINNY = 5 };
 
 #ifndef QR_SKINNY_NW
 #define QR_SKINNY_NW 4
@@ -742,7 +709,6 @@ hipError_t launch_skinny(bool out_bf16, const GemmArgs &a, hipStream_t stream)
 void tile_dims(int cfg, int &bm, int &bn)
 {
     switch (cfg) {
-    case CFG_BIG: bm = CfgBig2::BM; bn = CfgBig2::BN; break;
     case CFG_BIG4: bm = CfgBig4::BM; bn = CfgBig4::BN; break;
     case CFG_SKINNY: bm = 64; bn = 16 * kSkinnyNW; break;
     case CFG_M64: bm = CfgM64::BM; bn = CfgM64::BN; break;
@@ -773,11 +739,10 @@ hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hi
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
 {
     GemmPlan p;
-    // Large M: 256x256 tiles (8 waves of 128x64) where the per-block B scale keeps the wave's
-    // promotion to one scale product per row; the per-row B scales of WGrad need more
-    // registers, so WGrad keeps 256x128 tiles (8 waves of 64x64).
+    // Large M: 256x256 tiles, 8 waves of 128x64 (the per-row B scales of WGrad fit too, now
+    // that the operand tiles go straight from memory to LDS without register staging).
     if (M > 256)
-        p.cfg = bscale == BSCALE_BLOCK ? CFG_BIG4 : CFG_BIG;
+        p.cfg = CFG_BIG4;
     else if (M <= 64 && bscale == BSCALE_BLOCK)
         p.cfg = CFG_SKINNY;   // decode: stream B once, no split
     else if (M <= 64)
@@ -791,7 +756,7 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t nk = K / kGroup;
     int64_t split = 1;
-    if (p.cfg != CFG_BIG && p.cfg != CFG_BIG4 && p.cfg != CFG_SKINNY && tiles > 0 && tiles < 512 &&
+    if (p.cfg != CFG_BIG4 && p.cfg != CFG_SKINNY && tiles > 0 && tiles < 512 &&
         nk > 0) {
         split = (512 + tiles - 1) / tiles;
         const int64_t max_split = nk / 4 > 1 ? nk / 4 : 1;   // keep >= 4 groups per split
@@ -836,7 +801,6 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     const int blocks = a.tilesM * a.tilesN * plan.split;
     hipError_t e;
     switch (plan.cfg) {
-    case CFG_BIG: e = launch_t<CfgBig2>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_BIG4: e = launch_t<CfgBig4>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M64: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M128: e = launch_t<CfgM128>(bscale, out_bf16, a, blocks, stream); break;
