@@ -139,6 +139,11 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
     __shared__ float4 row_sc[kTile], col_sc[kTile];
     __shared__ float4 blk_sc;
     __shared__ uint32_t tiny_flag[2];   // per iteration parity: some group of the tile is tiny
+    // Transposed codes of the tile, staged so that they leave as whole 128-byte column
+    // segments: row c holds column c0 + c (its 128 tile rows, one byte each); its 16-byte
+    // chunk k (tile rows 16 k .. 16 k + 15) sits in slot k ^ ((c / 8) % 8).
+    constexpr bool STAGE_T = COL || BLKT;
+    __shared__ __attribute__((aligned(16))) uint8_t tcodes[STAGE_T ? kTile * kTile : 16];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -150,6 +155,11 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
         const int64_t r0 = bi * kTile, c0 = bj * kTile;
         const int64_t col = c0 + 8 * oc;
         const bool colok = col < cols;
+        // 8 codes of tile column c, tile rows 8 oq .. 8 oq + 7, into the staging tile
+        auto stage_t = [&](int c, uint2 codes8) {
+            *reinterpret_cast<uint2 *>(tcodes + c * kTile + (((oq >> 1) ^ ((c >> 3) & 7)) << 4) +
+                                       8 * (oq & 1)) = codes8;
+        };
 
         // ---- maxima
         if (t == 0)
@@ -251,17 +261,12 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
                 if (BLKT) {
                     uint2 ct[8];
                     transpose8x8(c8, ct);
-                    const int64_t r = r0 + 8 * oq;   // rows % 8 == 0: the octet is all in or out
-                    if (colok && r < rows) {
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            *reinterpret_cast<uint2 *>(qT + (col + i) * rows + r) = ct[i];
-                    }
+                    for (int i = 0; i < 8; ++i)
+                        stage_t(8 * oc + i, ct[i]);
                 }
             }
             if (COL) {
-                const int64_t r = r0 + 8 * oq;       // rows % 8 == 0: the octet is all in or out
-                const bool ok = colok && r < rows;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const Scale sc = unpack_scale(col_sc[8 * oc + i]);
@@ -274,8 +279,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
                                   quot_t<LIFT>(bf16_elem(v[5], i), sc),
                                   quot_t<LIFT>(bf16_elem(v[6], i), sc),
                                   quot_t<LIFT>(bf16_elem(v[7], i), sc));
-                    if (ok)
-                        *reinterpret_cast<uint2 *>(qT + (col + i) * rows + r) = c8;
+                    stage_t(8 * oc + i, c8);
                 }
             }
         };
@@ -283,6 +287,31 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
             encode(std::true_type{});
         else
             encode(std::false_type{});
+
+        // ---- transposed codes leave the staging tile as whole column segments: a wave
+        // stores 8 columns x 128 bytes per instruction.  (The next tile writes the staging
+        // tile only after two more barriers, so one buffer is enough.)
+        if (STAGE_T) {
+            lds_barrier();
+            const bool whole16 = (rows & 15) == 0;   // every column segment 16-byte aligned
+#pragma unroll
+            for (int p = 0; p < kTile * kTile / 16 / 256; ++p) {
+                const int c = p * 32 + (t >> 3), ch = t & 7;
+                const uint4 d = *reinterpret_cast<const uint4 *>(
+                    tcodes + c * kTile + ((ch ^ ((c >> 3) & 7)) << 4));
+                const int64_t cc = c0 + c, r = r0 + 16 * ch;   // rows % 8 == 0
+                if (cc >= cols || r >= rows)
+                    continue;
+                uint8_t *dst = qT + cc * rows + r;
+                if (whole16 && r + 16 <= rows) {
+                    *reinterpret_cast<uint4 *>(dst) = d;
+                } else {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(d.x, d.y);
+                    if (r + 8 < rows)
+                        *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(d.z, d.w);
+                }
+            }
+        }
     };
 
     // Two register buffers in turn, so that the loads of one tile are always in flight while
@@ -328,11 +357,11 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
 
 // ---------------------------------------------------------------- UAQ fold
 
-// RN_bf16(w / s): the quotient is formed in binary64 (correctly rounded) and rounded to bf16
-// directly from there.  When w / s is not a bf16 midpoint it lies at least ~2^-33 (relative)
-// from every midpoint (w has 8 significant bits, s 24), far more than binary64's rounding
-// error, so this equals rounding the exact quotient once.  (Rounding through binary32 first
-// would not: binary32's 2^-24 step can land exactly on a midpoint.)
+// RN_bf16(w / s), general case: the quotient is formed in binary64 (correctly rounded) and
+// rounded to bf16 directly from there.  When w / s is not a bf16 midpoint it lies at least
+// ~2^-33 (relative) from every midpoint (w has 8 significant bits, s 24), far more than
+// binary64's rounding error, so this equals rounding the exact quotient once.  (Rounding
+// through binary32 first would not: binary32's 2^-24 step can land exactly on a midpoint.)
 __device__ __forceinline__ uint16_t fold1(uint32_t wbits, float s)
 {
     const float wv = __uint_as_float(wbits << 16);
@@ -349,28 +378,87 @@ __device__ __forceinline__ uint16_t fold1(uint32_t wbits, float s)
     return (uint16_t)((fb >> 16) | (wbits & 0x8000u));
 }
 
+// RN_bf16(w / s) for s > 0 with r = RN32(1 / s); `col_ok` says 2^-120 <= s < 2^121.
+// z = |w| / s is bracketed without division: q = RN32(|w| * r) is within (2u + u^2) z of z
+// (u = 2^-24: one rounding in r, one in the product), i.e. within 2.01 binary32 ulps of q.
+// Let lo be q truncated to bf16 and hi = lo + one bf16 ulp.  Then z lies between the bf16
+// midpoint below lo and the one above hi, so it rounds to lo or hi, and only its side of
+// their midpoint m = lo + ulp / 2 is left to decide.  That is the sign of |w| - m * s, taken
+// exactly from one FMA: |w| and m * s are multiples of 2^(E_w - 32) or coarser, so with
+// |w| >= 2^-90 a non-zero difference is at least 2^-122 and its rounding keeps its sign; zero
+// would be the tie (even neighbour).  `slow` flags the elements outside those ranges (tiny or
+// huge quotients or weights, s out of range, non-finite w), which take the binary64 route;
+// zero weights give the signed zero directly.
+__device__ __forceinline__ uint32_t fold_fast(uint32_t wbits, float s, float r, bool col_ok,
+                                              uint32_t &slow)
+{
+    const float a = __uint_as_float((wbits & 0x7FFFu) << 16);
+    const uint32_t qb = __float_as_uint(a * r);
+    const uint32_t ew = (wbits >> 7) & 0xFFu, eq = qb >> 23;
+    const uint32_t lo = qb & 0xFFFF0000u;
+    const float d = fmaf(-__uint_as_float(lo | 0x8000u), s, a);
+    const uint32_t up = d > 0.0f ? 1u : (d == 0.0f ? (lo >> 16) & 1u : 0u);
+    const bool zero = (wbits & 0x7FFFu) == 0;            // +-0 / s = +-0 for s > 0
+    const bool ok = col_ok && ew >= 37u && eq - 27u <= 220u;
+    slow = (ok || zero) ? 0u : 1u;
+    return zero ? wbits : (((lo >> 16) + up) | (wbits & 0x8000u));
+}
+
+// One wave covers 64 consecutive 8-column chunks of a row (1 KB of bf16); the grid's y
+// dimension and the 4 waves of a workgroup walk the rows, so each lane forms the reciprocals
+// of its 8 columns once and reuses them for every row it folds.
 __global__ __launch_bounds__(256) void k_uaq_fold(const uint16_t *w, int64_t n, int64_t k,
                                                   int64_t ldw, const float *__restrict__ s,
                                                   uint16_t *out, int64_t ldo, float *gain)
 {
-    const int64_t chunks_per_row = k / 8;
-    const int64_t total = n * chunks_per_row;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
-        const int64_t row = c / chunks_per_row, kc = (c - row * chunks_per_row) * 8;
-        const uint4 v = *reinterpret_cast<const uint4 *>(w + row * ldw + kc);
-        const float4 s0 = *reinterpret_cast<const float4 *>(s + kc);
-        const float4 s1 = *reinterpret_cast<const float4 *>(s + kc + 4);
-        uint4 o;
-        o.x = fold1(v.x & 0xFFFFu, s0.x) | ((uint32_t)fold1(v.x >> 16, s0.y) << 16);
-        o.y = fold1(v.y & 0xFFFFu, s0.z) | ((uint32_t)fold1(v.y >> 16, s0.w) << 16);
-        o.z = fold1(v.z & 0xFFFFu, s1.x) | ((uint32_t)fold1(v.z >> 16, s1.y) << 16);
-        o.w = fold1(v.w & 0xFFFFu, s1.z) | ((uint32_t)fold1(v.w >> 16, s1.w) << 16);
-        *reinterpret_cast<uint4 *>(out + row * ldo + kc) = o;
+    const int64_t kc = ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63)) * 8;
+    if (kc >= k)
+        return;
+    const float4 s0 = *reinterpret_cast<const float4 *>(s + kc);
+    const float4 s1 = *reinterpret_cast<const float4 *>(s + kc + 4);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float rv[8];
+    bool ok[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rv[j] = __fdiv_rn(1.0f, sv[j]);                 // correctly rounded
+        ok[j] = (__float_as_uint(sv[j]) >> 23) - 7u <= 240u;   // 2^-120 <= s < 2^121
     }
-    if (gain) {
-        for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < k; c += stride)
-            gain[c] = gain[c] * s[c];
+    auto fold_chunk = [&](uint4 v) {
+        const uint32_t wb[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                                v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+        uint32_t res[8], sl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            res[j] = fold_fast(wb[j], sv[j], rv[j], ok[j], sl[j]);
+        if (sl[0] | sl[1] | sl[2] | sl[3] | sl[4] | sl[5] | sl[6] | sl[7]) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sl[j])
+                    res[j] = fold1(wb[j], sv[j]);
+        }
+        return make_uint4(res[0] | (res[1] << 16), res[2] | (res[3] << 16),
+                          res[4] | (res[5] << 16), res[6] | (res[7] << 16));
+    };
+    const int64_t step = (int64_t)gridDim.y * 4;
+    int64_t row = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+    for (; row + 3 * step < n; row += 4 * step) {       // four rows in flight per lane
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = *reinterpret_cast<const uint4 *>(w + (row + u * step) * ldw + kc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<uint4 *>(out + (row + u * step) * ldo + kc) = fold_chunk(v[u]);
+    }
+    for (; row < n; row += step) {
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(w + row * ldw + kc);
+        *reinterpret_cast<uint4 *>(out + row * ldo + kc) = fold_chunk(v0);
+    }
+    if (gain && blockIdx.y == 0 && threadIdx.x < 64) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            gain[kc + j] = gain[kc + j] * sv[j];
     }
 }
 
@@ -432,13 +520,16 @@ hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
                            const float *s, uint16_t *w_out, int64_t ld_out, float *gain,
                            hipStream_t stream)
 {
-    const int64_t total = n * (k / 8);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 16384)
-        blocks = 16384;
-    if (blocks < 1)
-        blocks = 1;
-    k_uaq_fold<<<(unsigned)blocks, 256, 0, stream>>>(w, n, k, ld_w, s, w_out, ld_out, gain);
+    // x: 512-column slabs; y: row groups of 4 waves, about 8 rows per wave (capped so the
+    // grid stays within the y limit: the row loop covers the rest).
+    const int64_t gx = (k + 511) / 512;
+    int64_t gy = (n + 31) / 32;
+    if (gy > 65535)
+        gy = 65535;
+    if (gx == 0 || gy == 0)
+        return hipSuccess;
+    k_uaq_fold<<<dim3((unsigned)gx, (unsigned)gy), 256, 0, stream>>>(w, n, k, ld_w, s, w_out,
+                                                                     ld_out, gain);
     return hipGetLastError();
 }
 

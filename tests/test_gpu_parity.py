@@ -46,6 +46,7 @@ def test_quant_rows(rows, cols, name):
 
 
 DUAL_SHAPES = [(256, 512, "small"), (200, 136, "ragged rows and columns"), (8, 8, "minimal"),
+               (264, 392, "rows % 16 == 8 over several tiles"),
                (8192, 4096, "backward_8b dY full size")]
 
 
@@ -70,6 +71,7 @@ def test_quant_dual_and_colT(rows, cols, name):
 
 
 W_SHAPES = [(512, 512, "tiny_fprop W"), (200, 136, "ragged blocks"),
+            (392, 264, "n % 16 == 8 over several blocks"),
             (4096, 4096, "prefill_8b W"), (14336, 4096, "decode_8b W")]
 
 
@@ -181,6 +183,31 @@ def test_uaq_fold_random_and_near_midpoints():
     # in place, no gain
     qr.uaq_fold(wd, sd, None, inplace=True)
     assert_bitexact(host(wd), ro, "folded weight in place")
+
+
+@pytest.mark.parametrize("n,k", [(37, 520), (301, 1040), (1, 8)])
+def test_uaq_fold_edges_and_ragged(n, k):
+    """Ragged grids (rows not a multiple of 4, columns not a multiple of 512, several trips of
+    the row loop) and the rare per-element routes: signed zeros, bf16 subnormals, quotients
+    that overflow bf16 or fall to its subnormals, scales outside [2^-120, 2^121)."""
+    say("uaq fold edges", n, k)
+    rng = np.random.default_rng(n * 7 + k)
+    w = qr_synth.normal_bf16(71 + n, (n, k), 0.02)
+    s = rng.uniform(1.5, 4.0, k).astype(np.float32)
+    flat = w.reshape(-1)
+    pick = rng.choice(flat.size, size=max(1, flat.size // 20), replace=False)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8040, 0x007F, 0x7F7F, 0xFF7F, 0x0080,
+                         0x3F80], np.uint16)
+    flat[pick] = specials[rng.integers(0, specials.size, pick.size)]
+    if k >= 8:
+        s[:8] = np.array([2.0 ** -126, 2.0 ** -121, 1e-30, 2.0 ** 121, 1e30, 2.0 ** 127,
+                          np.float32(3.4e38), 1.0], np.float32)
+    gain = rng.uniform(0.5, 2.0, k).astype(np.float32)
+    gd = dev(gain.copy())
+    out = qr.uaq_fold(dev_bf16(w), dev(s), gd)
+    ro, rg = oracle.uaq_fold(w, s, gain)
+    assert_bitexact(host(out), ro, "folded weight")
+    assert_bitexact(host(gd), rg, "gain")
 
 
 # ================================================================= GEMMs

@@ -39,7 +39,7 @@ def _run_mutant(tmp_root, name, old, new):
     shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
                     ignore=shutil.ignore_patterns("*.so", "*.tmp", "__pycache__"))
     shutil.copytree(os.path.join(ROOT, "tests"), os.path.join(d, "tests"),
-                    ignore=shutil.ignore_patterns("__pycache__", "*.so", "quotient_check"))
+                    ignore=shutil.ignore_patterns("__pycache__", "*.so", "quotient_check", "fold_check"))
     shutil.copy(os.path.join(ROOT, "qr_synth.py"), d)
     src_path = os.path.join(d, "oracle", "qr_oracle.c")
     src = open(src_path).read()
