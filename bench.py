@@ -21,7 +21,8 @@ records events only around the dominant kernel's launch, so the step time carrie
 event overhead.  The JSON line reports the step's GEMM throughput (all GEMM flops / step
 time) as `value`, each op's time with its roofline fraction, the roofline of the dominant
 kernel from its launches in the timed pass, and the CPU oracle timed on a bounded token slice
-of the same step.
+of the same step.  Outside the step (it runs once per optimizer step) it also times the
+batched re-quantization of a 32B decoder layer's four weights (`weight_update`).
 """
 import argparse
 import hashlib
@@ -218,7 +219,51 @@ def run_gpu(args):
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(end) / args.steps
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
-    return step_ms, wall, per_op, dom, dom_ms
+    del st, ops
+    torch.cuda.empty_cache()
+    upd = run_weight_update(torch, qr)
+    return step_ms, wall, per_op, dom, dom_ms, upd
+
+
+def run_weight_update(torch, qr, iters=10):
+    """Quantize-on-update of the 32B decoder layer's four weights (QKV, O, gate+up, down),
+    each with its transposed copy, as one batched call; timed outside the step (it runs once
+    per optimizer step, not per token).  Inputs: seeded N(0, 0.02) on the device."""
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(6001)
+    shapes = [(7168, 5120), (5120, 5120), (55296, 5120), (5120, 27648)]
+    ws = [(torch.randn(sh, device=dev, generator=g) * 0.02).to(torch.bfloat16) for sh in shapes]
+    items = []
+    nbytes = 0
+    for w in ws:
+        n, k = w.shape
+        nb = ((n + 127) // 128) * ((k + 127) // 128)
+        q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        qT = torch.empty((k, n), dtype=torch.uint8, device=dev)
+        s = torch.empty(nb, dtype=torch.float32, device=dev)
+        sT = torch.empty(nb, dtype=torch.float32, device=dev)
+        items.append((w, n, k, k, q, s, qT, sT))
+        nbytes += n * k * (2 + 1 + 1) + 2 * nb * 4
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        qr.qr_quant_w_128x128_batched(items)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        qr.qr_quant_w_128x128_batched(items)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del ws, items
+    torch.cuda.empty_cache()
+    return {"workload": "32B decoder layer weights (QKV 7168x5120, O 5120x5120, gate+up "
+                        "55296x5120, down 5120x27648) re-quantized 128x128 with transposed "
+                        "copies, one batched call",
+            "us": round(us, 1), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": 1}
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -277,7 +322,7 @@ def main():
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, upd = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -312,6 +357,7 @@ def main():
                    "gemm_gflop_per_step": round(gemm_total / 1e9, 2)},
         "roofline": roof,
         "kernels": kernels,
+        "weight_update": upd,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -23,8 +23,16 @@ QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD = 0, 1, 2
 
 # Every entry point include/qr.h declares.
 EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant_w_128x128",
-           "qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad",
-           "qr_gemm_workspace_bytes", "qr_uaq_fold")
+           "qr_quant_w_128x128_batched", "qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad",
+           "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes", "qr_uaq_fold")
+QR_MAX_WEIGHT_BATCH = 4096
+
+
+class qr_weight_desc(ctypes.Structure):
+    """Mirror of the C struct qr_weight_desc (one weight of a batched quantization)."""
+    _fields_ = [("w_bf16", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("ld_w", ctypes.c_int64), ("q", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("qT", ctypes.c_void_p), ("sT", ctypes.c_void_p)]
 
 _lib = None
 
@@ -53,6 +61,8 @@ def load():
     L.qr_quant_act_1x128.restype = I32
     L.qr_quant_w_128x128.argtypes = [P, I64, I64, I64, P, P, P, P, P]
     L.qr_quant_w_128x128.restype = I32
+    L.qr_quant_w_128x128_batched.argtypes = [ctypes.POINTER(qr_weight_desc), I32, P]
+    L.qr_quant_w_128x128_batched.restype = I32
     for name in ("qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad"):
         f = getattr(L, name)
         f.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
@@ -105,6 +115,20 @@ def qr_quant_act_1x128(x, rows, cols, ld_x, q_row, s_row, q_colT, s_colT, stream
 def qr_quant_w_128x128(w, n, k, ld_w, q, s, qT, sT, stream=None):
     _check(load().qr_quant_w_128x128(_ptr(w), n, k, ld_w, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
                                      _stream(stream)), "qr_quant_w_128x128")
+
+
+def qr_quant_w_128x128_batched(items, stream=None):
+    """items: sequence of (w, n, k, ld_w, q, s, qT, sT) as for qr_quant_w_128x128 (qT, sT may
+    be None)."""
+    arr = (qr_weight_desc * max(1, len(items)))()
+    for i, (w, n, k, ld_w, q, s_, qT, sT) in enumerate(items):
+        arr[i] = qr_weight_desc(None if w is None else w.data_ptr(), n, k, ld_w,
+                                None if q is None else q.data_ptr(),
+                                None if s_ is None else s_.data_ptr(),
+                                None if qT is None else qT.data_ptr(),
+                                None if sT is None else sT.data_ptr())
+    _check(load().qr_quant_w_128x128_batched(arr, len(items), _stream(stream)),
+           "qr_quant_w_128x128_batched")
 
 
 def _gemm(name, a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream):
@@ -173,6 +197,27 @@ def quant_w(w, transposed=False, stream=None):
     qr_quant_w_128x128(w, n, k, w.stride(0), q, s, qT, sT, stream)
     return q, s, qT, sT
 
+
+
+def quant_w_batched(ws, transposed=False, stream=None):
+    """ws: list of bf16 [n, k] weights on the GPU, quantized in one call.  Returns a list of
+    (q, s, qT, sT) per weight; transposed is a bool or a list of bools."""
+    import torch
+    flags = transposed if isinstance(transposed, (list, tuple)) else [transposed] * len(ws)
+    outs, items = [], []
+    for w, t in zip(ws, flags):
+        n, k = w.shape
+        dev = w.device
+        q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        s = torch.empty((_cdiv(n, 128), _cdiv(k, 128)), dtype=torch.float32, device=dev)
+        qT = sT = None
+        if t:
+            qT = torch.empty((k, n), dtype=torch.uint8, device=dev)
+            sT = torch.empty((_cdiv(k, 128), _cdiv(n, 128)), dtype=torch.float32, device=dev)
+        outs.append((q, s, qT, sT))
+        items.append((w, n, k, w.stride(0), q, s, qT, sT))
+    qr_quant_w_128x128_batched(items, stream)
+    return outs
 
 def _workspace(kind, M, N, K, device):
     import torch

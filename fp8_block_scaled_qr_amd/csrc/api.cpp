@@ -4,6 +4,9 @@
 
 #include "qr_internal.h"
 
+#include <algorithm>
+#include <vector>
+
 namespace {
 
 constexpr int32_t kAbiVersion = 1;
@@ -45,6 +48,28 @@ constexpr int64_t kMaxDim = int64_t(1) << 31;
 constexpr int64_t kMaxLd = int64_t(1) << 22;
 
 qr_status launch_status(hipError_t e) { return e == hipSuccess ? QR_OK : QR_ERR_LAUNCH; }
+
+// Argument checks of one 128x128 weight quantization (all but aliasing).
+qr_status check_weight(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, const uint8_t *q,
+                       const float *s, const uint8_t *qT, const float *sT)
+{
+    if (n < 0 || k < 0 || n >= kMaxDim || k >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (!q || !s || (qT == nullptr) != (sT == nullptr))
+        return QR_ERR_NULL;
+    if (n % 8 != 0 || k % 8 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k) || ld_w >= kMaxLd)
+        return QR_ERR_SHAPE;
+    if (cdiv(n, 128) > 65535)
+        return QR_ERR_SHAPE;
+    if (n == 0 || k == 0)
+        return QR_OK;
+    if (!w_bf16)
+        return QR_ERR_NULL;
+    if (misaligned(w_bf16, 16) || misaligned(q, 16) || misaligned(qT, 16) || misaligned(s, 4) ||
+        misaligned(sT, 4))
+        return QR_ERR_ALIGN;
+    return QR_OK;
+}
 
 qr_status check_gemm(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                      int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype, void *ws,
@@ -162,21 +187,9 @@ qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int
 qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *q,
                              float *s, uint8_t *qT, float *sT, qr_stream stream)
 {
-    if (n < 0 || k < 0 || n >= kMaxDim || k >= kMaxDim)
-        return QR_ERR_SHAPE;
-    if (!q || !s || (qT == nullptr) != (sT == nullptr))
-        return QR_ERR_NULL;
-    if (n % 8 != 0 || k % 8 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k) || ld_w >= kMaxLd)
-        return QR_ERR_SHAPE;
-    if (cdiv(n, 128) > 65535)
-        return QR_ERR_SHAPE;
-    if (n == 0 || k == 0)
-        return QR_OK;
-    if (!w_bf16)
-        return QR_ERR_NULL;
-    if (misaligned(w_bf16, 16) || misaligned(q, 16) || misaligned(qT, 16) || misaligned(s, 4) ||
-        misaligned(sT, 4))
-        return QR_ERR_ALIGN;
+    const qr_status st = check_weight(w_bf16, n, k, ld_w, q, s, qT, sT);
+    if (st != QR_OK || n == 0 || k == 0)
+        return st;
     const int64_t nblk = cdiv(n, 128) * cdiv(k, 128);
     const Range rw = span(w_bf16, strided_bytes(n, k, ld_w, 2));
     const Range outs[4] = {span(q, n * k), span(s, nblk * 4), span(qT, n * k), span(sT, nblk * 4)};
@@ -190,6 +203,63 @@ qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t l
     const int mode = qr::QMODE_BLK | (qT ? qr::QMODE_BLKT : 0);
     return launch_status(qr::launch_quant_tile(mode, static_cast<const uint16_t *>(w_bf16), n, k,
                                                ld_w, q, s, qT, sT, (hipStream_t)stream));
+}
+
+qr_status qr_quant_w_128x128_batched(const qr_weight_desc *descs, int32_t count,
+                                     qr_stream stream)
+{
+    if (count < 0 || count > QR_MAX_WEIGHT_BATCH)
+        return QR_ERR_SHAPE;
+    if (count == 0)
+        return QR_OK;
+    if (!descs)
+        return QR_ERR_NULL;
+    // every descriptor as for qr_quant_w_128x128, then no output may overlap any input or
+    // any other output (inputs may overlap each other)
+    struct Tagged {
+        Range r;
+        bool out;
+    };
+    std::vector<Tagged> ranges;
+    std::vector<qr::WeightDesc> plain, trans;
+    for (int32_t i = 0; i < count; ++i) {
+        const qr_weight_desc &d = descs[i];
+        const qr_status st = check_weight(d.w_bf16, d.n, d.k, d.ld_w, d.q, d.s, d.qT, d.sT);
+        if (st != QR_OK)
+            return st;
+        if (d.n == 0 || d.k == 0)
+            continue;
+        const int64_t nblk = cdiv(d.n, 128) * cdiv(d.k, 128);
+        ranges.push_back({span(d.w_bf16, strided_bytes(d.n, d.k, d.ld_w, 2)), false});
+        ranges.push_back({span(d.q, d.n * d.k), true});
+        ranges.push_back({span(d.s, nblk * 4), true});
+        ranges.push_back({span(d.qT, d.qT ? d.n * d.k : 0), true});
+        ranges.push_back({span(d.sT, d.sT ? nblk * 4 : 0), true});
+        const qr::WeightDesc w = {static_cast<const uint16_t *>(d.w_bf16), d.n, d.k, d.ld_w,
+                                  d.q, d.s, d.qT, d.sT, nblk};
+        (d.qT ? trans : plain).push_back(w);
+    }
+    ranges.erase(std::remove_if(ranges.begin(), ranges.end(),
+                                [](const Tagged &t) { return t.r.lo == t.r.hi; }),
+                 ranges.end());
+    std::sort(ranges.begin(), ranges.end(),
+              [](const Tagged &a, const Tagged &b) { return a.r.lo < b.r.lo; });
+    // sweep by start address: a range overlaps an earlier one iff it starts below the largest
+    // end seen so far (over all ranges if it is an output, over the outputs if it is an input)
+    uintptr_t end_all = 0, end_out = 0;
+    for (const Tagged &t : ranges) {
+        if (t.r.lo < end_out || (t.out && t.r.lo < end_all))
+            return QR_ERR_ALIAS;
+        end_all = std::max(end_all, t.r.hi);
+        if (t.out)
+            end_out = std::max(end_out, t.r.hi);
+    }
+    hipError_t e = hipSuccess;
+    if (!plain.empty())
+        e = qr::launch_quant_w_batch(plain.data(), (int)plain.size(), false, (hipStream_t)stream);
+    if (e == hipSuccess && !trans.empty())
+        e = qr::launch_quant_w_batch(trans.data(), (int)trans.size(), true, (hipStream_t)stream);
+    return launch_status(e);
 }
 
 qr_status qr_gemm_fp8_bsfprop(const uint8_t *a, const float *sa, const uint8_t *b,

@@ -24,6 +24,27 @@ hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t 
                              int64_t ld_x, uint8_t *q, float *s, uint8_t *qT, float *sT,
                              hipStream_t stream);
 
+// One weight of a batched 128x128 quantization (BLK, plus BLKT when qT is used).
+struct WeightDesc {
+    const uint16_t *w;      // bf16 [n, k], leading dimension ld
+    int64_t n, k, ld;
+    uint8_t *q;             // [n, k]
+    float *s;               // [ceil(n/128), ceil(k/128)]
+    uint8_t *qT;            // [k, n] or unused
+    float *sT;              // [ceil(k/128), ceil(n/128)] or unused
+    int64_t tiles;          // ceil(n/128) * ceil(k/128), > 0
+};
+constexpr int kMaxWeightBatch = 32;   // descriptors per launch (they travel as a kernel argument)
+struct WeightTable {
+    int count;
+    WeightDesc d[kMaxWeightBatch];
+};
+
+// Quantizes count weights (all with, or all without, the transposed copy) in launches of up
+// to kMaxWeightBatch descriptors.
+hipError_t launch_quant_w_batch(const WeightDesc *descs, int count, bool transposed,
+                                hipStream_t stream);
+
 hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
                            const float *s, uint16_t *w_out, int64_t ld_out, float *gain,
                            hipStream_t stream);

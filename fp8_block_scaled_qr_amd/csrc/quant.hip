@@ -116,16 +116,14 @@ __device__ __forceinline__ void load_tile(const uint16_t *__restrict__ x, int64_
     }
 }
 
-// Persistent: workgroup b handles tiles b, b + gridDim.x, ... (row-major over the tile grid)
+// The workgroup handles tiles first, first + stride, ... of x (row-major over the tile grid)
 // and prefetches the next tile's 32 KB into registers while it reduces, encodes and stores
-// the current one, so reads and writes of the whole grid overlap.
+// the current one, so reads and writes overlap.  Every thread of the workgroup calls it.
 template <int MODE>
-__global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ldx,
-                                                    uint8_t *__restrict__ q,
-                                                    float *__restrict__ s,
-                                                    uint8_t *__restrict__ qT,
-                                                    float *__restrict__ sT)
+__device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int64_t rows,
+                                            int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
+                                            float *__restrict__ s, uint8_t *__restrict__ qT,
+                                            float *__restrict__ sT, int64_t first, int64_t stride)
 {
     constexpr bool ROW = (MODE & QMODE_ROW) != 0;
     constexpr bool COL = (MODE & QMODE_COL) != 0;
@@ -325,8 +323,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
         const int64_t c = bj * kTile + 8 * oc;
         load_tile(x, valid ? rows : 0, ldx, valid ? bi * kTile : 0, c, c < cols, oq, v);
     };
-    const int64_t step = gridDim.x;
-    const int64_t dbi = step / ngc, dbj = step - dbi * ngc;
+    const int64_t dbi = stride / ngc, dbj = stride - dbi * ngc;
     auto advance = [&](int64_t &bi, int64_t &bj) {
         bi += dbi;
         bj += dbj;
@@ -336,7 +333,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
         }
     };
     uint4 va[8], vb[8];
-    int64_t bi = (int64_t)blockIdx.x / ngc, bj = (int64_t)blockIdx.x - bi * ngc;
+    int64_t bi = first / ngc, bj = first - bi * ngc;
     int64_t ni = bi, nj = bj;
     prefetch(bi, bj, va);
     while (bi < ngr) {
@@ -352,6 +349,39 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
         process(bi, bj, 1, vb);
         bi = ni;
         bj = nj;
+    }
+}
+
+// Persistent: as many workgroups as fit on the CUs at once; workgroup b handles tiles b,
+// b + gridDim.x, ...
+template <int MODE>
+__global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ldx,
+                                                    uint8_t *__restrict__ q,
+                                                    float *__restrict__ s,
+                                                    uint8_t *__restrict__ qT,
+                                                    float *__restrict__ sT)
+{
+    quant_tiles<MODE>(x, rows, cols, ldx, q, s, qT, sT, blockIdx.x, gridDim.x);
+}
+
+// A list of weights quantized in one persistent launch (a weight update re-quantizes every
+// layer).  The tiles of all tensors form one round-robin sequence over the workgroups, so a
+// small tensor does not leave most of the grid idle.  The table travels by value in the
+// kernel arguments.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_quant_w_batch(WeightTable tab)
+{
+    const int64_t G = gridDim.x;
+    int64_t before = 0;   // tiles of the tensors already walked
+    for (int i = 0; i < tab.count; ++i) {
+        const WeightDesc &d = tab.d[i];
+        int64_t first = ((int64_t)blockIdx.x - before) % G;
+        if (first < 0)
+            first += G;
+        quant_tiles<MODE>(d.w, d.n, d.k, d.ld, d.q, d.s, d.qT, d.sT, first, G);
+        before += d.tiles;
+        __syncthreads();   // LDS of this tensor's last tile is read before the next one writes
     }
 }
 
@@ -514,6 +544,33 @@ hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t 
     default:
         return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_quant_w_batch(const WeightDesc *descs, int count, bool transposed,
+                                hipStream_t stream)
+{
+    constexpr int BT = QMODE_BLK | QMODE_BLKT, B = QMODE_BLK;
+    const int64_t limit = persistent_grid(
+        transposed ? reinterpret_cast<const void *>(&k_quant_w_batch<BT>)
+                   : reinterpret_cast<const void *>(&k_quant_w_batch<B>));
+    for (int i0 = 0; i0 < count; i0 += kMaxWeightBatch) {
+        WeightTable tab;
+        tab.count = count - i0 < kMaxWeightBatch ? count - i0 : kMaxWeightBatch;
+        int64_t total = 0;
+        for (int i = 0; i < tab.count; ++i) {
+            tab.d[i] = descs[i0 + i];
+            total += tab.d[i].tiles;
+        }
+        const dim3 grid((unsigned)(total < limit ? total : limit));
+        if (transposed)
+            k_quant_w_batch<BT><<<grid, 256, 0, stream>>>(tab);
+        else
+            k_quant_w_batch<B><<<grid, 256, 0, stream>>>(tab);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,

@@ -118,6 +118,34 @@ qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t l
                              uint8_t *q, float *s, uint8_t *qT, float *sT, qr_stream stream);
 
 /*
+ * Weight update re-quantization [JET, section "system implementation": the weights are
+ * quantized to FP8 in the parameter-update phase]: every weight of a model is re-quantized
+ * after an optimizer step.  This call does a list of them in one launch, with the tiles of
+ * all weights shared out over the whole GPU, so small weights do not leave it idle.
+ *
+ * descs[i] describes one weight exactly as the arguments of qr_quant_w_128x128 (same layouts,
+ * size rules and alignment); its qT/sT pair may be NULL for some weights and not others.
+ * count: 0 .. QR_MAX_WEIGHT_BATCH; the descriptor array is host memory, read during the call
+ * only.  A weight with n == 0 or k == 0 is skipped.
+ * Aliasing: no output may overlap any input or any other output, across all descriptors
+ * (inputs may overlap each other).  Every descriptor is validated before anything launches;
+ * on error nothing runs and the first failing check's status is returned.
+ */
+typedef struct qr_weight_desc {
+    const void *w_bf16;   /* bf16 [n, k], leading dimension ld_w */
+    int64_t n, k, ld_w;
+    uint8_t *q;           /* [n, k] codes */
+    float *s;             /* [ceil(n/128), ceil(k/128)] scales */
+    uint8_t *qT;          /* NULL or [k, n] transposed codes */
+    float *sT;            /* NULL or [ceil(k/128), ceil(n/128)] transposed scales */
+} qr_weight_desc;
+
+#define QR_MAX_WEIGHT_BATCH 4096
+
+qr_status qr_quant_w_128x128_batched(const qr_weight_desc *descs, int32_t count,
+                                     qr_stream stream);
+
+/*
  * FProp [JET]:  Y[m, n] = sum_k deq(A)[m, k] * deq(W)[n, k].
  *   a  [M, K] codes with sa [M, K/128]            (1x128 groups along K, from q_row)
  *   b  [N, K] codes with sb [ceil(N/128), K/128]   (the 128x128-quantized weight W[N, K])

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 9, declared
+    assert len(declared) == 10, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -84,6 +84,37 @@ def test_quant_w_validation(L):
     assert f(A, 128, 128, 128, B, A, None, None, None) == ALIAS
     assert f(A, 128, 128, 128, B, C, B + 64, D, None) == ALIAS
     assert f(A, 0, 128, 128, B, C, None, None, None) == OK
+
+
+def batch(L, descs):
+    arr = (qr.qr_weight_desc * max(1, len(descs)))(*[qr.qr_weight_desc(*d) for d in descs])
+    return L.qr_quant_w_128x128_batched(arr, len(descs), None)
+
+
+def test_quant_w_batched_validation(L):
+    f = L.qr_quant_w_128x128_batched
+    assert f(None, 0, None) == OK                                     # nothing to do
+    assert f(None, 1, None) == NULL
+    arr = (qr.qr_weight_desc * 1)()
+    assert f(arr, -1, None) == SHAPE
+    assert f(arr, qr.QR_MAX_WEIGHT_BATCH + 1, None) == SHAPE
+    M = 1 << 20                                                       # 1 MiB apart
+    good0 = (A, 128, 128, 128, B, C, None, None)
+    good1 = (A + M, 256, 128, 128, B + M, C + M, D, E)
+    # each descriptor is checked like qr_quant_w_128x128
+    assert batch(L, [good0, (A + M, 100, 128, 128, B + M, C + M, None, None)]) == SHAPE
+    assert batch(L, [good0, (A + M, 128, 128, 128, None, C + M, None, None)]) == NULL
+    assert batch(L, [good0, (A + M, 128, 128, 128, B + M, C + M, D, None)]) == NULL
+    assert batch(L, [(A + 8, 128, 128, 128, B, C, None, None), good1]) == ALIGN
+    # aliasing across descriptors: an output over another weight's input or output
+    assert batch(L, [good0, (A + M, 128, 128, 128, A + 64, C + M, None, None)]) == ALIAS
+    assert batch(L, [good0, (A + M, 128, 128, 128, B + M, B + 64, None, None)]) == ALIAS
+    assert batch(L, [good0, (A + M, 256, 128, 128, B + M, C + M, B + 128, E)]) == ALIAS
+    assert batch(L, [good0, (A + M, 128, 128, 128, B + M, C, None, None)]) == ALIAS
+    assert batch(L, [good1, (A, 128, 128, 128, B, C, None, None),
+                     (A + 2 * M, 8, 8, 8, A + M + 32, C + 2 * M, None, None)]) == ALIAS
+    # empty weights are skipped (nothing launched)
+    assert batch(L, [(A, 0, 128, 128, B, C, None, None), (A, 128, 0, 0, B, C, D, E)]) == OK
 
 
 def gemm(L, name, a, sa, b, sb, M, N, K, y, dt, ws, wsb):

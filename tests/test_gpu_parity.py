@@ -87,6 +87,44 @@ def test_quant_w(n, k, name):
     assert_bitexact(host(sT), np.ascontiguousarray(rs.T), "transposed scales")
 
 
+def test_quant_w_batched():
+    """A weight update's re-quantization in one call: 41 descriptors (more than one launch
+    table of 32), ragged and 8B-sized shapes, the transposed copy for some and not others, a
+    strided input, two descriptors sharing one input, and an empty weight (skipped)."""
+    say("quant_w batched")
+    rng = np.random.default_rng(17)
+    small = [(200, 136), (392, 264), (128, 128), (8, 8), (136, 8), (8, 392), (256, 520)]
+    shapes = [small[i % len(small)] for i in range(36)] + [(4096, 4096), (1024, 4096)]
+    hosts = [qr_synth.normal_bf16(900 + i, sh, float(rng.uniform(0.005, 0.05)))
+             for i, sh in enumerate(shapes)]
+    ws = [dev_bf16(h) for h in hosts]
+    flags = [bool(i % 3) for i in range(len(ws))]
+    big = qr_synth.normal_bf16(950, (256, 640), 0.02)           # strided: ld 640, k 384
+    hosts.append(np.ascontiguousarray(big[:, 64:448]))
+    ws.append(dev_bf16(big)[:, 64:448])
+    flags.append(True)
+    hosts.append(hosts[2])                                      # same input, second descriptor
+    ws.append(ws[2])
+    flags.append(not flags[2])
+    outs = qr.quant_w_batched(ws, flags)
+    # an empty weight among real ones: its (unused) pointers may be anything non-null
+    q0, s0, _, _ = outs[0]
+    items = [(ws[3], 0, 8, 8, q0, s0, None, None)]
+    for w, (q, s, qT, sT) in zip(ws, outs):
+        items.append((w, w.shape[0], w.shape[1], w.stride(0), q, s, qT, sT))
+    assert len(items) == 41
+    qr.qr_quant_w_128x128_batched(items)
+    for i, (h, (q, s, qT, sT)) in enumerate(zip(hosts, outs)):
+        rq, rs = oracle.quant_blocks(h)
+        assert_bitexact(host(q), rq, f"codes {i}")
+        assert_bitexact(host(s), rs, f"scales {i}")
+        if flags[i]:
+            assert_bitexact(host(qT), np.ascontiguousarray(rq.T), f"transposed codes {i}")
+            assert_bitexact(host(sT), np.ascontiguousarray(rs.T), f"transposed scales {i}")
+        else:
+            assert qT is None and sT is None
+
+
 def test_quant_strided_input():
     say("quant strided ld")
     big = qr_synth.normal_bf16(11, (96, 640), 1.0)
