@@ -76,9 +76,15 @@ def decode_flops():
     return gemm_flops(MD, F, H)
 
 
-def kernel_source_sha():
+# Sources each op's kernels are built from (a traffic figure is valid only for these).
+GEMM_SOURCES = ("gemm.hip", "qr_device.h", "qr_internal.h")
+QUANT_SOURCES = ("quant.hip", "qr_device.h", "qr_internal.h")
+
+
+def kernel_source_sha(kernel="wgrad"):
+    files = GEMM_SOURCES if op_table()[kernel][0] == "mfma" or "decode" in kernel else QUANT_SOURCES
     h = hashlib.sha256()
-    for f in ("gemm.hip", "quant.hip", "qr_device.h", "api.cpp"):
+    for f in files:
         with open(os.path.join(ROOT, "fp8_block_scaled_qr_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -94,7 +100,7 @@ def measured_traffic(kernel):
     except (OSError, ValueError):
         return None
     e = d.get(kernel)
-    if not e or e.get("source_sha") != kernel_source_sha():
+    if not e or e.get("source_sha") != kernel_source_sha(kernel):
         return None
     return e.get("bytes_per_launch")
 
