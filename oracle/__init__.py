@@ -13,6 +13,8 @@ marshals arguments and strings the definitions together:
 * ``fprop`` / ``dgrad`` / ``wgrad`` -- dequantize, then multiply in fp64 (returns Y and
   S = sum |a*b|, the quantity the GEMM tolerance is stated against).
 * ``uaq_fold``     -- W' = RN_bf16(W / s[col]), gain' = RN32(gain * s).
+* ``rmsnorm``      -- the norm whose gain carries the UAQ scale: y = h * gain / sqrt(mean(h^2)
+  + eps) in fp64 and its RN_bf16 (the input of the fused norm-and-quantize kernel).
 
 Sources: Jet-RL (arXiv 2601.14243v1) notes, section on the fine-grained GEMM quantization
 scheme (Figure 6 there); QuRL (ICLR 2026) notes, key design 1 (UAQ).
@@ -72,6 +74,8 @@ def lib():
         L.orc_matmul_nt_sampled.restype = None
         L.orc_uaq_fold.argtypes = [_u16p, _i64, _i64, _i64, _f32p, _u16p, _f32p]
         L.orc_uaq_fold.restype = ctypes.c_int
+        L.orc_rmsnorm.argtypes = [_u16p, _i64, _i64, _i64, _f32p, ctypes.c_float, _f64p, _u16p]
+        L.orc_rmsnorm.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -259,3 +263,20 @@ def uaq_fold(w_bf16: np.ndarray, s: np.ndarray, gain=None):
     if rc:
         raise ValueError("UAQ fold: non-finite weight or non-positive scale")
     return out, g
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+def rmsnorm(h_bf16: np.ndarray, gain: np.ndarray, eps: float):
+    """Returns (y fp64 [rows, cols], RN_bf16(y) bits [rows, cols]) for
+    y = h * gain / sqrt(mean(h^2 over the row) + eps)."""
+    h = _c(h_bf16, np.uint16)
+    rows, cols = h.shape
+    g = _c(np.asarray(gain, np.float32), np.float32)
+    assert g.shape == (cols,)
+    y = np.empty((rows, cols), np.float64)
+    yb = np.empty((rows, cols), np.uint16)
+    if lib().orc_rmsnorm(_p(h, _u16p), rows, cols, cols, _p(g, _f32p), float(eps), _p(y, _f64p),
+                         _p(yb, _u16p)):
+        raise ValueError("RMSNorm: non-finite input or gain, or a bad eps")
+    return y, yb

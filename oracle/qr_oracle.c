@@ -30,6 +30,8 @@
  *     scale) and sum the products in fp64.
  *   - The UAQ fold writes W' = RN_bf16(W / s) (the exact quotient rounded once) and
  *     gain' = RN32(gain * s).
+ *   - The norm whose gain carries s (the QuRL notes fold s into it) is the standard RMSNorm,
+ *     y = h * gain / sqrt(mean(h^2) + eps), evaluated in binary64 and rounded once to bf16.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math; x86-64 SSE
  * arithmetic, so binary32 and binary64 operations are correctly rounded and subnormals kept).
@@ -335,5 +337,37 @@ int orc_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld, const floa
     if (gain)
         for (int64_t c = 0; c < k; ++c)
             gain[c] = gain[c] * s[c];
+    return 0;
+}
+
+/* ---------------------------------------------------------------- RMSNorm in front of a linear */
+
+/* y[r, c] = h[r, c] * gain[c] / sqrt(mean_c h[r, c]^2 + eps), per row, in binary64 (relative
+ * error below 2^-50); y_exact (may be NULL) receives it and y_bf16 its RN_bf16.  This is the
+ * norm whose gain the UAQ fold scales by s; the fused kernel quantizes its bf16 output in
+ * 1x128 groups.  Returns 0, or -1 on a non-finite h or gain or a negative / non-finite eps. */
+int orc_rmsnorm(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld, const float *gain,
+                float eps, double *y_exact, uint16_t *y_bf16)
+{
+    if (!all_finite_bf16(h, rows, cols, ld) || !(eps >= 0.0f) || !isfinite(eps))
+        return -1;
+    for (int64_t c = 0; c < cols; ++c)
+        if (!isfinite(gain[c]))
+            return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < cols; ++c) {
+            double x = (double)orc_bf16_to_f32(h[r * ld + c]);
+            ss += x * x;
+        }
+        double inv = 1.0 / sqrt(ss / (double)cols + (double)eps);
+        for (int64_t c = 0; c < cols; ++c) {
+            double y = (double)orc_bf16_to_f32(h[r * ld + c]) * (double)gain[c] * inv;
+            if (y_exact)
+                y_exact[r * cols + c] = y;
+            y_bf16[r * cols + c] = f64_to_bf16_rne(y);
+        }
+    }
     return 0;
 }

@@ -1,7 +1,8 @@
 """The oracle's pins catch plausible mistakes: each case below plants one mistake in a copy of
 the oracle source (a wrong rounding rule, a dropped saturation, a lost sign of zero, a
 transposed or shifted scale index, a wrong constant, a reciprocal in place of the division, a
-dropped absolute value, a double rounding, an off-by-one group) and runs the pin suite on that
+dropped absolute value, a double rounding, an off-by-one group, a wrong mean, a dropped eps
+or gain in the norm) and runs the pin suite on that
 copy, which must fail.  CPU only: the copies live in a temporary directory and the HIP library
 is not involved."""
 import os
@@ -28,6 +29,9 @@ MUTANTS = {
     "abs_sum_sampled": ("\n            a += fabs(p);", "\n            a += p;"),
     "uaq_f32_quotient": ("double q = (double)orc_bf16_to_f32(w[r * ld + c]) / (double)s[c];",
                          "double q = (double)(orc_bf16_to_f32(w[r * ld + c]) / s[c]);"),
+    "rms_mean_over_cols_plus_1": ("ss / (double)cols + (double)eps", "ss / (double)(cols + 1) + (double)eps"),
+    "rms_no_eps": ("ss / (double)cols + (double)eps", "ss / (double)cols"),
+    "rms_no_gain": ("* (double)gain[c] * inv", "* inv"),
     "column_group_short": ("int64_t r0 = g * GROUP, r1 = r0 + GROUP < rows ? r0 + GROUP : rows;",
                            "int64_t r0 = g * GROUP, r1 = r0 + GROUP - 1 < rows ? "
                            "r0 + GROUP - 1 : rows;"),

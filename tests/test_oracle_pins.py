@@ -474,3 +474,82 @@ def test_uaq_gain_and_rejections():
     bad[3] = 0.0
     with pytest.raises(ValueError):
         oracle.uaq_fold(np.zeros((1, 128), np.uint16), bad)
+
+
+# ============================================================== RMSNorm (the norm carrying s)
+
+def _bf16_frac(b):
+    return Fraction(float(bf16_f32(np.array([b], np.uint16))[0]))
+
+
+def _exact_rms_bf16(hrow, grow, eps):
+    """RN_bf16(h * g / sqrt(q)), q = mean(h^2) + eps, decided in exact rationals: for a
+    candidate bf16 bracket lo <= |y| < hi (from a float estimate, verified exactly), |y| lies
+    above the midpoint m iff (h g)^2 > m^2 q.  Returns bf16 bit patterns."""
+    hv = [Fraction(float(v)) for v in hrow]
+    q = sum(v * v for v in hv) / len(hv) + Fraction(float(np.float32(eps)))
+    out = []
+    for v, g in zip(hv, grow):
+        a2 = (v * Fraction(float(g))) ** 2 / q          # y^2, exact
+        sign = (v * Fraction(float(g))) < 0
+        if a2 == 0:
+            out.append(0x8000 if sign else 0)
+            continue
+        est = math.sqrt(float(a2))
+        b = int(np.array([est], np.float32).view(np.uint32)[0]) >> 16   # truncated estimate
+        for _ in range(4):                                # move the bracket until it holds
+            lo, hi = _bf16_frac(b), _bf16_frac(b + 1)
+            if lo * lo > a2:
+                b -= 1
+            elif hi * hi <= a2:
+                b += 1
+            else:
+                break
+        lo, hi = _bf16_frac(b), _bf16_frac(b + 1)
+        assert lo * lo <= a2 < hi * hi
+        mid2 = ((lo + hi) / 2) ** 2
+        up = a2 > mid2 or (a2 == mid2 and (b & 1))
+        out.append((b + up) | (0x8000 if sign else 0))
+    return out
+
+
+def test_rmsnorm_matches_exact_rational_rounding():
+    rng = np.random.default_rng(71)
+    for i, (std, eps) in enumerate([(1.0, 1e-6), (1e-3, 1e-6), (30.0, 0.0), (0.05, 1.0)]):
+        h = qr_synth.normal_bf16(72 + i, (3, 96), std, 73 + i, 2)
+        g = rng.uniform(0.5, 4.0, 96).astype(np.float32)
+        g[::7] *= -1.0
+        _, yb = oracle.rmsnorm(h, g, eps)
+        hf = bf16_f32(h)
+        for r in range(h.shape[0]):
+            assert [int(v) for v in yb[r]] == _exact_rms_bf16(hf[r], g, eps), (std, eps, r)
+
+
+def test_rmsnorm_constant_rows_and_power_of_two_invariance():
+    # a constant row with eps = 0 normalizes to +-1 exactly (times the gain)
+    vals = [0x3F80, 0x4049, 0xC2F7, 0x0123, 0x7F00, 0xB8A1]
+    h = np.array([[v] * 256 for v in vals], np.uint16)
+    y, yb = oracle.rmsnorm(h, np.ones(256, np.float32), 0.0)
+    for r, v in enumerate(vals):
+        assert np.all(yb[r] == (0xBF80 if v & 0x8000 else 0x3F80)), hex(v)
+    # scaling h by 2^j leaves y unchanged when eps = 0
+    h = qr_synth.normal_bf16(75, (8, 512), 1.0, 76, 5)
+    g = np.random.default_rng(77).uniform(0.5, 2.0, 512).astype(np.float32)
+    y0, b0 = oracle.rmsnorm(h, g, 0.0)
+    h8 = qr_synth.f32_to_bf16_bits(bf16_f32(h) * np.float32(2.0 ** -20))
+    y1, b1 = oracle.rmsnorm(h8, g, 0.0)
+    assert np.array_equal(b0, b1) and np.array_equal(y0, y1)
+
+
+def test_rmsnorm_rejections():
+    h = np.zeros((2, 128), np.uint16)
+    g = np.ones(128, np.float32)
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(h, g, -1.0)
+    bad = g.copy()
+    bad[5] = np.inf
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(h, bad, 1e-6)
+    h[1, 3] = 0x7F80
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(h, g, 1e-6)
