@@ -21,8 +21,9 @@ records events only around the dominant kernel's launch, so the step time carrie
 event overhead.  The JSON line reports the step's GEMM throughput (all GEMM flops / step
 time) as `value`, each op's time with its roofline fraction, the roofline of the dominant
 kernel from its launches in the timed pass, and the CPU oracle timed on a bounded token slice
-of the same step.  Outside the step (it runs once per optimizer step) it also times the
-batched re-quantization of a 32B decoder layer's four weights (`weight_update`).
+of the same step.  Outside the step it also times the batched re-quantization of a 32B
+decoder layer's four weights (`weight_update`, once per optimizer step) and the norm with the
+activation quantize fused in (`norm_quant`, the producer of FProp's operand).
 """
 import argparse
 import hashlib
@@ -225,10 +226,40 @@ def run_gpu(args):
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(end) / args.steps
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+    normq = run_norm_quant(torch, qr, st)
     del st, ops
     torch.cuda.empty_cache()
     upd = run_weight_update(torch, qr)
-    return step_ms, wall, per_op, dom, dom_ms, upd
+    return step_ms, wall, per_op, dom, dom_ms, upd, normq
+
+
+def run_norm_quant(torch, qr, st, iters=20):
+    """The norm in front of FProp with its 1x128 quantization fused in, on the prefill hidden
+    state [8192, 4096] (the step's X stands in for h; the gain carries the UAQ s), writing the
+    FProp operand only (codes and scales): 2 + 1 + 4/128 bytes per element."""
+    dev = "cuda:0"
+    g = st.s.clone()
+    q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    s = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    f = lambda: qr.qr_rmsnorm_quant_1x128(st.X, T, H, H, g, 1e-6, None, q, s)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        f()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    nbytes = T * H * 2 + T * H + T * (H // 128) * 4 + H * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "RMSNorm (gain carrying the UAQ s) + 1x128 quantize of h [8192, 4096], "
+                        "codes and scales out (the FProp operand)",
+            "us": round(us, 2), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def run_weight_update(torch, qr, iters=10):
@@ -328,7 +359,7 @@ def main():
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms, upd = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, upd, normq = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -364,6 +395,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "weight_update": upd,
+        "norm_quant": normq,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -23,8 +23,9 @@ QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD = 0, 1, 2
 
 # Every entry point include/qr.h declares.
 EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant_w_128x128",
-           "qr_quant_w_128x128_batched", "qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad",
-           "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes", "qr_uaq_fold")
+           "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_gemm_fp8_bsfprop",
+           "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes",
+           "qr_uaq_fold")
 QR_MAX_WEIGHT_BATCH = 4096
 
 
@@ -63,6 +64,8 @@ def load():
     L.qr_quant_w_128x128.restype = I32
     L.qr_quant_w_128x128_batched.argtypes = [ctypes.POINTER(qr_weight_desc), I32, P]
     L.qr_quant_w_128x128_batched.restype = I32
+    L.qr_rmsnorm_quant_1x128.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P]
+    L.qr_rmsnorm_quant_1x128.restype = I32
     for name in ("qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad"):
         f = getattr(L, name)
         f.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
@@ -129,6 +132,12 @@ def qr_quant_w_128x128_batched(items, stream=None):
                                 None if sT is None else sT.data_ptr())
     _check(load().qr_quant_w_128x128_batched(arr, len(items), _stream(stream)),
            "qr_quant_w_128x128_batched")
+
+
+def qr_rmsnorm_quant_1x128(h, rows, cols, ld_h, gain, eps, y, q_row, s_row, stream=None):
+    _check(load().qr_rmsnorm_quant_1x128(_ptr(h), rows, cols, ld_h, _ptr(gain), float(eps),
+                                         _ptr(y), _ptr(q_row), _ptr(s_row), _stream(stream)),
+           "qr_rmsnorm_quant_1x128")
 
 
 def _gemm(name, a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream):
@@ -218,6 +227,18 @@ def quant_w_batched(ws, transposed=False, stream=None):
         items.append((w, n, k, w.stride(0), q, s, qT, sT))
     qr_quant_w_128x128_batched(items, stream)
     return outs
+
+def rmsnorm_quant(h, gain, eps=1e-6, want_y=True, stream=None):
+    """h: bf16 [rows, cols] on the GPU, gain fp32 [cols].  Returns (y or None, q, s)."""
+    import torch
+    rows, cols = h.shape
+    dev = h.device
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if want_y else None
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=dev)
+    qr_rmsnorm_quant_1x128(h, rows, cols, h.stride(0), gain, eps, y, q, s, stream)
+    return y, q, s
+
 
 def _workspace(kind, M, N, K, device):
     import torch

@@ -184,6 +184,39 @@ qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int
                                                (hipStream_t)stream));
 }
 
+qr_status qr_rmsnorm_quant_1x128(const void *h_bf16, int64_t rows, int64_t cols, int64_t ld_h,
+                                 const float *gain, float eps, void *y_bf16, uint8_t *q_row,
+                                 float *s_row, qr_stream stream)
+{
+    if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (cols % 8 != 0 || ld_h % 8 != 0 || (rows > 0 && ld_h < cols) || ld_h >= kMaxLd)
+        return QR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return QR_ERR_ARG;
+    if (rows == 0 || cols == 0)
+        return QR_OK;
+    if (!h_bf16 || !gain || !q_row || !s_row)
+        return QR_ERR_NULL;
+    if (misaligned(h_bf16, 16) || misaligned(y_bf16, 16) || misaligned(q_row, 16) ||
+        misaligned(gain, 16) || misaligned(s_row, 4))
+        return QR_ERR_ALIGN;
+    const Range ins[2] = {span(h_bf16, strided_bytes(rows, cols, ld_h, 2)), span(gain, cols * 4)};
+    const Range outs[3] = {span(y_bf16, y_bf16 ? rows * cols * 2 : 0), span(q_row, rows * cols),
+                           span(s_row, rows * cdiv(cols, 128) * 4)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r))
+                return QR_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j]))
+                return QR_ERR_ALIAS;
+    }
+    return launch_status(qr::launch_rmsnorm_quant(
+        static_cast<const uint16_t *>(h_bf16), rows, cols, ld_h, gain, eps,
+        static_cast<uint16_t *>(y_bf16), q_row, s_row, (hipStream_t)stream));
+}
+
 qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *q,
                              float *s, uint8_t *qT, float *sT, qr_stream stream)
 {

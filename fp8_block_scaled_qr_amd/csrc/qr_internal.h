@@ -45,6 +45,12 @@ struct WeightTable {
 hipError_t launch_quant_w_batch(const WeightDesc *descs, int count, bool transposed,
                                 hipStream_t stream);
 
+// y = RN_bf16(h * gain / sqrt(mean(h^2) + eps)) per row of h [rows, cols] (ld_h); y is
+// optional (NULL); q [rows, cols] and s [rows, ceil(cols/128)] are y's 1x128 codes and scales.
+hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld_h,
+                                const float *gain, float eps, uint16_t *y, uint8_t *q, float *s,
+                                hipStream_t stream);
+
 hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
                            const float *s, uint16_t *w_out, int64_t ld_out, float *gain,
                            hipStream_t stream);

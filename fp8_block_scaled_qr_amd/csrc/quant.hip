@@ -385,6 +385,103 @@ __global__ __launch_bounds__(256) void k_quant_w_batch(WeightTable tab)
     }
 }
 
+// ---------------------------------------------------------------- RMSNorm + 1x128 quantize
+
+__device__ __forceinline__ float sumsq8(const uint4 &v, float ss)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = bf16_elem(v, i);
+        ss = __builtin_fmaf(x, x, ss);   // x * x is exact in binary32 (8-bit significands)
+    }
+    return ss;
+}
+
+// y = RN_bf16((h * inv) * gain) for 8 consecutive elements
+__device__ __forceinline__ uint4 rms_apply(const uint4 &v, float inv, const float4 &g0,
+                                           const float4 &g1)
+{
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16(bf16_elem(v, 2 * i) * inv * g[2 * i]) |
+               (f32_to_bf16(bf16_elem(v, 2 * i + 1) * inv * g[2 * i + 1]) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The norm in front of a linear layer with its 1x128 quantization fused in: one wave per row.
+// In pass p, lanes 16 t .. 16 t + 15 take 128-column group 4 p + t, 8 columns (16 bytes)
+// each, so a pass reads 1 KB of the row and a group's max is a 16-lane DPP reduction.  The
+// first phase sums h^2 (NP > 0: the row stays in registers, NP passes at most; NP == 0: the
+// second phase reads it again); the second forms y = RN_bf16((h * inv) * gain) with
+// inv = 1 / sqrt(sum / cols + eps) and encodes y exactly as the 1x128 quantizer does.
+template <int NP>
+__global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restrict__ h,
+                                                       int64_t rows, int64_t cols, int64_t ldh,
+                                                       const float *__restrict__ gain, float eps,
+                                                       uint16_t *__restrict__ y,
+                                                       uint8_t *__restrict__ q,
+                                                       float *__restrict__ s)
+{
+    const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;   // the whole wave; no barrier follows
+    const int64_t ngc = (cols + kTile - 1) / kTile, npass = (ngc + 3) / 4;
+    const uint16_t *hr = h + row * ldh;
+    auto col_of = [&](int64_t p) { return (4 * p + sub) * kTile + 8 * li; };
+    auto load = [&](int64_t p) -> uint4 {
+        const int64_t c = col_of(p);   // cols % 8 == 0: an octet is all in or out
+        return c < cols ? *reinterpret_cast<const uint4 *>(hr + c) : make_uint4(0, 0, 0, 0);
+    };
+    float ss = 0.0f;
+    uint4 keep[NP > 0 ? NP : 1];
+    if (NP > 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            keep[p] = p < npass ? load(p) : make_uint4(0, 0, 0, 0);
+            ss = sumsq8(keep[p], ss);
+        }
+    } else {
+        for (int64_t p = 0; p < npass; ++p)
+            ss = sumsq8(load(p), ss);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        ss += __shfl_xor(ss, o);       // every lane ends with the same sum
+    const float inv = 1.0f / sqrtf(ss / (float)cols + eps);
+
+    auto body = [&](int64_t p, const uint4 &v) {
+        const int64_t c = col_of(p);
+        const bool ok = c < cols;
+        uint4 yv = make_uint4(0, 0, 0, 0);
+        if (ok) {
+            const float4 g0 = *reinterpret_cast<const float4 *>(gain + c);
+            const float4 g1 = *reinterpret_cast<const float4 *>(gain + c + 4);
+            yv = rms_apply(v, inv, g0, g1);
+            if (y)
+                *reinterpret_cast<uint4 *>(y + row * cols + c) = yv;
+        }
+        const Scale sc = make_scale(row16_max(absmax8(yv)));   // all 64 lanes take part
+        const uint2 c8 = tiny_scale(sc) ? encode8<true>(yv, sc) : encode8<false>(yv, sc);
+        if (ok)
+            *reinterpret_cast<uint2 *>(q + row * cols + c) = c8;
+        const int64_t g = 4 * p + sub;
+        if (li == 0 && g < ngc)
+            s[row * ngc + g] = sc.s;
+    };
+    if (NP > 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            if (p < npass)   // uniform across the wave
+                body(p, keep[p]);
+    } else {
+        for (int64_t p = 0; p < npass; ++p)
+            body(p, load(p));
+    }
+}
+
 // ---------------------------------------------------------------- UAQ fold
 
 // RN_bf16(w / s), general case: the quotient is formed in binary64 (correctly rounded) and
@@ -571,6 +668,23 @@ hipError_t launch_quant_w_batch(const WeightDesc *descs, int count, bool transpo
             return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld_h,
+                                const float *gain, float eps, uint16_t *y, uint8_t *q, float *s,
+                                hipStream_t stream)
+{
+    if (rows == 0 || cols == 0)
+        return hipSuccess;
+    const int64_t npass = ((cols + kTile - 1) / kTile + 3) / 4;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (npass <= 8)
+        k_rmsnorm_quant<8><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+    else if (npass <= 16)
+        k_rmsnorm_quant<16><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+    else
+        k_rmsnorm_quant<0><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,

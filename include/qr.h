@@ -103,6 +103,29 @@ qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int
                              qr_stream stream);
 
 /*
+ * Norm and activation quantize in one pass (the producer of the FProp operand).  The norm in
+ * front of a linear layer carries the UAQ scale in its gain [QURL, key design 1: s is
+ * folded into the norm once], and its output is what [JET] quantizes in 1x128 groups; this
+ * call does both, so the bf16 activation need not be written and read back:
+ *   y[m, c] = RN_bf16((h[m, c] * inv[m]) * gain[c]),  inv[m] = 1 / sqrt(mean_c h[m, c]^2 + eps)
+ * (binary32 arithmetic: the sum of squares in one fixed order per row, each operation
+ * correctly rounded), then q_row / s_row are y's 1x128 codes and scales exactly as
+ * qr_quant_act_1x128 would produce them from y.
+ *   h      bf16 [rows, cols], leading dimension ld_h (the hidden state before the norm).
+ *   gain   fp32 [cols] (the norm gain, already multiplied by s if the next layer is folded).
+ *   eps    >= 0, finite.
+ *   y_bf16 NULL, or bf16 [rows, cols] (dense): the normalized activation, for a consumer that
+ *          needs it in bf16 (WGrad's 128x1 operand).
+ *   q_row [rows, cols] codes, s_row [rows, ceil(cols/128)] scales.
+ * Size rules: rows, cols >= 0; cols % 8 == 0, ld_h % 8 == 0, ld_h < 2^22.  h, y, q_row and gain
+ * 16-byte aligned, s_row 4-byte aligned.  No output may overlap an input or another output.
+ * A bad eps returns QR_ERR_ARG.
+ */
+qr_status qr_rmsnorm_quant_1x128(const void *h_bf16, int64_t rows, int64_t cols, int64_t ld_h,
+                                 const float *gain, float eps, void *y_bf16, uint8_t *q_row,
+                                 float *s_row, qr_stream stream);
+
+/*
  * Weight quantization, 128x128 blocks [JET]; run once per weight update.
  *
  * w: bf16 [n, k] (n = output features, k = input features), leading dimension ld_w.

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -84,6 +84,24 @@ def test_quant_w_validation(L):
     assert f(A, 128, 128, 128, B, A, None, None, None) == ALIAS
     assert f(A, 128, 128, 128, B, C, B + 64, D, None) == ALIAS
     assert f(A, 0, 128, 128, B, C, None, None, None) == OK
+
+
+def test_rmsnorm_quant_validation(L):
+    f = L.qr_rmsnorm_quant_1x128
+    assert f(A, -1, 128, 128, B, 1e-6, None, C, D, None) == SHAPE
+    assert f(A, 4, 100, 104, B, 1e-6, None, C, D, None) == SHAPE         # cols % 8
+    assert f(A, 4, 128, 120, B, 1e-6, None, C, D, None) == SHAPE         # ld < cols
+    assert f(A, 4, 128, 128, B, -1.0, None, C, D, None) == ARG           # eps < 0
+    assert f(A, 4, 128, 128, B, float("nan"), None, C, D, None) == ARG
+    assert f(A, 4, 128, 128, None, 1e-6, None, C, D, None) == NULL       # gain required
+    assert f(A, 4, 128, 128, B, 1e-6, None, None, D, None) == NULL
+    assert f(A + 2, 4, 128, 128, B, 1e-6, None, C, D, None) == ALIGN
+    assert f(A, 4, 128, 128, B + 4, 1e-6, None, C, D, None) == ALIGN     # gain 16-byte
+    assert f(A, 4, 128, 128, B, 1e-6, E + 8, C, D, None) == ALIGN        # y 16-byte
+    assert f(A, 4, 128, 128, B, 1e-6, None, A + 64, D, None) == ALIAS    # codes over h
+    assert f(A, 4, 128, 128, B, 1e-6, C + 256, C, D, None) == ALIAS      # y over codes
+    assert f(A, 4, 128, 128, B, 1e-6, None, C, B + 16, None) == ALIAS    # scales over gain
+    assert f(A, 0, 128, 128, B, 1e-6, None, C, D, None) == OK
 
 
 def batch(L, descs):

@@ -125,6 +125,48 @@ def test_quant_w_batched():
             assert qT is None and sT is None
 
 
+RMS_SHAPES = [(256, 512, 1e-6, "small"), (77, 200, 1e-6, "ragged rows, partial group"),
+              (1, 8, 1e-5, "one row, 8 columns"), (300, 5120, 1e-6, "32B hidden: 10 passes"),
+              (40, 27648, 1e-6, "down-proj width: row read twice"),
+              (8192, 4096, 1e-6, "prefill_8b hidden full size")]
+
+
+@pytest.mark.parametrize("rows,cols,eps,name", RMS_SHAPES)
+def test_rmsnorm_quant(rows, cols, eps, name):
+    """The fused norm + 1x128 quantize.  y is RN_bf16 of a binary32 evaluation whose sum of
+    squares has a relative error below ~2^-18, so y may differ from RN_bf16(exact) by one
+    ulp only where the exact value lies within 2^-17 (relative) of a bf16 midpoint; the
+    codes and scales must equal the oracle's 1x128 quantizer applied to the GPU's y, and the
+    call without y must give the same codes."""
+    say("rmsnorm_quant", rows, cols, name)
+    rng = np.random.default_rng(rows + cols)
+    h = qr_synth.normal_bf16(rows * 3 + cols, (rows, cols), 1.0, 7, max(1, cols // 100))
+    s_uaq = rng.uniform(1.5, 4.0, cols).astype(np.float32)      # gain carrying a UAQ scale
+    g = (rng.uniform(0.5, 2.0, cols) * s_uaq).astype(np.float32)
+    if rows > 4:
+        h[1] = 0                                                  # a zero row (eps > 0)
+        h[2] = qr_synth.f32_to_bf16_bits(np.full(cols, 3.0e-39, np.float32))  # subnormals
+    hd, gd = dev_bf16(h), dev(g)
+    y, q, s = qr.rmsnorm_quant(hd, gd, eps)
+    yg = host(y)
+    yx, yb = oracle.rmsnorm(h, g, eps)
+    diff = yg.astype(np.int32) - yb.astype(np.int32)
+    bad = np.argwhere(diff != 0)
+    assert np.all(np.abs(diff) <= 1), "y off by more than one bf16 ulp"
+    for i, j in bad[:2000]:
+        lo, hi = sorted((int(yg[i, j]) & 0x7FFF, int(yb[i, j]) & 0x7FFF))
+        mid = (float(qr_synth.bf16_bits_to_f32(np.array([lo], np.uint16))[0]) +
+               float(qr_synth.bf16_bits_to_f32(np.array([hi], np.uint16))[0])) / 2
+        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]), (i, j, yx[i, j])
+    assert bad.shape[0] <= max(2, yg.size // 500)
+    rq, rs = oracle.quant_rows(np.ascontiguousarray(yg))
+    assert_bitexact(host(q), rq, "codes of y")
+    assert_bitexact(host(s), rs, "scales of y")
+    _, q2, s2 = qr.rmsnorm_quant(hd, gd, eps, want_y=False)
+    assert_bitexact(host(q2), host(q), "codes without y")
+    assert_bitexact(host(s2), host(s), "scales without y")
+
+
 def test_quant_strided_input():
     say("quant strided ld")
     big = qr_synth.normal_bf16(11, (96, 640), 1.0)
