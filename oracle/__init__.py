@@ -13,6 +13,8 @@ marshals arguments and strings the definitions together:
 * ``fprop`` / ``dgrad`` / ``wgrad`` -- dequantize, then multiply in fp64 (returns Y and
   S = sum |a*b|, the quantity the GEMM tolerance is stated against).
 * ``uaq_fold``     -- W' = RN_bf16(W / s[col]), gain' = RN32(gain * s).
+* ``quant_int8_rows`` / ``gemm_int8`` -- the INT8 W8A8 variant (one symmetric scale per row,
+  exact integer products).
 * ``rmsnorm``      -- the norm whose gain carries the UAQ scale: y = h * gain / sqrt(mean(h^2)
   + eps) in fp64 and its RN_bf16 (the input of the fused norm-and-quantize kernel).
 
@@ -76,6 +78,14 @@ def lib():
         L.orc_uaq_fold.restype = ctypes.c_int
         L.orc_rmsnorm.argtypes = [_u16p, _i64, _i64, _i64, _f32p, ctypes.c_float, _f64p, _u16p]
         L.orc_rmsnorm.restype = ctypes.c_int
+        _i8p = ctypes.POINTER(ctypes.c_int8)
+        L.orc_quant_int8_rows.argtypes = [_u16p, _i64, _i64, _i64, _i8p, _f32p]
+        L.orc_quant_int8_rows.restype = ctypes.c_int
+        L.orc_gemm_int8.argtypes = [_i8p, _f32p, _i8p, _f32p, _i64, _i64, _i64, _f64p]
+        L.orc_gemm_int8.restype = None
+        L.orc_gemm_int8_sampled.argtypes = [_i8p, _f32p, _i8p, _f32p, _i64, _i64p, _i64p, _i64,
+                                            _f64p]
+        L.orc_gemm_int8_sampled.restype = None
         _LIB = L
     return _LIB
 
@@ -280,3 +290,39 @@ def rmsnorm(h_bf16: np.ndarray, gain: np.ndarray, eps: float):
                          _p(yb, _u16p)):
         raise ValueError("RMSNorm: non-finite input or gain, or a bad eps")
     return y, yb
+
+
+# ------------------------------------------------------------------ INT8 W8A8
+
+_i8p = ctypes.POINTER(ctypes.c_int8)
+
+
+def quant_int8_rows(x_bf16: np.ndarray):
+    """One symmetric INT8 scale per row of a [rows, cols] bf16 tensor -> (q int8 [rows, cols],
+    s f32 [rows])."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(rows, np.float32)
+    if lib().orc_quant_int8_rows(_p(x, _u16p), rows, cols, cols, _p(q, _i8p), _p(s, _f32p)):
+        raise ValueError("non-finite input to the INT8 quantizer")
+    return q, s
+
+
+def gemm_int8(qa, sa, qb, sb, sample=None):
+    """Y = sa[m] sb[n] sum_k qa[m, k] qb[n, k] (exact integer sum, fp64 scaling); with
+    sample=(mi, ni) only those positions."""
+    A, B = _c(qa, np.int8), _c(qb, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    sa, sb = _c(np.asarray(sa), np.float32), _c(np.asarray(sb), np.float32)
+    if sample is None:
+        Y = np.empty((M, N), np.float64)
+        lib().orc_gemm_int8(_p(A, _i8p), _p(sa, _f32p), _p(B, _i8p), _p(sb, _f32p), M, N, K,
+                            _p(Y, _f64p))
+        return Y
+    mi, ni = (_c(np.asarray(v), np.int64) for v in sample)
+    Y = np.empty(mi.size, np.float64)
+    lib().orc_gemm_int8_sampled(_p(A, _i8p), _p(sa, _f32p), _p(B, _i8p), _p(sb, _f32p), K,
+                                _p(mi, _i64p), _p(ni, _i64p), mi.size, _p(Y, _f64p))
+    return Y

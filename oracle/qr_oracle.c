@@ -32,6 +32,10 @@
  *     gain' = RN32(gain * s).
  *   - The norm whose gain carries s (the QuRL notes fold s into it) is the standard RMSNorm,
  *     y = h * gain / sqrt(mean(h^2) + eps), evaluated in binary64 and rounded once to bf16.
+ *   - The INT8 variant (QuRL's experiment setup: channel-wise weights, token-wise
+ *     activations) is symmetric: one scale per row, s = RN32(amax / 127); the code is the
+ *     binary32 quotient RN32(x / s) rounded to the nearest integer (ties to even) and clamped
+ *     to [-127, 127]; the GEMM is the exact integer dot product times both row scales.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math; x86-64 SSE
  * arithmetic, so binary32 and binary64 operations are correctly rounded and subnormals kept).
@@ -370,4 +374,70 @@ int orc_rmsnorm(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld, const
         }
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------- INT8 W8A8 variant */
+
+/* One symmetric scale per row (a token of the activation, an output channel of the weight):
+ * s[r] = RN32(amax_r / 127), q[r, c] = clamp(RNE(RN32(x[r, c] / s[r])), -127, 127), and 0 for
+ * a row with amax == 0.  Returns 0, or -1 on a non-finite input. */
+int orc_quant_int8_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int8_t *q,
+                        float *s)
+{
+    if (!all_finite_bf16(x, rows, cols, ld))
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) {
+            float a = fabsf(orc_bf16_to_f32(x[r * ld + c]));
+            if (a > amax)
+                amax = a;
+        }
+        float sc = amax / 127.0f;
+        s[r] = sc;
+        for (int64_t c = 0; c < cols; ++c) {
+            int8_t code = 0;
+            if (sc != 0.0f) {
+                float v = orc_bf16_to_f32(x[r * ld + c]) / sc;
+                double n = rint((double)v);            /* nearest integer, ties to even */
+                if (n > 127.0)
+                    n = 127.0;
+                if (n < -127.0)
+                    n = -127.0;
+                code = (int8_t)n;
+            }
+            q[r * cols + c] = code;
+        }
+    }
+    return 0;
+}
+
+/* Y[m, n] = sa[m] * sb[n] * sum_k A[m, k] * B[n, k]: the integer sum is exact (int64), the
+ * scaling in binary64.  Y may be NULL when only the sampled form is used. */
+void orc_gemm_int8(const int8_t *A, const float *sa, const int8_t *B, const float *sb, int64_t M,
+                   int64_t N, int64_t K, double *Y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)A[m * K + k] * (int64_t)B[n * K + k];
+            Y[m * N + n] = (double)sa[m] * (double)sb[n] * (double)acc;
+        }
+}
+
+/* The same at sampled positions (mi[t], ni[t]). */
+void orc_gemm_int8_sampled(const int8_t *A, const float *sa, const int8_t *B, const float *sb,
+                           int64_t K, const int64_t *mi, const int64_t *ni, int64_t count,
+                           double *Y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += (int64_t)A[mi[t] * K + k] * (int64_t)B[ni[t] * K + k];
+        Y[t] = (double)sa[mi[t]] * (double)sb[ni[t]] * (double)acc;
+    }
 }

@@ -1,8 +1,9 @@
 /*
  * Host check of the GPU kernels' per-element quotient (test code only).
  *
- * The quantizers need v = RN32(x / s) exactly (the code of x is E4M3(v)).  On the GPU each
- * 128-element group computes s = RN32(amax / 448) and r = RN32(1 / s) once, and each element
+ * The quantizers need v = RN32(x / s) exactly (the code of x is E4M3(v), or RNE(v) for the
+ * INT8 variant).  On the GPU each group computes s = RN32(amax / D), D = 448 for FP8 (the
+ * default) or 127 for INT8 (first argument), and r = RN32(1 / s) once, and each element
  * then takes three operations (P. Markstein, IBM J. Res. Dev. 34(1), 1990):
  *     q = RN(x * r);  e = RN(q * s - x) [one FMA];  v = RN(-e * r + q) [one FMA]
  * Groups with 0 < s < 2^-100 first scale both x and s by m = 2^64 (exact: a power of two
@@ -21,11 +22,12 @@
  *
  * Build at -O0: gcc -O2 folds the negations across the two FMAs, which is not sign-of-zero
  * safe (x = -0 then yields +0); the GPU compiler keeps the operations as written.
- * gcc -O0 -ffp-contract=off -fopenmp [-mfma] quotient_check.c -lm
+ * gcc -O0 -ffp-contract=off -fopenmp [-mfma] quotient_check.c -lm;  ./a.out [D]
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 static float bf16(uint32_t b)
@@ -43,13 +45,14 @@ static uint32_t bits(float f)
     return u;
 }
 
-int main(void)
+int main(int argc, char **argv)
 {
+    const float div = argc > 1 ? (float)atof(argv[1]) : 448.0f;
     long long mismatches = 0, pairs = 0, inexact = 0;
 #pragma omp parallel for schedule(dynamic, 64) reduction(+ : mismatches, pairs, inexact)
     for (uint32_t ab = 0; ab < 0x7F80u; ++ab) {          /* every finite amax >= 0 */
         const float amax = bf16(ab);
-        const float s = amax / 448.0f;
+        const float s = amax / div;
         const float m = (s > 0.0f && s < 0x1p-100f) ? 0x1p64f : 1.0f;
         const float sq = s * m;
         const float r = sq == 0.0f ? 0.0f : 1.0f / sq;
@@ -74,6 +77,7 @@ int main(void)
             inexact += bits(v) != bits(ref);
         }
     }
-    printf("pairs %lld mismatches %lld not_bit_identical %lld\n", pairs, mismatches, inexact);
+    printf("divisor %g pairs %lld mismatches %lld not_bit_identical %lld\n", (double)div, pairs,
+           mismatches, inexact);
     return mismatches != 0;
 }

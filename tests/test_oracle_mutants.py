@@ -2,7 +2,7 @@
 the oracle source (a wrong rounding rule, a dropped saturation, a lost sign of zero, a
 transposed or shifted scale index, a wrong constant, a reciprocal in place of the division, a
 dropped absolute value, a double rounding, an off-by-one group, a wrong mean, a dropped eps
-or gain in the norm) and runs the pin suite on that
+or gain in the norm, INT8 ties away from zero, a wrong INT8 divisor or scale index) and runs the pin suite on that
 copy, which must fail.  CPU only: the copies live in a temporary directory and the HIP library
 is not involved."""
 import os
@@ -32,6 +32,10 @@ MUTANTS = {
     "rms_mean_over_cols_plus_1": ("ss / (double)cols + (double)eps", "ss / (double)(cols + 1) + (double)eps"),
     "rms_no_eps": ("ss / (double)cols + (double)eps", "ss / (double)cols"),
     "rms_no_gain": ("* (double)gain[c] * inv", "* inv"),
+    "int8_ties_away": ("double n = rint((double)v);", "double n = round((double)v);"),
+    "int8_scale_128": ("float sc = amax / 127.0f;", "float sc = amax / 128.0f;"),
+    "int8_gemm_scale_index": ("(double)sa[m] * (double)sb[n] * (double)acc",
+                              "(double)sa[m] * (double)sb[m] * (double)acc"),
     "column_group_short": ("int64_t r0 = g * GROUP, r1 = r0 + GROUP < rows ? r0 + GROUP : rows;",
                            "int64_t r0 = g * GROUP, r1 = r0 + GROUP - 1 < rows ? "
                            "r0 + GROUP - 1 : rows;"),

@@ -553,3 +553,67 @@ def test_rmsnorm_rejections():
     h[1, 3] = 0x7F80
     with pytest.raises(ValueError):
         oracle.rmsnorm(h, g, 1e-6)
+
+
+# ============================================================== INT8 W8A8 variant
+
+def test_int8_rows_match_exact_rationals():
+    """s = RN32(amax / 127) and q = clamp(RNE(RN32(x / s)), +-127), decided in rationals
+    (Python rounds Fractions half to even)."""
+    for seed, std in ((81, 1.0), (83, 1e-3), (85, 3e4)):
+        x = qr_synth.normal_bf16(seed, (5, 200), std, seed + 1, 3)
+        q, s = oracle.quant_int8_rows(x)
+        xf = bf16_f32(x)
+        for r in range(5):
+            amax = max(abs(Fraction(float(v))) for v in xf[r])
+            sr = rn32(amax / 127)
+            assert Fraction(float(s[r])) == sr
+            for c in range(200):
+                n = round(rn32(Fraction(float(xf[r, c])) / sr))
+                assert int(q[r, c]) == max(-127, min(127, n)), (seed, r, c)
+
+
+def test_int8_ties_amax_zero_and_symmetries():
+    # amax = 127 gives s = 1 exactly, so x = k + 1/2 is an exact tie: to even
+    row = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, 126.5, -127.0]
+    x = qr_synth.f32_to_bf16_bits(np.array([row + [0.0] * 6], np.float32))
+    q, s = oracle.quant_int8_rows(x)
+    assert s[0] == 1.0
+    assert [int(v) for v in q[0, :10]] == [127, 2, 4, -2, -4, 0, 0, 2, 126, -127]
+    # the amax element of any row encodes to +-127; a zero row has s = 0 and zero codes
+    x = qr_synth.normal_bf16(87, (64, 96), 1.0)
+    x[5] = 0
+    q, s = oracle.quant_int8_rows(x)
+    amax_pos = np.argmax(np.abs(bf16_f32(x)), axis=1)
+    for r in range(64):
+        if r == 5:
+            assert s[r] == 0 and not q[r].any()
+        else:
+            assert abs(int(q[r, amax_pos[r]])) == 127
+    # sign symmetry and power-of-two invariance
+    qn, sn = oracle.quant_int8_rows(x ^ np.uint16(0x8000))
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    x2 = qr_synth.f32_to_bf16_bits(bf16_f32(x) * np.float32(2.0 ** 40))
+    q2, s2 = oracle.quant_int8_rows(x2)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(2.0 ** 40))
+    # error bound: |x - q s| <= s (1/2 + 127 * 2^-24): half a step, plus the binary32
+    # quotient's own rounding (relative 2^-24 of |x/s| <= 127)
+    err = np.abs(bf16_f32(x).astype(np.float64) - q * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 127 * 2.0 ** -24))
+
+
+def test_int8_gemm_brute_force():
+    rng = np.random.default_rng(89)
+    for M, N, K in ((3, 5, 128), (4, 4, 256), (2, 7, 384)):
+        qa = rng.integers(-127, 128, (M, K)).astype(np.int8)
+        qb = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        sa = rng.uniform(1e-3, 2.0, M).astype(np.float32)
+        sb = rng.uniform(1e-3, 2.0, N).astype(np.float32)
+        Y = oracle.gemm_int8(qa, sa, qb, sb)
+        for m in range(M):
+            for n in range(N):
+                acc = sum(int(qa[m, k]) * int(qb[n, k]) for k in range(K))
+                exact = Fraction(float(sa[m])) * Fraction(float(sb[n])) * acc
+                assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+        mi, ni = np.array([0, M - 1, 1]), np.array([N - 1, 0, 2])
+        assert np.array_equal(oracle.gemm_int8(qa, sa, qb, sb, sample=(mi, ni)), Y[mi, ni])

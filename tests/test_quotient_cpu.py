@@ -17,16 +17,20 @@ def _has_fma():
         return False
 
 
-def test_quotient_matches_ieee_division_for_every_bf16_pair(tmp_path):
+@pytest.mark.parametrize("divisor", ["448", "127"])
+def test_quotient_matches_ieee_division_for_every_bf16_pair(tmp_path, divisor):
+    """FP8 scales s = RN32(amax / 448) and INT8 scales s = RN32(amax / 127)."""
     exe = str(tmp_path / "quotient_check")
     cmd = ["gcc", "-O0", "-ffp-contract=off", "-fopenmp", os.path.join(HERE, "quotient_check.c"),
            "-o", exe, "-lm"]
     if _has_fma():
         cmd.insert(3, "-mfma")
     subprocess.run(cmd, check=True)
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    r = subprocess.run([exe, divisor], capture_output=True, text=True, timeout=600)
     print(r.stdout)
-    fields = dict(zip(r.stdout.split()[0::2], map(int, r.stdout.split()[1::2])))
+    words = r.stdout.split()
+    fields = dict(zip(words[2::2], map(int, words[3::2])))
+    assert words[:2] == ["divisor", divisor]
     assert fields["pairs"] == 1065402240          # every finite (amax, x) with |x| <= amax
     assert fields["mismatches"] == 0, r.stdout
     assert r.returncode == 0
