@@ -22,8 +22,9 @@ event overhead.  The JSON line reports the step's GEMM throughput (all GEMM flop
 time) as `value`, each op's time with its roofline fraction, the roofline of the dominant
 kernel from its launches in the timed pass, and the CPU oracle timed on a bounded token slice
 of the same step.  Outside the step it also times the batched re-quantization of a 32B
-decoder layer's four weights (`weight_update`, once per optimizer step) and the norm with the
-activation quantize fused in (`norm_quant`, the producer of FProp's operand).
+decoder layer's four weights (`weight_update`, once per optimizer step), the norm with the
+activation quantize fused in (`norm_quant`, the producer of FProp's operand) and the INT8
+W8A8 variant at the same shapes (`int8_w8a8`).
 """
 import argparse
 import hashlib
@@ -39,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak) + quantize GB/s (% HBM)"
 
 T, H, F, MD = 8192, 4096, 14336, 64     # tokens, hidden, decode FFN width, decode batch
@@ -227,10 +229,11 @@ def run_gpu(args):
     step_ms = start.elapsed_time(end) / args.steps
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
     normq = run_norm_quant(torch, qr, st)
+    int8 = run_int8(torch, qr, st)
     del st, ops
     torch.cuda.empty_cache()
     upd = run_weight_update(torch, qr)
-    return step_ms, wall, per_op, dom, dom_ms, upd, normq
+    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8
 
 
 def run_norm_quant(torch, qr, st, iters=20):
@@ -260,6 +263,57 @@ def run_norm_quant(torch, qr, st, iters=20):
                         "codes and scales out (the FProp operand)",
             "us": round(us, 2), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def _median_us(torch, f, iters):
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        f()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
+def run_int8(torch, qr, st, iters=20):
+    """The INT8 W8A8 variant at the same shapes: the per-token quantize of X [8192, 4096], the
+    prefill GEMM 8192x4096x4096 and the decode GEMM 64x14336x4096 (bf16 out)."""
+    dev = "cuda:0"
+    e = lambda *sh, dt: torch.empty(sh, dtype=dt, device=dev)
+    i8, f32, bf = torch.int8, torch.float32, torch.bfloat16
+    qx, sx = e(T, H, dt=i8), e(T, dt=f32)
+    qw, sw = e(H, H, dt=i8), e(H, dt=f32)
+    qr.qr_quant_int8_rowwise(st.W, H, H, H, qw, sw)
+    g = torch.Generator(device=dev).manual_seed(7001)
+    wd = (torch.randn((F, H), device=dev, generator=g) * 0.02).to(bf)
+    qwd, swd = e(F, H, dt=i8), e(F, dt=f32)
+    qr.qr_quant_int8_rowwise(wd, F, H, H, qwd, swd)
+    del wd
+    qxd, sxd = e(MD, H, dt=i8), e(MD, dt=f32)
+    qr.qr_quant_int8_rowwise(st.Xd, MD, H, H, qxd, sxd)
+    y, yd = e(T, H, dt=bf), e(MD, F, dt=bf)
+    out = {}
+    us = _median_us(torch, lambda: qr.qr_quant_int8_rowwise(st.X, T, H, H, qx, sx), iters)
+    nb = T * H * 3 + T * 4
+    out["quant_x"] = {"us": round(us, 2), "bound": "hbm", "bytes": nb,
+                      "achieved": round(nb / us / 1e3, 1), "unit": "GB/s",
+                      "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    us = _median_us(torch, lambda: qr.qr_gemm_int8_w8a8(qx, sx, qw, sw, T, H, H, y, 1), iters)
+    tops = 2.0 * T * H * H / (us * 1e-6) / 1e12
+    out["gemm_prefill"] = {"shape": [T, H, H], "us": round(us, 2), "bound": "mfma",
+                           "achieved": round(tops, 1), "unit": "TOP/s",
+                           "frac": round(tops / PEAK_INT8_TOPS, 4)}
+    us = _median_us(torch, lambda: qr.qr_gemm_int8_w8a8(qxd, sxd, qwd, swd, MD, F, H, yd, 1), iters)
+    nb = F * H + F * 4 + MD * H + MD * 4 + MD * F * 2
+    out["gemm_decode"] = {"shape": [MD, F, H], "us": round(us, 2), "bound": "hbm", "bytes": nb,
+                          "achieved": round(nb / us / 1e3, 1), "unit": "GB/s",
+                          "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def run_weight_update(torch, qr, iters=10):
@@ -359,7 +413,7 @@ def main():
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms, upd, normq = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8 = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -396,6 +450,7 @@ def main():
         "kernels": kernels,
         "weight_update": upd,
         "norm_quant": normq,
+        "int8_w8a8": int8,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

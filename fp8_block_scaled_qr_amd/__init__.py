@@ -23,7 +23,8 @@ QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD = 0, 1, 2
 
 # Every entry point include/qr.h declares.
 EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant_w_128x128",
-           "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_gemm_fp8_bsfprop",
+           "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_quant_int8_rowwise",
+           "qr_gemm_int8_w8a8", "qr_gemm_fp8_bsfprop",
            "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes",
            "qr_uaq_fold")
 QR_MAX_WEIGHT_BATCH = 4096
@@ -66,6 +67,10 @@ def load():
     L.qr_quant_w_128x128_batched.restype = I32
     L.qr_rmsnorm_quant_1x128.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P]
     L.qr_rmsnorm_quant_1x128.restype = I32
+    L.qr_quant_int8_rowwise.argtypes = [P, I64, I64, I64, P, P, P]
+    L.qr_quant_int8_rowwise.restype = I32
+    L.qr_gemm_int8_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+    L.qr_gemm_int8_w8a8.restype = I32
     for name in ("qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad"):
         f = getattr(L, name)
         f.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
@@ -138,6 +143,16 @@ def qr_rmsnorm_quant_1x128(h, rows, cols, ld_h, gain, eps, y, q_row, s_row, stre
     _check(load().qr_rmsnorm_quant_1x128(_ptr(h), rows, cols, ld_h, _ptr(gain), float(eps),
                                          _ptr(y), _ptr(q_row), _ptr(s_row), _stream(stream)),
            "qr_rmsnorm_quant_1x128")
+
+
+def qr_quant_int8_rowwise(x, rows, cols, ld_x, q, s, stream=None):
+    _check(load().qr_quant_int8_rowwise(_ptr(x), rows, cols, ld_x, _ptr(q), _ptr(s),
+                                        _stream(stream)), "qr_quant_int8_rowwise")
+
+
+def qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, y_dtype, stream=None):
+    _check(load().qr_gemm_int8_w8a8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(y),
+                                    int(y_dtype), _stream(stream)), "qr_gemm_int8_w8a8")
 
 
 def _gemm(name, a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream):
@@ -238,6 +253,25 @@ def rmsnorm_quant(h, gain, eps=1e-6, want_y=True, stream=None):
     s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=dev)
     qr_rmsnorm_quant_1x128(h, rows, cols, h.stride(0), gain, eps, y, q, s, stream)
     return y, q, s
+
+
+def quant_int8(x, stream=None):
+    """x: bf16 [rows, cols] on the GPU -> (q int8 [rows, cols], s fp32 [rows])."""
+    import torch
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    qr_quant_int8_rowwise(x, rows, cols, x.stride(0), q, s, stream)
+    return q, s
+
+
+def gemm_int8(a, sa, b, sb, out_dtype=QR_OUT_BF16, stream=None):
+    """a int8 [M, K] with sa [M], b int8 [N, K] with sb [N] -> y [M, N]."""
+    M, K = a.shape
+    N = b.shape[0]
+    y = _out(M, N, out_dtype, a.device)
+    qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, out_dtype, stream)
+    return y
 
 
 def _workspace(kind, M, N, K, device):

@@ -217,6 +217,55 @@ qr_status qr_rmsnorm_quant_1x128(const void *h_bf16, int64_t rows, int64_t cols,
         static_cast<uint16_t *>(y_bf16), q_row, s_row, (hipStream_t)stream));
 }
 
+qr_status qr_quant_int8_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                int8_t *q, float *s, qr_stream stream)
+{
+    if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (cols % 8 != 0 || ld_x % 8 != 0 || (rows > 0 && ld_x < cols) || ld_x >= kMaxLd)
+        return QR_ERR_SHAPE;
+    if (rows == 0 || cols == 0)
+        return QR_OK;
+    if (!x_bf16 || !q || !s)
+        return QR_ERR_NULL;
+    if (misaligned(x_bf16, 16) || misaligned(q, 16) || misaligned(s, 4))
+        return QR_ERR_ALIGN;
+    const Range rx = span(x_bf16, strided_bytes(rows, cols, ld_x, 2));
+    const Range rq = span(q, rows * cols), rs = span(s, rows * 4);
+    if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs))
+        return QR_ERR_ALIAS;
+    return launch_status(qr::launch_quant_int8_rows(static_cast<const uint16_t *>(x_bf16), rows,
+                                                    cols, ld_x, q, s, (hipStream_t)stream));
+}
+
+qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, const float *sb,
+                            int64_t M, int64_t N, int64_t K, void *y, qr_out_dtype y_dtype,
+                            qr_stream stream)
+{
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (K % 128 != 0 || K > 131072)   // |sum| <= 127^2 K must fit an int32
+        return QR_ERR_SHAPE;
+    if (y_dtype != QR_OUT_F32 && y_dtype != QR_OUT_BF16)
+        return QR_ERR_ARG;
+    if (M == 0 || N == 0)
+        return QR_OK;
+    if (!a || !sa || !b || !sb || !y)
+        return QR_ERR_NULL;
+    if (misaligned(a, 16) || misaligned(b, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
+        misaligned(sb, 4))
+        return QR_ERR_ALIGN;
+    const int64_t esz = y_dtype == QR_OUT_BF16 ? 2 : 4;
+    const Range ry = span(y, M * N * esz);
+    const Range ins[4] = {span(a, M * K), span(sa, M * 4), span(b, N * K), span(sb, N * 4)};
+    for (const Range &r : ins)
+        if (overlap(ry, r))
+            return QR_ERR_ALIAS;
+    // K == 0 (empty contraction) runs the same kernel: no step executes and zeros are stored
+    return launch_status(qr::launch_gemm_i8(y_dtype == QR_OUT_BF16, a, sa, b, sb, M, N, K, y,
+                                            (hipStream_t)stream));
+}
+
 qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *q,
                              float *s, uint8_t *qT, float *sT, qr_stream stream)
 {

@@ -673,6 +673,180 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
     }
 }
 
+// ---------------------------------------------------------------- INT8 W8A8 GEMM
+
+struct GemmI8Args {
+    const int8_t *A;     // [M, K]
+    const float *sa;     // [M]
+    const int8_t *B;     // [N, K]
+    const float *sb;     // [N]
+    void *C;             // [M, N], fp32 or bf16
+    int64_t M, N, K;
+    int nk;              // K / 128
+    int tilesM, tilesN;
+};
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// C[m, n] = sa[m] * sb[n] * sum_k A[m, k] B[n, k] with one symmetric scale per row of each
+// operand: the integer sum is exact in the int32 MFMA accumulators (|sum| <= 127^2 K), so the
+// MFMAs accumulate in place over all of K and both scales are applied once, in the epilogue.
+// Staging is the FP8 GEMM's: 128-byte rows of both operands go straight to swizzled LDS, two
+// stages.  A 32-byte fragment (lane l: row l % 16, 16-byte chunks 2 (l / 16) and
+// 2 (l / 16) + 1 of the 128-byte K step) feeds two 16x16x64 MFMAs, one per chunk; A and B use
+// the same lane-to-K assignment, so together the two cover all 128 K of the step.
+template <class T, bool OUT_BF16>
+__global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
+{
+    constexpr int NW = T::WM * T::WN;
+    constexpr int DA = T::BM / 8 / NW, DB = T::BN / 8 / NW;
+    static_assert(DA * 8 * NW == T::BM && DB * 8 * NW == T::BN, "whole 1 KB loads per wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][T::BM * kGroup];
+    __shared__ __attribute__((aligned(1024))) uint8_t smB[2][T::BN * kGroup];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    const int lq = lane >> 4, lr = lane & 15;
+
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0)
+        bid = (bid & 7) * (nb >> 3) + (bid >> 3);   // a contiguous band of tiles per XCD
+    const int tm = bid / g.tilesN, tn = bid - tm * g.tilesN;
+    const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int nk = g.nk;
+
+    auto swz = [](int row) { return (row & 7) ^ ((row >> 3) & 1); };
+    const int frow = lane & 15, fq = lane >> 4;
+    const int frag_lo = frow * 128 + (((2 * fq) ^ swz(frow)) << 4);
+    const int frag_hi = frow * 128 + (((2 * fq + 1) ^ swz(frow)) << 4);
+
+    const int64_t rowsA = M - m0 < T::BM ? M - m0 : T::BM;
+    const int64_t rowsB = N - n0 < T::BN ? N - n0 : T::BN;
+    const v4i_sgpr rA = make_rsrc_sgpr(g.A + m0 * K, (uint32_t)(rowsA * K));
+    const v4i_sgpr rB = make_rsrc_sgpr(g.B + n0 * K, (uint32_t)(rowsB * K));
+    const int lrow = lane >> 3, lslot = lane & 7;
+    auto tile_voff = [&](int t) -> uint32_t {
+        const int row = 8 * t + lrow;
+        return (uint32_t)(row * K + ((lslot ^ swz(row)) << 4));
+    };
+    const uint32_t ldsA = lds_addr_of(&smA[0][0]), ldsB = lds_addr_of(&smB[0][0]);
+    auto issue_step = [&](int kg, int st) {
+        const uint32_t k0 = (uint32_t)kg * kGroup;
+#pragma unroll
+        for (int j = 0; j < DA; ++j) {
+            const int t = wave + j * NW;
+            dma16(rA, ldsA + (uint32_t)(st * T::BM * kGroup + t * 1024), tile_voff(t) + k0);
+        }
+#pragma unroll
+        for (int j = 0; j < DB; ++j) {
+            const int t = wave + j * NW;
+            dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
+        }
+    };
+
+    v4i acc[T::IM][T::JN];
+#pragma unroll
+    for (int i = 0; i < T::IM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::JN; ++j)
+            acc[i][j] = v4i{0, 0, 0, 0};
+
+    struct Frag {
+        v4i lo, hi;
+    };
+    auto frag = [&](const uint8_t *tileBase, int r0) -> Frag {
+        const uint8_t *p = tileBase + r0 * 128;
+        Frag f;
+        f.lo = *reinterpret_cast<const v4i *>(p + frag_lo);
+        f.hi = *reinterpret_cast<const v4i *>(p + frag_hi);
+        return f;
+    };
+    auto compute = [&](const uint8_t *tA, const uint8_t *tB) {
+        Frag bf[T::JN];
+#pragma unroll
+        for (int j = 0; j < T::JN; ++j)
+            bf[j] = frag(tB, wn * T::TN + j * 16);
+        Frag afb[2];
+        afb[0] = frag(tA, wm * T::TM);
+        // per sub-tile row i: the JN low-half MFMAs, then the JN high-half ones, so the two
+        // MFMAs into one accumulator sit JN instructions apart instead of back to back
+#pragma unroll
+        for (int i = 0; i < T::IM; ++i) {
+            if (i + 1 < T::IM)
+                afb[(i + 1) & 1] = frag(tA, wm * T::TM + (i + 1) * 16);
+#pragma unroll
+            for (int j = 0; j < T::JN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[j].lo, afb[i & 1].lo,
+                                                                   acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < T::JN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[j].hi, afb[i & 1].hi,
+                                                                   acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // main loop: as the FP8 GEMM's (step k issues step k+1's loads into the other stage,
+    // computes, waits for its own loads, then the barrier publishes the stage)
+    const int glast = nk - 1;
+    if (nk > 0)
+        issue_step(0, 0);
+    vm_wait<0>();
+    stage_barrier();
+#pragma nounroll
+    for (int kg = 0; kg < nk; ++kg) {
+        const int st = kg & 1;
+        issue_step(min(kg + 1, glast), st ^ 1);
+        compute(smA[st], smB[st]);
+        vm_wait<0>();
+        stage_barrier();
+    }
+
+    // epilogue: lane holds C[m][n .. n + 3] of each sub-tile
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < T::IM; ++i) {
+        const int64_t m = m0 + wm * T::TM + i * 16 + lr;
+        if (m >= M)
+            continue;
+        const float am = g.sa[m];
+#pragma unroll
+        for (int j = 0; j < T::JN; ++j) {
+            const int64_t n = n0 + wn * T::TN + j * 16 + 4 * lq;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[r] = n + r < N ? (float)acc[i][j][r] * (am * g.sb[n + r]) : 0.0f;
+            if (!OUT_BF16) {
+                float *c = reinterpret_cast<float *>(g.C) + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    *reinterpret_cast<float4 *>(c) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            c[r] = v[r];
+                }
+            } else {
+                uint16_t *c = reinterpret_cast<uint16_t *>(g.C) + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    uint2 o;
+                    o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+                    o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<uint2 *>(c) = o;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            c[r] = (uint16_t)f32_to_bf16(v[r]);
+                }
+            }
+        }
+    }
+}
+
 // Tile configurations, indexed by GemmPlan::cfg.
 using CfgBig4 = TileCfg<256, 256, 2, 4>;   // prefill / training: 8 waves, 128x64 per wave
 using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
@@ -680,6 +854,15 @@ using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
 using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
 
 enum { CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_SKINNY = 5 };
+#ifndef QR_I8_SMALL_BN
+#define QR_I8_SMALL_BN 32
+#endif
+#ifndef QR_I8_SMALL_WN
+#define QR_I8_SMALL_WN 2
+#endif
+// INT8 GEMM for decode-sized M: 64x32 tiles, 2 waves (64x16 each), so a 14336-wide weight
+// gives 448 workgroups (the HBM stream needs many of them in flight)
+using CfgI8Small = TileCfg<64, QR_I8_SMALL_BN, 1, QR_I8_SMALL_WN>;
 
 #ifndef QR_SKINNY_NW
 #define QR_SKINNY_NW 4
@@ -818,6 +1001,42 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
         k_splitk_reduce<true><<<(unsigned)rb, 256, 0, stream>>>((const float *)ws, MN, plan.split, C);
     else
         k_splitk_reduce<false><<<(unsigned)rb, 256, 0, stream>>>((const float *)ws, MN, plan.split, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const int8_t *B,
+                          const float *sb, int64_t M, int64_t N, int64_t K, void *C,
+                          hipStream_t stream)
+{
+    GemmI8Args a;
+    a.A = A;
+    a.sa = sa;
+    a.B = B;
+    a.sb = sb;
+    a.C = C;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.nk = (int)(K / kGroup);
+    // 256x256 tiles when they give every CU a workgroup (prefill and training sizes), else
+    // 64x32 tiles (decode and small batches), which fill the chip at any M
+    const int64_t big_tiles = ((M + CfgBig4::BM - 1) / CfgBig4::BM) * ((N + CfgBig4::BN - 1) / CfgBig4::BN);
+    const bool big = big_tiles >= 256;
+    const int bm = big ? CfgBig4::BM : CfgI8Small::BM, bn = big ? CfgBig4::BN : CfgI8Small::BN;
+    a.tilesM = (int)((M + bm - 1) / bm);
+    a.tilesN = (int)((N + bn - 1) / bn);
+    const unsigned blocks = (unsigned)(a.tilesM * a.tilesN);
+    if (big) {
+        if (out_bf16)
+            k_gemm_i8<CfgBig4, true><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
+        else
+            k_gemm_i8<CfgBig4, false><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
+    } else {
+        if (out_bf16)
+            k_gemm_i8<CfgI8Small, true><<<blocks, CfgI8Small::THREADS, 0, stream>>>(a);
+        else
+            k_gemm_i8<CfgI8Small, false><<<blocks, CfgI8Small::THREADS, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

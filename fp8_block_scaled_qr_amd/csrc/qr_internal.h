@@ -55,6 +55,15 @@ hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
                            const float *s, uint16_t *w_out, int64_t ld_out, float *gain,
                            hipStream_t stream);
 
+// INT8 W8A8: C[m, n] = sa[m] * sb[n] * sum_k A[m, k] B[n, k] (int8 codes, K % 128 == 0).
+hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const int8_t *B,
+                          const float *sb, int64_t M, int64_t N, int64_t K, void *C,
+                          hipStream_t stream);
+
+// One symmetric INT8 scale per row: s [rows], q [rows, cols].
+hipError_t launch_quant_int8_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  int8_t *q, float *s, hipStream_t stream);
+
 // B-operand scale layouts of the block-scaled GEMM C[m, n] = sum_k A[m, k] B[n, k].
 enum : int {
     BSCALE_BLOCK = 0,  // sb [ceil(N/128), K/128]: one scale per 128x128 block of B

@@ -482,6 +482,78 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restric
     }
 }
 
+// ---------------------------------------------------------------- INT8 W8A8 rows
+
+// 8 int8 codes of one 16-byte bf16 load: clamp(RNE(RN32(x / s)), +-127)
+template <bool LIFT>
+__device__ __forceinline__ uint2 encode8_i8(const uint4 &v, const Scale &sc)
+{
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float n = __builtin_rintf(quot_t<LIFT>(bf16_elem(v, i), sc));   // ties to even
+        n = fminf(fmaxf(n, -127.0f), 127.0f);
+        w[i >> 2] |= ((uint32_t)(int32_t)n & 0xFFu) << (8 * (i & 3));
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+// One symmetric scale per row (a token of an activation, an output channel of a weight):
+// s = RN32(amax / 127).  One wave per row; pass p covers columns 512 p .. 512 p + 511, 16
+// bytes per lane.  NP > 0: the row stays in registers (NP passes at most); NP == 0: it is
+// read twice.
+template <int NP>
+__global__ __launch_bounds__(256) void k_quant_int8_rows(const uint16_t *__restrict__ x,
+                                                         int64_t rows, int64_t cols, int64_t ldx,
+                                                         uint8_t *__restrict__ q,
+                                                         float *__restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;   // the whole wave; no barrier follows
+    const int64_t npass = (cols + 511) / 512;
+    const uint16_t *xr = x + row * ldx;
+    auto load = [&](int64_t p) -> uint4 {
+        const int64_t c = 512 * p + 8 * lane;   // cols % 8 == 0: an octet is all in or out
+        return c < cols ? *reinterpret_cast<const uint4 *>(xr + c) : make_uint4(0, 0, 0, 0);
+    };
+    uint32_t m = 0;
+    uint4 keep[NP > 0 ? NP : 1];
+    if (NP > 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            keep[p] = p < npass ? load(p) : make_uint4(0, 0, 0, 0);
+            m = umax(m, absmax8(keep[p]));
+        }
+    } else {
+        for (int64_t p = 0; p < npass; ++p)
+            m = umax(m, absmax8(load(p)));
+    }
+    m = row16_max(m);
+    m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
+    m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
+    const Scale sc = scale_of(__fdiv_rn(__uint_as_float(m << 16), 127.0f));
+    if (lane == 0)
+        s[row] = sc.s;
+    const bool lift = tiny_scale(sc);   // uniform across the wave
+    auto body = [&](int64_t p, const uint4 &v) {
+        const int64_t c = 512 * p + 8 * lane;
+        if (c < cols)
+            *reinterpret_cast<uint2 *>(q + row * cols + c) =
+                lift ? encode8_i8<true>(v, sc) : encode8_i8<false>(v, sc);
+    };
+    if (NP > 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            if (p < npass)
+                body(p, keep[p]);
+    } else {
+        for (int64_t p = 0; p < npass; ++p)
+            body(p, load(p));
+    }
+}
+
 // ---------------------------------------------------------------- UAQ fold
 
 // RN_bf16(w / s), general case: the quotient is formed in binary64 (correctly rounded) and
@@ -684,6 +756,23 @@ hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t rows, int64_t cols, i
         k_rmsnorm_quant<16><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
     else
         k_rmsnorm_quant<0><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_int8_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  int8_t *q8, float *s, hipStream_t stream)
+{
+    if (rows == 0 || cols == 0)
+        return hipSuccess;
+    uint8_t *q = reinterpret_cast<uint8_t *>(q8);
+    const int64_t npass = (cols + 511) / 512;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (npass <= 8)
+        k_quant_int8_rows<8><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s);
+    else if (npass <= 16)
+        k_quant_int8_rows<16><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s);
+    else
+        k_quant_int8_rows<0><<<grid, 256, 0, stream>>>(x, rows, cols, ld_x, q, s);
     return hipGetLastError();
 }
 

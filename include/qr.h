@@ -103,6 +103,32 @@ qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int
                              qr_stream stream);
 
 /*
+ * INT8 W8A8 variant [QURL, experiment setup: channel-wise weight quantization and token-wise
+ * activation quantization, INT8 or FP8; the rollout's INT8 GEMM].  Symmetric, one scale per
+ * row: a row is a token of an activation or an output channel of a weight [n, k].
+ *   s[r] = RN32(amax_r / 127);  q[r, c] = clamp(RNE(RN32(x[r, c] / s[r])), -127, 127)
+ * (RNE: nearest integer, ties to even; a row with amax == 0 has s == 0 and zero codes).
+ *   x  bf16 [rows, cols], leading dimension ld_x;  q int8 [rows, cols];  s fp32 [rows].
+ * Size rules: rows, cols >= 0; cols % 8 == 0, ld_x % 8 == 0, ld_x < 2^22.  x and q 16-byte
+ * aligned, s 4-byte aligned; no output may overlap an input or the other output.
+ */
+qr_status qr_quant_int8_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                int8_t *q, float *s, qr_stream stream);
+
+/*
+ * INT8 W8A8 GEMM: y[m, n] = sa[m] * sb[n] * sum_k a[m, k] b[n, k], with the integer sum exact
+ * (int32) and the scaling in binary32 (y = float(sum) * (sa[m] * sb[n])).
+ *   a  int8 [M, K] with sa [M] (qr_quant_int8_rowwise of the activation)
+ *   b  int8 [N, K] with sb [N] (qr_quant_int8_rowwise of the weight W[N, K])
+ *   y  [M, N], fp32 or bf16 per y_dtype.
+ * Size rules: M, N >= 0; K % 128 == 0 and K <= 131072 (the sum stays within int32).  a, b, y
+ * 16-byte aligned, sa, sb 4-byte aligned; y must not overlap an input.  No workspace.
+ */
+qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, const float *sb,
+                            int64_t M, int64_t N, int64_t K, void *y, qr_out_dtype y_dtype,
+                            qr_stream stream);
+
+/*
  * Norm and activation quantize in one pass (the producer of the FProp operand).  The norm in
  * front of a linear layer carries the UAQ scale in its gain [QURL, key design 1: s is
  * folded into the norm once], and its output is what [JET] quantizes in 1x128 groups; this

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 13, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -102,6 +102,27 @@ def test_rmsnorm_quant_validation(L):
     assert f(A, 4, 128, 128, B, 1e-6, C + 256, C, D, None) == ALIAS      # y over codes
     assert f(A, 4, 128, 128, B, 1e-6, None, C, B + 16, None) == ALIAS    # scales over gain
     assert f(A, 0, 128, 128, B, 1e-6, None, C, D, None) == OK
+
+
+def test_int8_validation(L):
+    f = L.qr_quant_int8_rowwise
+    assert f(A, -1, 128, 128, B, C, None) == SHAPE
+    assert f(A, 4, 100, 104, B, C, None) == SHAPE                        # cols % 8
+    assert f(A, 4, 128, 120, B, C, None) == SHAPE                        # ld < cols
+    assert f(A, 4, 128, 128, None, C, None) == NULL
+    assert f(A + 2, 4, 128, 128, B, C, None) == ALIGN
+    assert f(A, 4, 128, 128, B + 8, C, None) == ALIGN
+    assert f(A, 4, 128, 128, A + 16, C, None) == ALIAS                   # codes over x
+    assert f(A, 4, 128, 128, B, B + 256, None) == ALIAS                  # scales over codes
+    assert f(A, 0, 128, 128, B, C, None) == OK
+    g = L.qr_gemm_int8_w8a8
+    assert g(A, B, C, D, 64, 64, 100, E, 1, None) == SHAPE               # K % 128
+    assert g(A, B, C, D, 64, 64, 131072 + 128, E, 1, None) == SHAPE      # int32 range
+    assert g(A, B, C, D, 64, 64, 128, E, 7, None) == ARG                 # output dtype
+    assert g(None, B, C, D, 64, 64, 128, E, 1, None) == NULL
+    assert g(A, B, C + 4, D, 64, 64, 128, E, 1, None) == ALIGN
+    assert g(A, B, C, D, 64, 64, 128, A + 1024, 1, None) == ALIAS        # y over a
+    assert g(A, B, C, D, 0, 64, 128, E, 1, None) == OK
 
 
 def batch(L, descs):

@@ -167,6 +167,64 @@ def test_rmsnorm_quant(rows, cols, eps, name):
     assert_bitexact(host(s2), host(s), "scales without y")
 
 
+INT8_ROWS = [(256, 512), (77, 200), (1, 8), (300, 5120), (40, 27648), (8192, 4096)]
+
+
+@pytest.mark.parametrize("rows,cols", INT8_ROWS)
+def test_quant_int8_rows(rows, cols):
+    """One symmetric INT8 scale per row: codes and scales bit-exact.  Covers the register-
+    resident rows (up to 8192 columns) and re-read rows, partial passes, a zero row, a row of
+    bf16 subnormals (a lifted scale) and a row of huge values."""
+    say("quant_int8", rows, cols)
+    x = qr_synth.normal_bf16(rows * 5 + cols, (rows, cols), 1.0, 11, max(1, cols // 100))
+    if rows > 4:
+        x[1] = 0
+        x[2] = qr_synth.f32_to_bf16_bits(np.linspace(-3e-39, 3e-39, cols).astype(np.float32))
+        x[3] = qr_synth.f32_to_bf16_bits(np.linspace(-3e38, 2e38, cols).astype(np.float32))
+    q, s = qr.quant_int8(dev_bf16(x))
+    rq, rs = oracle.quant_int8_rows(x)
+    assert_bitexact(host(q), rq, "int8 codes")
+    assert_bitexact(host(s), rs, "int8 scales")
+
+
+def _int8_case(M, N, K, seed):
+    x = qr_synth.normal_bf16(seed, (M, K), 1.0, seed + 1, max(1, K // 100))
+    w = qr_synth.normal_bf16(seed + 2, (N, K), 0.02)
+    qa, sa = oracle.quant_int8_rows(x)
+    qb, sb = oracle.quant_int8_rows(w)
+    return qa, sa, qb, sb
+
+
+def _check_int8(y, Y, out):
+    """fp32 out: |y - Y| <= 2^-22 |Y| (three binary32 roundings in the epilogue); bf16 out:
+    plus the bf16 rounding, at most 2^-8 |Y| (8 significant bits)."""
+    rel = 2.0 ** -22 if out == qr.QR_OUT_F32 else 2.0 ** -8 + 2.0 ** -21
+    err = np.abs(y - Y)
+    assert np.all(err <= rel * np.abs(Y)), float(np.max(err / np.maximum(np.abs(Y), 1e-300)))
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 200, 384), (64, 1000, 1024), (1, 128, 128),
+                                   (300, 264, 256), (520, 304, 384), (17, 72, 640)])
+@pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
+def test_gemm_int8(M, N, K, out):
+    say("gemm_int8", M, N, K, out)
+    qa, sa, qb, sb = _int8_case(M, N, K, M + N + K)
+    y = qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=out)
+    _check_int8(out_f64(y), oracle.gemm_int8(qa, sa, qb, sb), out)
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 4096, 4096), (64, 14336, 4096), (256, 5120, 27648)])
+def test_gemm_int8_full_size_sampled(M, N, K):
+    """The 8B prefill shape, the 8B decode shape and the 32B down projection at batch 256, on
+    sampled outputs (every tile and both ragged ends hit)."""
+    say("gemm_int8 full", M, N, K)
+    qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
+    y = out_f64(qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_BF16))
+    mi, ni = sample_positions(M, N, 4096, seed=M + N)
+    Y = oracle.gemm_int8(qa, sa, qb, sb, sample=(mi, ni))
+    _check_int8(y[mi, ni], Y, qr.QR_OUT_BF16)
+
+
 def test_quant_strided_input():
     say("quant strided ld")
     big = qr_synth.normal_bf16(11, (96, 640), 1.0)
