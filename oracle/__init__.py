@@ -13,6 +13,8 @@ marshals arguments and strings the definitions together:
 * ``fprop`` / ``dgrad`` / ``wgrad`` -- dequantize, then multiply in fp64 (returns Y and
   S = sum |a*b|, the quantity the GEMM tolerance is stated against).
 * ``uaq_fold``     -- W' = RN_bf16(W / s[col]), gain' = RN32(gain * s).
+* ``quant_nvfp4`` / ``gemm_w4a16`` -- the 4-bit weight path (E2M1 elements, E4M3 scales per
+  16, an fp32 tensor scale) and its bf16-activation GEMM.
 * ``quant_int8_rows`` / ``gemm_int8`` -- the INT8 W8A8 variant (one symmetric scale per row,
   exact integer products).
 * ``rmsnorm``      -- the norm whose gain carries the UAQ scale: y = h * gain / sqrt(mean(h^2)
@@ -86,6 +88,15 @@ def lib():
         L.orc_gemm_int8_sampled.argtypes = [_i8p, _f32p, _i8p, _f32p, _i64, _i64p, _i64p, _i64,
                                             _f64p]
         L.orc_gemm_int8_sampled.restype = None
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_decode.restype = ctypes.c_double
+        L.orc_e2m1_encode.argtypes = [ctypes.c_float]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_quant_nvfp4.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _u8p, _f32p]
+        L.orc_quant_nvfp4.restype = ctypes.c_int
+        L.orc_gemm_w4a16.argtypes = [_u16p, _u8p, _u8p, ctypes.c_float, _i64, _i64, _i64, _i64p,
+                                     _i64p, _i64, _f64p]
+        L.orc_gemm_w4a16.restype = None
         _LIB = L
     return _LIB
 
@@ -325,4 +336,37 @@ def gemm_int8(qa, sa, qb, sb, sample=None):
     Y = np.empty(mi.size, np.float64)
     lib().orc_gemm_int8_sampled(_p(A, _i8p), _p(sa, _f32p), _p(B, _i8p), _p(sb, _f32p), K,
                                 _p(mi, _i64p), _p(ni, _i64p), mi.size, _p(Y, _f64p))
+    return Y
+
+
+# ------------------------------------------------------------------ 4-bit weights
+
+def quant_nvfp4(w_bf16: np.ndarray):
+    """[n, k] bf16 weight (k % 16 == 0) -> (codes u8 [n, k/2], block scales u8 [n, k/16] (E4M3
+    codes), tensor scale float)."""
+    w = _c(w_bf16, np.uint16)
+    n, k = w.shape
+    codes = np.empty((n, k // 2), np.uint8)
+    bs = np.empty((n, k // 16), np.uint8)
+    t = np.zeros(1, np.float32)
+    if lib().orc_quant_nvfp4(_p(w, _u16p), n, k, k, _p(codes, _u8p), _p(bs, _u8p), _p(t, _f32p)):
+        raise ValueError("4-bit quantizer: non-finite input or k % 16 != 0")
+    return codes, bs, float(t[0])
+
+
+def gemm_w4a16(x_bf16, codes, bscale, t, sample=None):
+    """Y = t * X . dequant(W)^T in fp64; with sample=(mi, ni) only those positions."""
+    X = _c(x_bf16, np.uint16)
+    M, K = X.shape
+    C, B = _c(codes, np.uint8), _c(bscale, np.uint8)
+    N = C.shape[0]
+    if sample is None:
+        Y = np.empty((M, N), np.float64)
+        lib().orc_gemm_w4a16(_p(X, _u16p), _p(C, _u8p), _p(B, _u8p), float(t), M, N, K, None,
+                             None, 0, _p(Y, _f64p))
+        return Y
+    mi, ni = (_c(np.asarray(v), np.int64) for v in sample)
+    Y = np.empty(mi.size, np.float64)
+    lib().orc_gemm_w4a16(_p(X, _u16p), _p(C, _u8p), _p(B, _u8p), float(t), M, N, K,
+                         _p(mi, _i64p), _p(ni, _i64p), mi.size, _p(Y, _f64p))
     return Y

@@ -32,6 +32,11 @@
  *     gain' = RN32(gain * s).
  *   - The norm whose gain carries s (the QuRL notes fold s into it) is the standard RMSNorm,
  *     y = h * gain / sqrt(mean(h^2) + eps), evaluated in binary64 and rounded once to bf16.
+ *   - The 4-bit weight path (QeRL notes: NVFP4, 4-bit floats with two-level scaling, FP8 E4M3
+ *     block scales and an FP32 tensor scale): E2M1 elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+ *     signed), blocks of 16 consecutive elements along a weight row; t = RN32(amax / (448*6));
+ *     block scale code = E4M3(RN32(amax_b / RN32(6 t))); element code = E2M1(RN32(x / e)) with
+ *     e = RN32(block scale * t), nearest, ties to the even code, saturating at 6.
  *   - The INT8 variant (QuRL's experiment setup: channel-wise weights, token-wise
  *     activations) is symmetric: one scale per row, s = RN32(amax / 127); the code is the
  *     binary32 quotient RN32(x / s) rounded to the nearest integer (ties to even) and clamped
@@ -439,5 +444,99 @@ void orc_gemm_int8_sampled(const int8_t *A, const float *sa, const int8_t *B, co
         for (int64_t k = 0; k < K; ++k)
             acc += (int64_t)A[mi[t] * K + k] * (int64_t)B[ni[t] * K + k];
         Y[t] = (double)sa[mi[t]] * (double)sb[ni[t]] * (double)acc;
+    }
+}
+
+/* ---------------------------------------------------------------- 4-bit (NVFP4-style) weights */
+
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_decode(uint8_t c)
+{
+    double m = E2M1_MAG[c & 7];
+    return (c & 8) ? -m : m;
+}
+
+/* Nearest E2M1 magnitude, ties to the code with an even mantissa bit (even code), saturating
+ * at 6; the sign of v is kept (a negative v that rounds to 0 gives the code 8, -0). */
+uint8_t orc_e2m1_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    if (a >= 6.0)
+        return sign | 7;                          /* saturate (distances lose meaning far out) */
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        double dc = fabs(a - E2M1_MAG[c]), db = fabs(a - E2M1_MAG[best]);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+/* w [n, k] -> codes [n, k/2] (element 2j in the low nibble of byte j), block scales
+ * [n, k/16] (E4M3 codes), tensor scale *t.  k % 16 == 0.  Returns 0, or -1 on a non-finite
+ * input or a bad k. */
+int orc_quant_nvfp4(const uint16_t *w, int64_t n, int64_t k, int64_t ld, uint8_t *codes,
+                    uint8_t *bscale, float *t_out)
+{
+    if (k % 16 != 0 || !all_finite_bf16(w, n, k, ld))
+        return -1;
+    float amax = 0.0f;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t c = 0; c < k; ++c) {
+            float a = fabsf(orc_bf16_to_f32(w[r * ld + c]));
+            if (a > amax)
+                amax = a;
+        }
+    float t = amax / 2688.0f;
+    *t_out = t;
+    float u = 6.0f * t;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 16; ++b) {
+            float ab = 0.0f;
+            for (int64_t c = 16 * b; c < 16 * b + 16; ++c) {
+                float a = fabsf(orc_bf16_to_f32(w[r * ld + c]));
+                if (a > ab)
+                    ab = a;
+            }
+            uint8_t sb = t > 0.0f ? orc_e4m3_encode(ab / u) : 0;
+            bscale[r * (k / 16) + b] = sb;
+            float e = (float)orc_e4m3_decode(sb) * t;
+            for (int64_t c = 16 * b; c < 16 * b + 16; c += 2) {
+                uint8_t c0 = 0, c1 = 0;
+                float x0 = orc_bf16_to_f32(w[r * ld + c]), x1 = orc_bf16_to_f32(w[r * ld + c + 1]);
+                if (e != 0.0f) {
+                    c0 = orc_e2m1_encode(x0 / e);
+                    c1 = orc_e2m1_encode(x1 / e);
+                } else {
+                    c0 = signbit(x0) ? 8 : 0;
+                    c1 = signbit(x1) ? 8 : 0;
+                }
+                codes[r * (k / 2) + c / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    return 0;
+}
+
+/* Y[m, n] = t * sum_k X[m, k] * E2M1(code[n, k]) * E4M3(bscale[n, k/16]), in binary64 (X bf16
+ * [M, K]).  With mi/ni non-NULL only those count positions (Y[count]); else all of Y [M, N]. */
+void orc_gemm_w4a16(const uint16_t *X, const uint8_t *codes, const uint8_t *bscale, float t,
+                    int64_t M, int64_t N, int64_t K, const int64_t *mi, const int64_t *ni,
+                    int64_t count, double *Y)
+{
+    int64_t total = mi ? count : M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = mi ? mi[i] : i / N, n = ni ? ni[i] : i % N;
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) {
+            uint8_t byte = codes[n * (K / 2) + kk / 2];
+            uint8_t c = (kk & 1) ? (byte >> 4) : (byte & 15);
+            double w = orc_e2m1_decode(c) * orc_e4m3_decode(bscale[n * (K / 16) + kk / 16]);
+            acc += (double)orc_bf16_to_f32(X[m * K + kk]) * w;
+        }
+        Y[i] = acc * (double)t;
     }
 }

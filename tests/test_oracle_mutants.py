@@ -2,7 +2,8 @@
 the oracle source (a wrong rounding rule, a dropped saturation, a lost sign of zero, a
 transposed or shifted scale index, a wrong constant, a reciprocal in place of the division, a
 dropped absolute value, a double rounding, an off-by-one group, a wrong mean, a dropped eps
-or gain in the norm, INT8 ties away from zero, a wrong INT8 divisor or scale index) and runs the pin suite on that
+or gain in the norm, INT8 ties away from zero, a wrong INT8 divisor or scale index, an E2M1 tie to the odd code,
+a wrong FP4 tensor divisor, a dropped FP4 block scale) and runs the pin suite on that
 copy, which must fail.  CPU only: the copies live in a temporary directory and the HIP library
 is not involved."""
 import os
@@ -36,6 +37,11 @@ MUTANTS = {
     "int8_scale_128": ("float sc = amax / 127.0f;", "float sc = amax / 128.0f;"),
     "int8_gemm_scale_index": ("(double)sa[m] * (double)sb[n] * (double)acc",
                               "(double)sa[m] * (double)sb[m] * (double)acc"),
+    "e2m1_ties_odd": ("if (dc < db || (dc == db && (c & 1) == 0))",
+                      "if (dc < db || (dc == db && (c & 1) == 1))"),
+    "nvfp4_tensor_divisor": ("float t = amax / 2688.0f;", "float t = amax / 2048.0f;"),
+    "w4a16_no_block_scale": ("double w = orc_e2m1_decode(c) * orc_e4m3_decode(bscale[n * (K / 16) + kk / 16]);",
+                             "double w = orc_e2m1_decode(c);"),
     "column_group_short": ("int64_t r0 = g * GROUP, r1 = r0 + GROUP < rows ? r0 + GROUP : rows;",
                            "int64_t r0 = g * GROUP, r1 = r0 + GROUP - 1 < rows ? "
                            "r0 + GROUP - 1 : rows;"),

@@ -617,3 +617,102 @@ def test_int8_gemm_brute_force():
                 assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
         mi, ni = np.array([0, M - 1, 1]), np.array([N - 1, 0, 2])
         assert np.array_equal(oracle.gemm_int8(qa, sa, qb, sb, sample=(mi, ni)), Y[mi, ni])
+
+
+# ============================================================== 4-bit (NVFP4-style) weights
+
+E2M1_HAND = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]          # 1 sign, 2 exponent (bias 1), 1 mantissa
+
+
+def _e2m1_nearest(v: Fraction):
+    """Nearest E2M1 code by search, ties to the even code, saturating at 6 (sign kept)."""
+    sign = 8 if v < 0 else 0
+    a = abs(v)
+    best = min(range(8), key=lambda c: (abs(a - Fraction(E2M1_HAND[c])), c & 1))
+    return sign | best
+
+
+def test_e2m1_codec_hand_values_midpoints_and_saturation():
+    for c in range(16):
+        v = E2M1_HAND[c & 7] * (-1 if c & 8 else 1)
+        assert oracle.lib().orc_e2m1_decode(c) == v
+        if c != 8:
+            assert oracle.lib().orc_e2m1_encode(v) == c              # round trip
+    assert oracle.lib().orc_e2m1_encode(-0.0) == 8                   # sign of zero kept
+    mids = [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6)]
+    for m, code in mids:                                              # ties to the even code
+        assert oracle.lib().orc_e2m1_encode(m) == code, m
+        assert oracle.lib().orc_e2m1_encode(-m) == 8 | code
+        assert oracle.lib().orc_e2m1_encode(np.nextafter(np.float32(m), np.float32(9))) == \
+            _e2m1_nearest(Fraction(float(np.nextafter(np.float32(m), np.float32(9)))))
+        assert oracle.lib().orc_e2m1_encode(np.nextafter(np.float32(m), np.float32(0))) == \
+            _e2m1_nearest(Fraction(float(np.nextafter(np.float32(m), np.float32(0)))))
+    for v in (6.0, 6.5, 100.0, 3.0e38):                              # saturation
+        assert oracle.lib().orc_e2m1_encode(v) == 7 and oracle.lib().orc_e2m1_encode(-v) == 15
+
+
+def test_nvfp4_quantizer_matches_exact_rationals():
+    """t = RN32(amax / 2688), u = RN32(6 t), block scale = E4M3(RN32(amax_b / u)),
+    e = RN32(dq(scale) t), code = E2M1(RN32(x / e)), all decided in rationals with searches."""
+    for seed, std in ((91, 0.02), (93, 1.0), (95, 3e-3)):
+        w = qr_synth.normal_bf16(seed, (6, 64), std, seed + 1, 2)
+        codes, bs, t = oracle.quant_nvfp4(w)
+        wf = bf16_f32(w)
+        amax = max(abs(Fraction(float(v))) for v in wf.ravel())
+        tr = rn32(amax / 2688)
+        assert Fraction(t) == tr
+        u = rn32(6 * tr)
+        vals = e4m3_values_torch()
+        for r in range(6):
+            for b in range(4):
+                blk = [Fraction(float(v)) for v in wf[r, 16 * b:16 * b + 16]]
+                sb = e4m3_nearest(float(rn32(max(abs(v) for v in blk) / u)))
+                assert int(bs[r, b]) == sb
+                e = rn32(Fraction(float(vals[sb])) * tr)
+                for j, v in enumerate(blk):
+                    c = 16 * b + j
+                    got = (int(codes[r, c // 2]) >> (4 * (c & 1))) & 15
+                    want = _e2m1_nearest(rn32(v / e)) if e != 0 else (8 if v < 0 else 0)
+                    if v == 0:
+                        want = 8 if np.signbit(wf[r, c]) else 0
+                    assert got == want, (seed, r, c)
+
+
+def test_nvfp4_amax_element_zero_weight_and_power_of_two():
+    w = qr_synth.normal_bf16(97, (8, 128), 0.02)
+    codes, bs, t = oracle.quant_nvfp4(w)
+    wf = bf16_f32(w)
+    r, c = np.unravel_index(np.argmax(np.abs(wf)), wf.shape)
+    assert bs[r, c // 16] == 0x7E                                     # block scale 448
+    assert (int(codes[r, c // 2]) >> (4 * (c & 1))) & 7 == 7          # code +-6
+    z = np.zeros((4, 32), np.uint16)
+    z[1, 3] = 0x8000
+    cz, bz, tz = oracle.quant_nvfp4(z)
+    assert tz == 0 and not bz.any()
+    assert ((cz[1, 1] >> 4) & 15) == 8 and (cz & 0x77).sum() == 0     # signed zeros only
+    w2 = qr_synth.f32_to_bf16_bits(wf * np.float32(2.0 ** 30))
+    c2, b2, t2 = oracle.quant_nvfp4(w2)
+    assert np.array_equal(c2, codes) and np.array_equal(b2, bs) and t2 == t * 2.0 ** 30
+
+
+def test_w4a16_gemm_brute_force():
+    rng = np.random.default_rng(99)
+    w = qr_synth.normal_bf16(100, (5, 96), 0.02)
+    x = qr_synth.normal_bf16(101, (3, 96), 1.0)
+    codes, bs, t = oracle.quant_nvfp4(w)
+    Y = oracle.gemm_w4a16(x, codes, bs, t)
+    vals = e4m3_values_torch()
+    xf = bf16_f32(x)
+    for m in range(3):
+        for n in range(5):
+            acc = Fraction(0)
+            for k in range(96):
+                code = (int(codes[n, k // 2]) >> (4 * (k & 1))) & 15
+                wv = Fraction(E2M1_HAND[code & 7]) * (-1 if code & 8 else 1) * \
+                    Fraction(float(vals[bs[n, k // 16]]))
+                acc += Fraction(float(xf[m, k])) * wv
+            exact = acc * Fraction(t)
+            assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 48) + \
+                Fraction(1, 2 ** 120)
+    mi, ni = np.array([0, 2, 1]), np.array([4, 0, 3])
+    assert np.array_equal(oracle.gemm_w4a16(x, codes, bs, t, sample=(mi, ni)), Y[mi, ni])
