@@ -24,10 +24,11 @@ QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD = 0, 1, 2
 # Every entry point include/qr.h declares.
 EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant_w_128x128",
            "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_quant_int8_rowwise",
-           "qr_gemm_int8_w8a8", "qr_gemm_fp8_bsfprop",
+           "qr_gemm_int8_w8a8", "qr_quant_w_nvfp4", "qr_gemm_w4a16", "qr_gemm_fp8_bsfprop",
            "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes",
            "qr_uaq_fold")
 QR_MAX_WEIGHT_BATCH = 4096
+QR_NVFP4_WORKSPACE_BYTES = 4096
 
 
 class qr_weight_desc(ctypes.Structure):
@@ -71,6 +72,10 @@ def load():
     L.qr_quant_int8_rowwise.restype = I32
     L.qr_gemm_int8_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
     L.qr_gemm_int8_w8a8.restype = I32
+    L.qr_quant_w_nvfp4.argtypes = [P, I64, I64, I64, P, P, P, P, SZ, P]
+    L.qr_quant_w_nvfp4.restype = I32
+    L.qr_gemm_w4a16.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+    L.qr_gemm_w4a16.restype = I32
     for name in ("qr_gemm_fp8_bsfprop", "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad"):
         f = getattr(L, name)
         f.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
@@ -153,6 +158,16 @@ def qr_quant_int8_rowwise(x, rows, cols, ld_x, q, s, stream=None):
 def qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, y_dtype, stream=None):
     _check(load().qr_gemm_int8_w8a8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(y),
                                     int(y_dtype), _stream(stream)), "qr_gemm_int8_w8a8")
+
+
+def qr_quant_w_nvfp4(w, n, k, ld_w, codes, bscale, tscale, ws, ws_bytes, stream=None):
+    _check(load().qr_quant_w_nvfp4(_ptr(w), n, k, ld_w, _ptr(codes), _ptr(bscale), _ptr(tscale),
+                                   _ptr(ws), int(ws_bytes), _stream(stream)), "qr_quant_w_nvfp4")
+
+
+def qr_gemm_w4a16(x, codes, bscale, tscale, M, N, K, y, y_dtype, stream=None):
+    _check(load().qr_gemm_w4a16(_ptr(x), _ptr(codes), _ptr(bscale), _ptr(tscale), M, N, K,
+                                _ptr(y), int(y_dtype), _stream(stream)), "qr_gemm_w4a16")
 
 
 def _gemm(name, a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream):
@@ -271,6 +286,29 @@ def gemm_int8(a, sa, b, sb, out_dtype=QR_OUT_BF16, stream=None):
     N = b.shape[0]
     y = _out(M, N, out_dtype, a.device)
     qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, out_dtype, stream)
+    return y
+
+
+def quant_nvfp4(w, stream=None):
+    """w: bf16 [n, k] on the GPU -> (codes u8 [n, k/2], block scales u8 [n, k/16], tensor scale
+    fp32 [1])."""
+    import torch
+    n, k = w.shape
+    dev = w.device
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    bs = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+    t = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(QR_NVFP4_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    qr_quant_w_nvfp4(w, n, k, w.stride(0), codes, bs, t, ws, QR_NVFP4_WORKSPACE_BYTES, stream)
+    return codes, bs, t
+
+
+def gemm_w4a16(x, codes, bscale, tscale, out_dtype=QR_OUT_BF16, stream=None):
+    """x bf16 [M, K]; the 4-bit weight [N, K] -> y [M, N]."""
+    M, K = x.shape
+    N = codes.shape[0]
+    y = _out(M, N, out_dtype, x.device)
+    qr_gemm_w4a16(x, codes, bscale, tscale, M, N, K, y, out_dtype, stream)
     return y
 
 

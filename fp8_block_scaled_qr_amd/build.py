@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqr.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "fp4.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall",
           # packed fp32 VALU ops stay off (plain fp32 code only)

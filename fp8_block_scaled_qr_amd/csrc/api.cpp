@@ -266,6 +266,68 @@ qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, c
                                             (hipStream_t)stream));
 }
 
+qr_status qr_quant_w_nvfp4(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *codes,
+                           uint8_t *bscale, float *tscale, void *workspace,
+                           size_t workspace_bytes, qr_stream stream)
+{
+    if (n < 0 || k < 0 || n >= kMaxDim || k >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (k % 32 != 0 || ld_w % 8 != 0 || (n > 0 && ld_w < k) || ld_w >= kMaxLd)
+        return QR_ERR_SHAPE;
+    if (n == 0 || k == 0)
+        return QR_OK;
+    if (!w_bf16 || !codes || !bscale || !tscale || !workspace)
+        return QR_ERR_NULL;
+    if (workspace_bytes < QR_NVFP4_WORKSPACE_BYTES)
+        return QR_ERR_WORKSPACE;
+    if (misaligned(w_bf16, 16) || misaligned(codes, 16) || misaligned(tscale, 4) ||
+        misaligned(workspace, 4))
+        return QR_ERR_ALIGN;
+    const Range ins[1] = {span(w_bf16, strided_bytes(n, k, ld_w, 2))};
+    const Range outs[4] = {span(codes, n * k / 2), span(bscale, n * (k / 16)), span(tscale, 4),
+                           span(workspace, QR_NVFP4_WORKSPACE_BYTES)};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], ins[0]))
+            return QR_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j]))
+                return QR_ERR_ALIAS;
+    }
+    return launch_status(qr::launch_quant_nvfp4(static_cast<const uint16_t *>(w_bf16), n, k, ld_w,
+                                                codes, bscale, tscale,
+                                                static_cast<uint32_t *>(workspace),
+                                                (hipStream_t)stream));
+}
+
+qr_status qr_gemm_w4a16(const void *x_bf16, const uint8_t *codes, const uint8_t *bscale,
+                        const float *tscale, int64_t M, int64_t N, int64_t K, void *y,
+                        qr_out_dtype y_dtype, qr_stream stream)
+{
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if (K % 128 != 0 || cdiv(M, 64) > 65535)
+        return QR_ERR_SHAPE;
+    if (y_dtype != QR_OUT_F32 && y_dtype != QR_OUT_BF16)
+        return QR_ERR_ARG;
+    if (M == 0 || N == 0)
+        return QR_OK;
+    if (!x_bf16 || !codes || !bscale || !tscale || !y)
+        return QR_ERR_NULL;
+    if (misaligned(x_bf16, 16) || misaligned(codes, 16) || misaligned(bscale, 2) ||
+        misaligned(tscale, 4) || misaligned(y, 16))
+        return QR_ERR_ALIGN;
+    const int64_t esz = y_dtype == QR_OUT_BF16 ? 2 : 4;
+    const Range ry = span(y, M * N * esz);
+    const Range ins[4] = {span(x_bf16, M * K * 2), span(codes, N * K / 2), span(bscale, N * (K / 16)),
+                          span(tscale, 4)};
+    for (const Range &r : ins)
+        if (overlap(ry, r))
+            return QR_ERR_ALIAS;
+    return launch_status(qr::launch_gemm_w4a16(y_dtype == QR_OUT_BF16,
+                                               static_cast<const uint16_t *>(x_bf16), codes,
+                                               bscale, tscale, M, N, K, y, (hipStream_t)stream));
+}
+
 qr_status qr_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *q,
                              float *s, uint8_t *qT, float *sT, qr_stream stream)
 {

@@ -60,6 +60,17 @@ hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const
                           const float *sb, int64_t M, int64_t N, int64_t K, void *C,
                           hipStream_t stream);
 
+// 4-bit weights: w [n, k] (ld) -> codes [n, k/2], E4M3 block scales [n, k/16], tensor scale;
+// partial: kNvfp4Partials words of scratch (the first pass's maxima).
+constexpr int kNvfp4Partials = 1024;
+hipError_t launch_quant_nvfp4(const uint16_t *w, int64_t n, int64_t k, int64_t ld, uint8_t *codes,
+                              uint8_t *bscale, float *tscale, uint32_t *partial,
+                              hipStream_t stream);
+// Y [M, N] = t * X [M, K] . dequant(W)^T, X bf16 dense, K % 128 == 0.
+hipError_t launch_gemm_w4a16(bool out_bf16, const uint16_t *X, const uint8_t *codes,
+                             const uint8_t *bscale, const float *tscale, int64_t M, int64_t N,
+                             int64_t K, void *Y, hipStream_t stream);
+
 // One symmetric INT8 scale per row: s [rows], q [rows, cols].
 hipError_t launch_quant_int8_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
                                   int8_t *q, float *s, hipStream_t stream);

@@ -17,6 +17,9 @@
  *          between operators in BF16 and are quantized only inside the kernels.  Section
  *          "system implementation": weights are quantized to FP8 in the parameter-update
  *          phase.
+ *   [QERL] "QeRL: Beyond Efficiency -- Quantization-enhanced Reinforcement Learning for LLMs"
+ *          paper notes (abstract and key takeaways): the rollout runs on NVFP4 weights, a 4-bit
+ *          float format with two-level scaling (FP8 E4M3 block scales and an FP32 tensor scale).
  *   [QURL] "QuRL: Efficient Reinforcement Learning with Quantized Rollout" (ICLR 2026) paper
  *          notes, section "key design 1: update-aware quantization (UAQ)": WX = (W/s)(sX) with
  *          s > 1 applied per column of W and per row of the preceding activation, folded into
@@ -101,6 +104,40 @@ int32_t qr_abi_version(void);
 qr_status qr_quant_act_1x128(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t *q_row, float *s_row, uint8_t *q_colT, float *s_colT,
                              qr_stream stream);
+
+/*
+ * 4-bit weights [QERL: QeRL notes, NVFP4 -- 4-bit floats with two-level scaling, FP8 E4M3 block
+ * scales and an FP32 tensor scale -- for the rollout's weights].  Readings (the notes give no
+ * formula): blocks of 16 consecutive elements along a weight row, and
+ *   t = RN32(amax / 2688)                                  (the tensor scale; 2688 = 448 * 6)
+ *   bscale[r, b] = E4M3(RN32(amax_b / RN32(6 t)))          (nearest even, saturating)
+ *   code = E2M1(RN32(x / RN32(dq(bscale) * t)))            (nearest of 0, .5, 1, 1.5, 2, 3, 4, 6,
+ *                                                           ties to even, saturating, signed)
+ * A block whose scale encodes to 0 (and an all-zero weight, t == 0) gets signed-zero codes.
+ *   w       bf16 [n, k], leading dimension ld_w.
+ *   codes   [n, k/2] bytes: element 2j of a row in the low nibble of byte j.
+ *   bscale  [n, k/16] E4M3 codes;  tscale: one fp32 (device).
+ *   workspace: device scratch of at least QR_NVFP4_WORKSPACE_BYTES; contents do not matter.
+ * Size rules: n, k >= 0; k % 32 == 0, ld_w % 8 == 0, ld_w < 2^22.  w and codes 16-byte
+ * aligned; no output or the workspace may overlap the input or each other.
+ */
+#define QR_NVFP4_WORKSPACE_BYTES 4096
+qr_status qr_quant_w_nvfp4(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *codes,
+                           uint8_t *bscale, float *tscale, void *workspace,
+                           size_t workspace_bytes, qr_stream stream);
+
+/*
+ * GEMM of bf16 activations with 4-bit weights (the rollout's decode):
+ *   y[m, n] = t * sum_k x[m, k] * E2M1(codes[n, k]) * E4M3(bscale[n, k/16])
+ * with the products of x and the dequantized weight (both exact in bf16) accumulated in fp32.
+ *   x  bf16 [M, K] dense;  codes / bscale / tscale from qr_quant_w_nvfp4 of W [N, K];
+ *   y  [M, N], fp32 or bf16 per y_dtype.
+ * Size rules: M, N >= 0, M <= 64 * 65535; K % 128 == 0.  x, codes and y 16-byte aligned, bscale
+ * 2-byte aligned.
+ */
+qr_status qr_gemm_w4a16(const void *x_bf16, const uint8_t *codes, const uint8_t *bscale,
+                        const float *tscale, int64_t M, int64_t N, int64_t K, void *y,
+                        qr_out_dtype y_dtype, qr_stream stream);
 
 /*
  * INT8 W8A8 variant [QURL, experiment setup: channel-wise weight quantization and token-wise

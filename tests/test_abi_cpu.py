@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 15, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -123,6 +123,27 @@ def test_int8_validation(L):
     assert g(A, B, C + 4, D, 64, 64, 128, E, 1, None) == ALIGN
     assert g(A, B, C, D, 64, 64, 128, A + 1024, 1, None) == ALIAS        # y over a
     assert g(A, B, C, D, 0, 64, 128, E, 1, None) == OK
+
+
+def test_fp4_validation(L):
+    f = L.qr_quant_w_nvfp4
+    WS = qr.QR_NVFP4_WORKSPACE_BYTES
+    assert f(A, 128, 48, 48, B, C, D, E, WS, None) == SHAPE             # k % 32
+    assert f(A, 128, 128, 120, B, C, D, E, WS, None) == SHAPE           # ld < k
+    assert f(A, 128, 128, 128, None, C, D, E, WS, None) == NULL
+    assert f(A, 128, 128, 128, B, C, D, None, WS, None) == NULL         # workspace required
+    assert f(A, 128, 128, 128, B, C, D, E, WS - 4, None) == WORKSPACE
+    assert f(A + 2, 128, 128, 128, B, C, D, E, WS, None) == ALIGN
+    assert f(A, 128, 128, 128, A + 64, C, D, E, WS, None) == ALIAS      # codes over w
+    assert f(A, 128, 128, 128, B, C, D, C + 4, WS, None) == ALIAS       # workspace over scales
+    assert f(A, 0, 128, 128, B, C, D, E, WS, None) == OK
+    g = L.qr_gemm_w4a16
+    assert g(A, B, C, D, 64, 64, 96, E, 1, None) == SHAPE               # K % 128
+    assert g(A, B, C, D, 64, 64, 128, E, 5, None) == ARG
+    assert g(A, None, C, D, 64, 64, 128, E, 1, None) == NULL
+    assert g(A, B, C + 1, D, 64, 64, 128, E, 1, None) == ALIGN          # bscale 2-byte
+    assert g(A, B, C, D, 64, 64, 128, B + 64, 1, None) == ALIAS         # y over codes
+    assert g(A, B, C, D, 64, 0, 128, E, 1, None) == OK
 
 
 def batch(L, descs):

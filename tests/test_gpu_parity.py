@@ -225,6 +225,80 @@ def test_gemm_int8_full_size_sampled(M, N, K):
     _check_int8(y[mi, ni], Y, qr.QR_OUT_BF16)
 
 
+FP4_W = [(64, 128), (200, 96), (1, 32), (4096, 4096), (14336, 4096)]
+
+
+@pytest.mark.parametrize("n,k", FP4_W)
+def test_quant_nvfp4(n, k):
+    """4-bit weights: codes, block scales and the tensor scale bit-exact, including an all-zero
+    row, a block far below the tensor's amax (its scale encodes to 0: signed-zero codes), one with
+    a subnormal block scale and the amax element (scale 448, code 6)."""
+    say("quant_nvfp4", n, k)
+    w = qr_synth.normal_bf16(n * 3 + k, (n, k), 0.02)
+    if n > 2:
+        w[1] = 0
+        w[2, :16] = qr_synth.f32_to_bf16_bits(np.full(16, -1e-12, np.float32))
+        # a block whose E4M3 scale is subnormal (about 0.0068 of the tensor unit)
+        w[2, 16:32] = qr_synth.f32_to_bf16_bits(
+            np.linspace(-7.6e-6, 7.6e-6, 16).astype(np.float32))
+        w[0, 5] = qr_synth.f32_to_bf16_bits(np.array([0.5], np.float32))[0]
+    codes, bs, t = qr.quant_nvfp4(dev_bf16(w))
+    rc, rb, rt = oracle.quant_nvfp4(w)
+    assert_bitexact(host(bs), rb, "block scales")
+    assert_bitexact(host(codes), rc, "codes")
+    assert_bitexact(host(t), np.array([rt], np.float32), "tensor scale")
+
+
+def test_quant_nvfp4_strided_and_zero():
+    say("quant_nvfp4 strided, zero")
+    big = qr_synth.normal_bf16(13, (96, 640), 0.02)
+    codes, bs, t = qr.quant_nvfp4(dev_bf16(big)[:, 64:448])      # ld 640, k 384
+    rc, rb, rt = oracle.quant_nvfp4(np.ascontiguousarray(big[:, 64:448]))
+    assert_bitexact(host(codes), rc, "codes")
+    assert_bitexact(host(bs), rb, "block scales")
+    z = np.zeros((8, 64), np.uint16)
+    z[3, 7] = 0x8000
+    codes, bs, t = qr.quant_nvfp4(dev_bf16(z))
+    rc, rb, rt = oracle.quant_nvfp4(z)
+    assert_bitexact(host(codes), rc, "zero codes")
+    assert host(t)[0] == 0.0 and not host(bs).any()
+
+
+def _check_w4a16(y, Y, S):
+    """fp32 accumulation of K exact products: |y - Y| <= K 2^-23 sum |x w| t, plus the output
+    rounding (bf16: 2^-8 |Y|)."""
+    err = np.abs(y - Y)
+    assert np.all(err <= S + 2.0 ** -8 * np.abs(Y) + 1e-30), float(np.max(err / (S + 1e-30)))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 1000, 1024), (17, 72, 640), (1, 128, 128),
+                                   (100, 264, 256), (200, 520, 384)])
+def test_gemm_w4a16(M, N, K):
+    say("gemm_w4a16", M, N, K)
+    x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 3, max(1, K // 100))
+    w = qr_synth.normal_bf16(M * N + K, (N, K), 0.02)
+    codes, bs, t = qr.quant_nvfp4(dev_bf16(w))
+    hc, hb, ht = host(codes), host(bs), float(host(t)[0])
+    y = out_f64(qr.gemm_w4a16(dev_bf16(x), codes, bs, t, out_dtype=qr.QR_OUT_F32))
+    Y = oracle.gemm_w4a16(x, hc, hb, ht)
+    absw = oracle.gemm_w4a16(x & np.uint16(0x7FFF), hc & np.uint8(0x77), hb, ht)  # sum |x w| t
+    _check_w4a16(y, Y, K * 2.0 ** -23 * np.abs(absw))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 14336, 4096), (256, 5120, 27648)])
+def test_gemm_w4a16_full_size_sampled(M, N, K):
+    say("gemm_w4a16 full", M, N, K)
+    x = qr_synth.normal_bf16(M + 7, (M, K), 1.0, 9, max(1, K // 100))
+    w = qr_synth.normal_bf16(N + 11, (N, K), 0.02)
+    codes, bs, t = qr.quant_nvfp4(dev_bf16(w))
+    hc, hb, ht = host(codes), host(bs), float(host(t)[0])
+    y = out_f64(qr.gemm_w4a16(dev_bf16(x), codes, bs, t, out_dtype=qr.QR_OUT_BF16))
+    mi, ni = sample_positions(M, N, 2048, seed=M + N)
+    Y = oracle.gemm_w4a16(x, hc, hb, ht, sample=(mi, ni))
+    absw = oracle.gemm_w4a16(x & np.uint16(0x7FFF), hc & np.uint8(0x77), hb, ht, sample=(mi, ni))
+    _check_w4a16(y[mi, ni], Y, K * 2.0 ** -23 * np.abs(absw))
+
+
 def test_quant_strided_input():
     say("quant strided ld")
     big = qr_synth.normal_bf16(11, (96, 640), 1.0)
