@@ -305,7 +305,7 @@ qr_status qr_gemm_w4a16(const void *x_bf16, const uint8_t *codes, const uint8_t 
 {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
         return QR_ERR_SHAPE;
-    if (K % 128 != 0 || cdiv(M, 64) > 65535)
+    if (K % 128 != 0 || cdiv(M, 16) > 65535 || (M + 64) * K * 2 > (int64_t)UINT32_MAX)
         return QR_ERR_SHAPE;
     if (y_dtype != QR_OUT_F32 && y_dtype != QR_OUT_BF16)
         return QR_ERR_ARG;

@@ -24,7 +24,21 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int kAmaxGrid = kNvfp4Partials;   // partial maxima (one per workgroup of the first pass)
+constexpr int kAmaxGrid = kNvfp4Partials;
+
+// load depth of the 4-bit GEMM (steps ahead) for 16, 32 and 64 rows of X per workgroup
+#ifndef QR_W4_D1
+#define QR_W4_D1 3
+#endif
+#ifndef QR_W4_D2
+#define QR_W4_D2 2
+#endif
+#ifndef QR_W4_D4
+#define QR_W4_D4 2
+#endif
+#ifndef QR_W4_M2   // largest M run as 32-row tiles; larger M takes 64-row tiles
+#define QR_W4_M2 32
+#endif   // partial maxima (one per workgroup of the first pass)
 
 __device__ __forceinline__ uint32_t absmax8_16(const uint4 &v)
 {
@@ -134,111 +148,160 @@ __device__ __forceinline__ v8bf dequant8(uint32_t codes8, float sc)
                                                dequant2<2>(codes8, sc), dequant2<3>(codes8, sc)));
 }
 
-// Y[m, n] = t * sum_k X[m, k] * W[n, k], X bf16 [M, K], W in 4-bit codes.  A workgroup owns 64
-// rows of W (4 waves x 16) and 64 rows of X (grid y); a K step is 128.
-//   X: the step's 64 x 128 tile (16 KB) is staged in LDS (two buffers, register staging); row
-//      r's 16-byte chunk c sits in slot c ^ (r % 16).
-//   W: lane (n = l % 16, q = l / 16) loads the 32 codes of K range [32 q, 32 q + 32) of its row
-//      (16 bytes) and their 2 block scales, one step ahead.
-// MFMA s (0..3) of a step covers K offsets 32 q + 8 s .. + 7 in lane group q, for both
-// operands; four 16x16x32 bf16 MFMAs per 16-row block of X.
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void k_gemm_w4a16(const uint16_t *__restrict__ X,
-                                                    const uint8_t *__restrict__ codes,
-                                                    const uint8_t *__restrict__ bscale,
-                                                    const float *__restrict__ tscale, int64_t M,
-                                                    int64_t N, int64_t K, void *__restrict__ Y)
+// Y[m, n] = t * sum_k X[m, k] * W[n, k], X bf16 [M, K], W in 4-bit codes.  Decode-shaped: the
+// weight bytes dominate, so the kernel is built to keep many of them in flight.
+//   Workgroup: 64 rows of W (4 blocks of 16) x 16 MB rows of X (grid y).  Its 4 waves split K:
+//   wave w takes the 128-wide K steps s = w, w + 4, ... (the waves of a workgroup read adjacent
+//   code bytes), and each holds partial sums for the whole 64 x 16 MB tile; the partials are
+//   summed through LDS once, at the end.
+//   W codes: lane (l % 16, q = l / 16) loads, per block of 16 rows, the 32 codes of K range
+//   [32 q, 32 q + 32) of its row (16 bytes) into registers.
+//   W block scales: the step's 8 scale bytes of each of the 64 rows go to a per-wave LDS ring
+//   by two direct-to-LDS dword loads (lane = row); each lane reads back its 2 bytes per block.
+//   X: the lane's K range of its row of X (4 x 16 bytes per block of 16 rows) goes to the same
+//   ring by direct-to-LDS loads, and each fragment read back serves the 4 W blocks.
+//   All three run D steps ahead, refilled together at the end of each step: loads retire in
+//   order, so a stream kept shallower than another would cap the other's depth at its own.
+//   The ring's wait is explicit (vm_wait); the compiler's own, for the code registers, counts
+//   only its loads and so waits somewhat longer than needed.
+// MFMA t (0..3) of a step covers K offsets 32 q + 8 t .. + 7 in lane group q for both operands.
+// Out-of-range W rows: their codes are read from the last row and their block scales read 0
+// (buffer extent), as do X rows past M; steps past a wave's last one reload that step (unused).
+template <int MB, int D, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const uint16_t *__restrict__ X,
+                                                       const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ bscale,
+                                                       const float *__restrict__ tscale,
+                                                       int64_t M, int64_t N, int64_t K,
+                                                       void *__restrict__ Y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][64 * 256];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int XBYTES = MB * 4 * 64 * 16;  // X per wave and step
+    constexpr int SLOT = XBYTES + 2 * 64 * 4; // + the 64 rows' 8 scale bytes
+    constexpr int NLOAD = 4 + 2 + 4 * MB;     // loads per wave and step: codes, scales, X
+    static_assert((D - 1) * NLOAD < 64, "vmcnt range");
+    static_assert(4 * D * SLOT >= 4 * 4 * MB * 64 * 16, "the partials fit in the ring");
+    __shared__ __attribute__((aligned(16))) uint8_t xring[4][D][SLOT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lq = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 64, m0 = (int64_t)blockIdx.y * 64;
-    const int64_t nrow = n0 + 16 * wave + ln;
-    const bool nok = nrow < N;
+    const int64_t n0 = (int64_t)blockIdx.x * 64, m0 = (int64_t)blockIdx.y * (16 * MB);
     const int64_t steps = K / 128;
+    const int64_t mine = steps > wave ? (steps - wave + 3) / 4 : 0;
 
-    // X staging: thread tid takes row tid / 4, chunks 4 (tid % 4) .. + 3 of the 16 in a row
-    const int xr = tid >> 2, xc0 = 4 * (tid & 3);
-    const bool xok = m0 + xr < M;
-    const uint16_t *xsrc = X + (m0 + xr) * K + 8 * xc0;
-    auto xload = [&](int64_t s, uint4 (&v)[4]) {
+    const uint8_t *wrow[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = xok ? *reinterpret_cast<const uint4 *>(xsrc + 128 * s + 8 * j)
-                       : make_uint4(0, 0, 0, 0);
-    };
-    auto xstore = [&](int buf, const uint4 (&v)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<uint4 *>(&xs[buf][xr * 256 + (((xc0 + j) ^ (xr & 15)) << 4)]) = v[j];
-    };
-    const uint8_t *wsrc = codes + nrow * (K / 2) + 16 * lq;
-    const uint8_t *ssrc = bscale + nrow * (K / 16) + 2 * lq;
-    auto wload = [&](int64_t s, uint4 &c, uint32_t &sc2) {
-        if (nok) {
-            c = *reinterpret_cast<const uint4 *>(wsrc + 64 * s);
-            sc2 = *reinterpret_cast<const uint16_t *>(ssrc + 8 * s);
-        } else {
-            c = make_uint4(0, 0, 0, 0);
-            sc2 = 0;
-        }
-    };
-
-    v4f acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    uint4 xv[4], wc, wcn;
-    uint32_t ws2 = 0, wsn = 0;
-    if (steps > 0) {
-        xload(0, xv);
-        xstore(0, xv);
-        wload(0, wc, ws2);
+    for (int nb = 0; nb < 4; ++nb) {
+        const int64_t n = n0 + 16 * nb + ln;
+        wrow[nb] = codes + (n < N ? n : N - 1) * (K / 2) + 16 * lq;
     }
-    __syncthreads();
-    for (int64_t s = 0; s < steps; ++s) {
-        const int buf = (int)(s & 1);
-        const bool more = s + 1 < steps;
-        if (more) {
-            xload(s + 1, xv);
-            wload(s + 1, wcn, wsn);
-        }
-        const float sc0 = __builtin_amdgcn_cvt_f32_fp8((int)(ws2 & 0xFFu), 0);
-        const float sc1 = __builtin_amdgcn_cvt_f32_fp8((int)(ws2 >> 8), 0);
-        const v8bf wf[4] = {dequant8(wc.x, sc0), dequant8(wc.y, sc0), dequant8(wc.z, sc1),
-                            dequant8(wc.w, sc1)};
+    // the workgroup's block scales, rows n0 .. N - 1 (rows past N read zeros)
+    const int64_t kb = K / 16;
+    const v4i_sgpr rs = make_rsrc_sgpr(bscale + n0 * kb, (uint32_t)((N - n0 < 64 ? N - n0 : 64) * kb));
+    const uint32_t soff = (uint32_t)(lane * kb);   // + 8 s + 4 h
+    // X through a buffer descriptor over rows m0 .. M - 1: rows past M read zeros
+    const v4i_sgpr rx = make_rsrc_sgpr(X + m0 * K, (uint32_t)((M - m0) * K * 2));
+    const uint32_t xoff = (uint32_t)((ln * K + 32 * lq) * 2);   // + (16 mb K + 128 s + 8 t) 2
+    const uint32_t ring = lds_addr_of(&xring[wave][0][0]);
+
+    auto step_of = [&](int64_t i) { return wave + 4 * (i < mine ? i : mine - 1); };
+    auto refill = [&](int64_t i, int slot, uint4 (&c)[4]) {
+        const int64_t s = step_of(i);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int row = 16 * mb + ln;
+        for (int nb = 0; nb < 4; ++nb)
+            c[nb] = *reinterpret_cast<const uint4 *>(wrow[nb] + 64 * s);
+        // the slot's previous contents are read (their LDS reads returned) before refilling
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const v8bf xf = *reinterpret_cast<const v8bf *>(
-                    &xs[buf][row * 256 + (((4 * lq + t) ^ (row & 15)) << 4)]);
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[t], xf, acc[mb], 0, 0, 0);
+        for (int h = 0; h < 2; ++h)
+            dma4(rs, ring + (uint32_t)(slot * SLOT + XBYTES + 256 * h), soff + (uint32_t)(8 * s + 4 * h));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                dma16(rx, ring + (uint32_t)(slot * SLOT + (mb * 4 + t) * 1024),
+                      xoff + (uint32_t)((16 * mb * K + 128 * s + 8 * t) * 2));
+    };
+
+    v4f acc[4][MB];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            acc[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Every load is issued on every path (clamped past the end), so the number of loads issued
+    // after a step's X is always (D - 1) NLOAD when the step waits for it.
+    if (mine > 0) {
+        uint4 cw[D][4];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            refill(j, j, cw[j]);
+        for (int64_t i0 = 0; i0 < mine; i0 += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const int64_t i = i0 + j;
+                if (i < mine) {
+                    vm_wait<(D - 1) * NLOAD>();
+                    const uint8_t *xs = &xring[wave][j][0];
+                    float sc[4][2];
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
+                        // row 16 nb + l % 16, scale bytes 2 q, 2 q + 1 of the step
+                        const uint32_t b2 = *reinterpret_cast<const uint16_t *>(
+                            xs + XBYTES + 256 * (lq >> 1) + 4 * (16 * nb + ln) + 2 * (lq & 1));
+                        sc[nb][0] = __builtin_amdgcn_cvt_f32_fp8((int)(b2 & 0xFFu), 0);
+                        sc[nb][1] = __builtin_amdgcn_cvt_f32_fp8((int)(b2 >> 8), 0);
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        v8bf wf[4];
+#pragma unroll
+                        for (int nb = 0; nb < 4; ++nb) {
+                            const uint32_t c8 = t == 0 ? cw[j][nb].x : t == 1 ? cw[j][nb].y
+                                              : t == 2 ? cw[j][nb].z : cw[j][nb].w;
+                            wf[nb] = dequant8(c8, sc[nb][t >> 1]);
+                        }
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const v8bf xf = *reinterpret_cast<const v8bf *>(
+                                xs + (mb * 4 + t) * 1024 + 16 * lane);
+#pragma unroll
+                            for (int nb = 0; nb < 4; ++nb)
+                                acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    wf[nb], xf, acc[nb][mb], 0, 0, 0);
+                        }
+                    }
+                }
+                refill(i + D, j, cw[j]);
             }
         }
-        if (more) {
-            xstore(buf ^ 1, xv);   // read last in step s - 1, before the barrier that ended it
-            wc = wcn;
-            ws2 = wsn;
-        }
-        __syncthreads();
     }
+    vm_wait<0>();   // the ring's last refills land before the ring is reused below
+    __syncthreads();
 
-    // epilogue: lane holds Y[m = row l % 16 of block mb][n .. n + 3]
-    const float t = *tscale;
-    const int64_t n = n0 + 16 * wave + 4 * lq;
-    const bool vec_ok = (N & 3) == 0 && n + 3 < N;
+    v4f(*red)[4 * MB][64] = reinterpret_cast<v4f(*)[4 * MB][64]>(&xring[0][0][0]);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int64_t m = m0 + 16 * mb + ln;
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            red[wave][nb * MB + mb][lane] = acc[nb][mb];
+    __syncthreads();
+
+    // lane l of block (nb, mb) holds Y[m = m0 + 16 mb + l % 16][n = n0 + 16 nb + 4 (l / 16) + r]
+    const float t = *tscale;
+    for (int idx = tid; idx < 4 * MB * 64; idx += 256) {
+        const int blk = idx >> 6, l = idx & 63;
+        const v4f p = red[0][blk][l] + red[1][blk][l] + red[2][blk][l] + red[3][blk][l];
+        const int nb = blk / MB, mb = blk % MB;
+        const int64_t m = m0 + 16 * mb + (l & 15);
+        const int64_t n = n0 + 16 * nb + 4 * (l >> 4);
         if (m >= M)
             continue;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            v[r] = acc[mb][r] * t;
+            v[r] = p[r] * t;
+        const bool vec_ok = (N & 3) == 0 && n + 3 < N;
         if (!OUT_BF16) {
             float *c = reinterpret_cast<float *>(Y) + m * N + n;
             if (vec_ok) {
@@ -263,6 +326,18 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(const uint16_t *__restrict__
             }
         }
     }
+}
+
+template <int MB, int D>
+void launch_w4a16_cfg(bool out_bf16, const uint16_t *X, const uint8_t *codes,
+                      const uint8_t *bscale, const float *tscale, int64_t M, int64_t N,
+                      int64_t K, void *Y, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
+    if (out_bf16)
+        k_gemm_w4a16<MB, D, true><<<grid, 256, 0, stream>>>(X, codes, bscale, tscale, M, N, K, Y);
+    else
+        k_gemm_w4a16<MB, D, false><<<grid, 256, 0, stream>>>(X, codes, bscale, tscale, M, N, K, Y);
 }
 
 }  // namespace
@@ -295,11 +370,12 @@ hipError_t launch_gemm_w4a16(bool out_bf16, const uint16_t *X, const uint8_t *co
                              const uint8_t *bscale, const float *tscale, int64_t M, int64_t N,
                              int64_t K, void *Y, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    if (out_bf16)
-        k_gemm_w4a16<true><<<grid, 256, 0, stream>>>(X, codes, bscale, tscale, M, N, K, Y);
+    if (M <= 16)
+        launch_w4a16_cfg<1, QR_W4_D1>(out_bf16, X, codes, bscale, tscale, M, N, K, Y, stream);
+    else if (M <= QR_W4_M2)
+        launch_w4a16_cfg<2, QR_W4_D2>(out_bf16, X, codes, bscale, tscale, M, N, K, Y, stream);
     else
-        k_gemm_w4a16<false><<<grid, 256, 0, stream>>>(X, codes, bscale, tscale, M, N, K, Y);
+        launch_w4a16_cfg<4, QR_W4_D4>(out_bf16, X, codes, bscale, tscale, M, N, K, Y, stream);
     return hipGetLastError();
 }
 

@@ -63,8 +63,6 @@ struct GemmArgs {
     int split, kgps;    // number of K splits, groups per split
 };
 
-// Buffer descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-class GPUs.
-constexpr int kBufFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past every descriptor's extent
 
 // The promotion of a unit's partial sum runs QR_PROMOTE_LAG MFMAs after the MFMA that made it,
@@ -77,20 +75,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past every descript
 // hand: the compiler does not see these as memory operations, so it inserts no waits of its
 // own for them (its waits around a loop back edge drain the whole ring).  The caller waits
 // with vm_wait<N>() before the first use, where N is the number of loads issued after the
-// one needed (loads retire in order).  The descriptor is four SGPRs: base address, stride 0,
-// extent in bytes, raw-buffer flags; offsets at or past the extent read zeros.
-typedef int v4i_sgpr __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ v4i_sgpr make_rsrc_sgpr(const void *base, uint32_t extent)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    v4i_sgpr r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)extent);
-    r[3] = kBufFlags;
-    return r;
-}
+// one needed (loads retire in order).
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -106,40 +91,6 @@ __device__ __forceinline__ float asm_load_b32(const v4i_sgpr &rsrc, uint32_t off
     float v;
     asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
     return v;
-}
-
-// Every register an asm load writes must stay live (be named by a later asm statement) until
-// the vm_wait that covers the load: the compiler does not know the write is still pending
-// and would otherwise reuse the register.
-template <int N>
-__device__ __forceinline__ void vm_wait()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Direct-to-LDS loads issued through inline asm: the buffer load writes lane i's 16 (or 4)
-// bytes to LDS address M0 + 16 i (4 i).  The compiler does not see them as memory
-// operations, so it adds no waits for them (it cannot tell that they fill the other LDS
-// stage and would otherwise wait for them before every read of the current one); the caller
-// waits with vm_wait before the barrier that publishes the stage.
-__device__ __forceinline__ void dma16(const v4i_sgpr &rsrc, uint32_t lds_addr, uint32_t voff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
-__device__ __forceinline__ void dma4(const v4i_sgpr &rsrc, uint32_t lds_addr, uint32_t voff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
-// LDS byte address of a __shared__ object (uniform).
-__device__ __forceinline__ uint32_t lds_addr_of(const void *p)
-{
-    return (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
 }
 
 // Workgroup barrier for the LDS stage ring, without the memory fence of __syncthreads():

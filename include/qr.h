@@ -132,7 +132,7 @@ qr_status qr_quant_w_nvfp4(const void *w_bf16, int64_t n, int64_t k, int64_t ld_
  * with the products of x and the dequantized weight (both exact in bf16) accumulated in fp32.
  *   x  bf16 [M, K] dense;  codes / bscale / tscale from qr_quant_w_nvfp4 of W [N, K];
  *   y  [M, N], fp32 or bf16 per y_dtype.
- * Size rules: M, N >= 0, M <= 64 * 65535; K % 128 == 0.  x, codes and y 16-byte aligned, bscale
+ * Size rules: M, N >= 0, (M + 64) K < 2^31; K % 128 == 0.  x, codes and y 16-byte aligned, bscale
  * 2-byte aligned.
  */
 qr_status qr_gemm_w4a16(const void *x_bf16, const uint8_t *codes, const uint8_t *bscale,
