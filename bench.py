@@ -23,8 +23,9 @@ time) as `value`, each op's time with its roofline fraction, the roofline of the
 kernel from its launches in the timed pass, and the CPU oracle timed on a bounded token slice
 of the same step.  Outside the step it also times the batched re-quantization of a 32B
 decoder layer's four weights (`weight_update`, once per optimizer step), the norm with the
-activation quantize fused in (`norm_quant`, the producer of FProp's operand) and the INT8
-W8A8 variant at the same shapes (`int8_w8a8`).
+activation quantize fused in (`norm_quant`, the producer of FProp's operand), the INT8
+W8A8 variant at the same shapes (`int8_w8a8`) and the 4-bit weight path at the decode shape
+(`w4a16`: quantizing the 14336x4096 weight, then the 64x14336x4096 GEMM with bf16 X).
 """
 import argparse
 import hashlib
@@ -230,10 +231,11 @@ def run_gpu(args):
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
     normq = run_norm_quant(torch, qr, st)
     int8 = run_int8(torch, qr, st)
+    w4 = run_w4a16(torch, qr, st)
     del st, ops
     torch.cuda.empty_cache()
     upd = run_weight_update(torch, qr)
-    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8
+    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4
 
 
 def run_norm_quant(torch, qr, st, iters=20):
@@ -310,6 +312,35 @@ def run_int8(torch, qr, st, iters=20):
                            "frac": round(tops / PEAK_INT8_TOPS, 4)}
     us = _median_us(torch, lambda: qr.qr_gemm_int8_w8a8(qxd, sxd, qwd, swd, MD, F, H, yd, 1), iters)
     nb = F * H + F * 4 + MD * H + MD * 4 + MD * F * 2
+    out["gemm_decode"] = {"shape": [MD, F, H], "us": round(us, 2), "bound": "hbm", "bytes": nb,
+                          "achieved": round(nb / us / 1e3, 1), "unit": "GB/s",
+                          "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def run_w4a16(torch, qr, st, iters=20):
+    """The 4-bit weight path at the decode shape: NVFP4-style quantization of the 14336x4096
+    weight (E2M1 codes, an E4M3 scale per 16, an fp32 tensor scale; two passes, the first for
+    the tensor's amax) and the decode GEMM 64x14336x4096 with bf16 X (bf16 out)."""
+    dev = "cuda:0"
+    u8 = torch.uint8
+    g = torch.Generator(device=dev).manual_seed(7002)
+    wd = (torch.randn((F, H), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    codes = torch.empty((F, H // 2), dtype=u8, device=dev)
+    bs = torch.empty((F, H // 16), dtype=u8, device=dev)
+    t = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(qr.QR_NVFP4_WORKSPACE_BYTES, dtype=u8, device=dev)
+    yd = torch.empty((MD, F), dtype=torch.bfloat16, device=dev)
+    out = {}
+    us = _median_us(torch, lambda: qr.qr_quant_w_nvfp4(wd, F, H, H, codes, bs, t, ws,
+                                                       qr.QR_NVFP4_WORKSPACE_BYTES), iters)
+    nb = F * H * 2 + F * H // 2 + F * H // 16 + 4
+    out["quant_w"] = {"shape": [F, H], "us": round(us, 2), "bound": "hbm", "bytes": nb,
+                      "achieved": round(nb / us / 1e3, 1), "unit": "GB/s",
+                      "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del wd
+    us = _median_us(torch, lambda: qr.qr_gemm_w4a16(st.Xd, codes, bs, t, MD, F, H, yd, 1), iters)
+    nb = F * H // 2 + F * H // 16 + 4 + MD * H * 2 + MD * F * 2
     out["gemm_decode"] = {"shape": [MD, F, H], "us": round(us, 2), "bound": "hbm", "bytes": nb,
                           "achieved": round(nb / us / 1e3, 1), "unit": "GB/s",
                           "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
@@ -402,7 +433,7 @@ def main():
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8 = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4 = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -440,6 +471,7 @@ def main():
         "weight_update": upd,
         "norm_quant": normq,
         "int8_w8a8": int8,
+        "w4a16": w4,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
