@@ -21,7 +21,8 @@
 //     (row & 7) so that both the 16-byte stores and the fragment reads are bank-conflict
 //     free.  The next step's global loads are issued before the current step's MFMAs.
 //   * Work-group ids are remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
-//     takes a contiguous run of tiles, which share A rows in its L2.
+//     takes a contiguous run of tiles, laid out as near-square blocks whose tiles share A and
+//     B panels in that XCD's L2.
 //   * Skinny M (decode) uses small tiles and a deterministic split over K: partial sums go
 //     to a caller workspace and a second kernel adds them in a fixed order.
 #include "qr_device.h"
@@ -106,6 +107,26 @@ __device__ __forceinline__ void stage_barrier()
     asm volatile("" ::: "memory");
 }
 
+// Tile order: workgroup ids are dealt round-robin to the 8 XCDs, so id b is remapped to
+// position (b mod 8) * (nb / 8) + b / 8 and each XCD takes a contiguous run of positions.  The
+// positions are then laid out in groups of QR_RASTER_GM tile rows, column by column inside a
+// group, so that the tiles an XCD runs at the same time form a near-square block: at each K
+// step they read fewer distinct A and B panels through that XCD's L2 (4x8 tiles share 12
+// panels where a 2x16 strip of one row band needs 18).
+#ifndef QR_RASTER_GM
+#define QR_RASTER_GM 4
+#endif
+__device__ __forceinline__ void tile_of(int pos, int tilesM, int tilesN, int &tm, int &tn)
+{
+    const int per_group = QR_RASTER_GM * tilesN;
+    const int grp = pos / per_group;
+    const int m_first = grp * QR_RASTER_GM;
+    const int rows = min(QR_RASTER_GM, tilesM - m_first);
+    const int idx = pos - grp * per_group;
+    tm = m_first + idx % rows;
+    tn = idx / rows;
+}
+
 template <class T, int BSCALE, bool OUT_BF16>
 __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 {
@@ -139,7 +160,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const int tiles = g.tilesM * g.tilesN;
     const int split = bid / tiles;
     const int tile = bid - split * tiles;
-    const int tm = tile / g.tilesN, tn = tile - tm * g.tilesN;
+    int tm, tn;
+    tile_of(tile, g.tilesM, g.tilesN, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
     const int gb = split * g.kgps;
     const int ge = min(g.nk, gb + g.kgps);
@@ -221,9 +243,21 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         return f;
     };
 
-    // compute(stage): the MFMAs of one K step from an LDS stage, with the promotions
+    // compute(stage): the MFMAs of one K step from an LDS stage, with the promotions.  The
+    // fragments of the first MFMA are read first, then the other B fragments, then the
+    // scales (first needed by the first promotion): every wave starts the step at the same
+    // barrier, so the first MFMA should wait for as few LDS reads as possible.
     auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS) {
         const float *tSA = tS, *tSB = tS + T::BM;
+        v8i bf[T::JN];
+        v8i afb[2];
+        bf[0] = frag(tB, wn * T::TN);
+        afb[0] = frag(tA, wm * T::TM);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < T::JN; ++j)
+            bf[j] = frag(tB, wn * T::TN + j * 16);
+        __builtin_amdgcn_sched_barrier(0);
         float sav[T::IM];
 #pragma unroll
         for (int i = 0; i < T::IM; ++i)
@@ -241,10 +275,6 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             // boundary or lies inside one block)
             sbw = tSB[T::BN >= kGroup ? (wn * T::TN) / kGroup : 0];
         }
-        v8i bf[T::JN];
-#pragma unroll
-        for (int j = 0; j < T::JN; ++j)
-            bf[j] = frag(tB, wn * T::TN + j * 16);
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         // Software pipeline over single MFMAs (one M sub-tile x one N sub-tile): the partial
         // of unit u is promoted QR_PROMOTE_LAG units later, so the VALU never waits on it.
@@ -261,8 +291,6 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         };
         // A fragments double-buffered: sub-tile i+1's fragment is read from LDS while
         // sub-tile i's MFMAs run, so the LDS latency stays hidden.
-        v8i afb[2];
-        afb[0] = frag(tA, wm * T::TM);
 #pragma unroll
         for (int u = 0; u < T::IM * T::JN; ++u) {
             const int i = u / T::JN, j = u % T::JN;
@@ -663,8 +691,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
     int bid = blockIdx.x;
     const int nb = gridDim.x;
     if ((nb & 7) == 0)
-        bid = (bid & 7) * (nb >> 3) + (bid >> 3);   // a contiguous band of tiles per XCD
-    const int tm = bid / g.tilesN, tn = bid - tm * g.tilesN;
+        bid = (bid & 7) * (nb >> 3) + (bid >> 3);   // a contiguous run of tiles per XCD
+    int tm, tn;
+    tile_of(bid, g.tilesM, g.tilesN, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
     const int64_t M = g.M, N = g.N, K = g.K;
     const int nk = g.nk;

@@ -452,6 +452,8 @@ def test_fprop_tiny_fp32_full():
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (1, 128, 128), (300, 264, 256),
                                    (129, 1000, 640), (64, 512, 1024), (256, 384, 2048),
                                    (520, 136, 384),
+                                   # 256x256 tiles with one K step, and with ragged M and N
+                                   (300, 264, 128), (600, 520, 1152),
                                    # decode batches (M <= 64): ragged N, group counts that
                                    # are not a multiple of the kernel's 8-group ring
                                    (5, 200, 1152), (17, 1000, 384), (33, 72, 640),
@@ -516,7 +518,10 @@ def test_backward_8b_dgrad_wgrad_sampled():
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (384, 200, 384), (128, 77, 1024),
-                                   (1024, 136, 512)])
+                                   (1024, 136, 512),
+                                   # WGrad on 256x256 tiles (N > 256): ragged rows, and a
+                                   # contraction of one group (M = 128 tokens)
+                                   (256, 520, 384), (128, 300, 256)])
 def test_dgrad_wgrad_small_full(M, N, K):
     """Full comparison on small backward shapes: M tokens, N output features, K inputs."""
     say("dgrad/wgrad small", M, N, K)
