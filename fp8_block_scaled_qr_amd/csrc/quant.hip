@@ -123,7 +123,8 @@ template <int MODE>
 __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int64_t rows,
                                             int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
                                             float *__restrict__ s, uint8_t *__restrict__ qT,
-                                            float *__restrict__ sT, int64_t first, int64_t stride)
+                                            float *__restrict__ sT, int64_t first, int64_t stride,
+                                            int64_t pend)
 {
     constexpr bool ROW = (MODE & QMODE_ROW) != 0;
     constexpr bool COL = (MODE & QMODE_COL) != 0;
@@ -318,13 +319,16 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
     // Tile (bi, bj) is walked incrementally (no 64-bit division in the loop).  A tile past
     // the end gets an empty descriptor (its loads return zeros without touching memory), so
     // the loads are issued unconditionally and the compiler's wait counts stay exact.
-    auto prefetch = [&](int64_t bi, int64_t bj, uint4 (&v)[8]) {
-        const bool valid = bi < ngr;
+    // The walk visits linear tile indices first, first + stride, ... below pend (at most the
+    // tile count).
+    auto prefetch = [&](int64_t pi, int64_t bi, int64_t bj, uint4 (&v)[8]) {
+        const bool valid = pi < pend;
         const int64_t c = bj * kTile + 8 * oc;
         load_tile(x, valid ? rows : 0, ldx, valid ? bi * kTile : 0, c, c < cols, oq, v);
     };
     const int64_t dbi = stride / ngc, dbj = stride - dbi * ngc;
-    auto advance = [&](int64_t &bi, int64_t &bj) {
+    auto advance = [&](int64_t &pi, int64_t &bi, int64_t &bj) {
+        pi += stride;
         bi += dbi;
         bj += dbj;
         if (bj >= ngc) {
@@ -333,27 +337,35 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
         }
     };
     uint4 va[8], vb[8];
-    int64_t bi = first / ngc, bj = first - bi * ngc;
-    int64_t ni = bi, nj = bj;
-    prefetch(bi, bj, va);
-    while (bi < ngr) {
-        advance(ni, nj);
-        prefetch(ni, nj, vb);
+    int64_t pi = first, bi = first / ngc, bj = first - bi * ngc;
+    int64_t np = pi, ni = bi, nj = bj;
+    prefetch(pi, bi, bj, va);
+    while (pi < pend) {
+        advance(np, ni, nj);
+        prefetch(np, ni, nj, vb);
         process(bi, bj, 0, va);
+        pi = np;
         bi = ni;
         bj = nj;
-        if (bi >= ngr)
+        if (pi >= pend)
             break;
-        advance(ni, nj);
-        prefetch(ni, nj, va);
+        advance(np, ni, nj);
+        prefetch(np, ni, nj, va);
         process(bi, bj, 1, vb);
+        pi = np;
         bi = ni;
         bj = nj;
     }
 }
 
-// Persistent: as many workgroups as fit on the CUs at once; workgroup b handles tiles b,
-// b + gridDim.x, ...
+// Persistent: as many workgroups as fit on the CUs at once; workgroup b handles tiles
+// first(b), first(b) + gridDim.x, ... (row-major over the tile grid), so at any time the grid
+// works on one contiguous window of tiles.  first(b) = b, except for the row-group pass when
+// the window holds whole row bands, 8 or more: ids are dealt round-robin to the 8 XCDs, and
+// XCD x (ids b with b mod 8 = x) then takes whole row bands x, x + 8, ... of each window, so
+// the 4-byte row-scale stores of a band (its tiles' scales share 128-byte lines) merge in one
+// L2 before they are written back.  (The column pass keeps first(b) = b: with 128-column
+// tiles and a row of tiles a multiple of 8 long, a column band already stays on one XCD.)
 template <int MODE>
 __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ldx,
@@ -362,7 +374,15 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
                                                     uint8_t *__restrict__ qT,
                                                     float *__restrict__ sT)
 {
-    quant_tiles<MODE>(x, rows, cols, ldx, q, s, qT, sT, blockIdx.x, gridDim.x);
+    const int64_t ngc = (cols + kTile - 1) / kTile;
+    const int64_t nt = ((rows + kTile - 1) / kTile) * ngc;
+    const int64_t G = gridDim.x;
+    int64_t first = blockIdx.x;
+    if (MODE == QMODE_ROW && (G & 7) == 0 && (G / 8) % ngc == 0) {
+        const int64_t xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
+        first = (xcd + 8 * (l / ngc)) * ngc + l % ngc;
+    }
+    quant_tiles<MODE>(x, rows, cols, ldx, q, s, qT, sT, first, G, nt);
 }
 
 // A list of weights quantized in one persistent launch (a weight update re-quantizes every
@@ -379,7 +399,7 @@ __global__ __launch_bounds__(256) void k_quant_w_batch(WeightTable tab)
         int64_t first = ((int64_t)blockIdx.x - before) % G;
         if (first < 0)
             first += G;
-        quant_tiles<MODE>(d.w, d.n, d.k, d.ld, d.q, d.s, d.qT, d.sT, first, G);
+        quant_tiles<MODE>(d.w, d.n, d.k, d.ld, d.q, d.s, d.qT, d.sT, first, G, d.tiles);
         before += d.tiles;
         __syncthreads();   // LDS of this tensor's last tile is read before the next one writes
     }
