@@ -6,10 +6,11 @@ input, at the 8B-layer shapes (hidden 4096, 8192 tokens; decode FFN 14336 at bat
 
   uaq_fold        W [4096, 4096] / s (per input column), gain * s        (one-time op; timed)
   quant_w         128x128 blocks of the folded W, plus the transposed copy for DGrad
-  quant_x         1x128 groups of X [8192, 4096]  (X is the norm output carrying s)
+  quant_x_dual    1x128 rows of X [8192, 4096] for FProp and its 128x1 columns (transposed)
+                  for WGrad, one read (X is the norm output carrying s); the column codes are
+                  the FP8 activations kept for the backward
   fprop           Y = X W^T            8192 x 4096 x 4096, bf16 out
   quant_dy_dual   1x128 rows and 128x1 columns (transposed) of dY [8192, 4096], one read
-  quant_x_col     128x1 columns (transposed) of X
   dgrad           dX = dY W            8192 x 4096 x 4096, bf16 out
   wgrad           dW = dY^T X          4096 x 4096 x 8192, bf16 out
   quant_x_dec     1x128 groups of the decode activation X [64, 4096]
@@ -63,10 +64,10 @@ def op_table():
         "uaq_fold": ("hbm", H * H * 2 * 2 + H * 4 * 3),
         # read bf16, write codes twice + scales twice
         "quant_w": ("hbm", H * H * 2 + 2 * H * H + 2 * (H // g) ** 2 * 4),
-        "quant_x": ("hbm", T * H * 2 + T * H + T * (H // g) * 4),
+        # read X once, write row codes + scales and transposed column codes + scales
+        "quant_x_dual": ("hbm", T * H * 2 + 2 * T * H + T * (H // g) * 4 + H * (T // g) * 4),
         "fprop": ("mfma", gemm_flops(T, H, H)),
         "quant_dy_dual": ("hbm", T * H * 2 + 2 * T * H + 2 * T * (H // g) * 4),
-        "quant_x_col": ("hbm", T * H * 2 + T * H + H * (T // g) * 4),
         "dgrad": ("mfma", gemm_flops(T, H, H)),
         "wgrad": ("mfma", gemm_flops(H, H, T)),
         "quant_x_dec": ("hbm", MD * H * 2 + MD * H + MD * (H // g) * 4),
@@ -161,12 +162,12 @@ class Step:
         return [
             ("uaq_fold", lambda: qr.qr_uaq_fold(self.W, H, H, H, self.s, self.Wf, self.gain)),
             ("quant_w", lambda: qr.qr_quant_w_128x128(self.Wf, H, H, H, self.qW, self.sW, self.qWT, self.sWT)),
-            ("quant_x", lambda: qr.qr_quant_act_1x128(self.X, T, H, H, self.qX, self.sX, None, None)),
+            ("quant_x_dual", lambda: qr.qr_quant_act_1x128(self.X, T, H, H, self.qX, self.sX, self.qXT,
+                                                           self.sXT)),
             ("fprop", lambda: qr.qr_gemm_fp8_bsfprop(self.qX, self.sX, self.qW, self.sW, T, H, H, self.Y, BF,
                                                      *self.ws["fprop"])),
             ("quant_dy_dual", lambda: qr.qr_quant_act_1x128(self.dY, T, H, H, self.qdY, self.sdY, self.qdYT,
                                                             self.sdYT)),
-            ("quant_x_col", lambda: qr.qr_quant_act_1x128(self.X, T, H, H, None, None, self.qXT, self.sXT)),
             ("dgrad", lambda: qr.qr_gemm_fp8_bsdgrad(self.qdY, self.sdY, self.qWT, self.sWT, T, H, H, self.dX, BF,
                                                      *self.ws["dgrad"])),
             ("wgrad", lambda: qr.qr_gemm_fp8_bswgrad(self.qdYT, self.sdYT, self.qXT, self.sXT, T, H, H, self.dW, BF,
@@ -461,9 +462,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic (seeded; 8B-layer shapes)",
         "config": {"workload": ("8B-layer FP8 step: UAQ fold + 128x128 W quantize (4096x4096), "
-                                "1x128 X quantize + FProp 8192x4096x4096, fused dual dY "
-                                "quantize-transpose + X 128x1, DGrad and WGrad (8192 tokens), "
-                                "decode FProp 64x14336x4096"),
+                                "1x128 + 128x1 X quantize in one read (the 128x1 codes kept "
+                                "for WGrad) + FProp 8192x4096x4096, fused dual dY "
+                                "quantize-transpose, DGrad and WGrad (8192 tokens), decode "
+                                "FProp 64x14336x4096"),
                    "tokens": T, "hidden": H, "decode_batch": MD, "decode_ffn": F,
                    "gemm_gflop_per_step": round(gemm_total / 1e9, 2)},
         "roofline": roof,
