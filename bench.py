@@ -25,8 +25,10 @@ kernel from its launches in the timed pass, and the CPU oracle timed on a bounde
 of the same step.  Outside the step it also times the batched re-quantization of a 32B
 decoder layer's four weights (`weight_update`, once per optimizer step), the norm with the
 activation quantize fused in (`norm_quant`, the producer of FProp's operand), the INT8
-W8A8 variant at the same shapes (`int8_w8a8`) and the 4-bit weight path at the decode shape
-(`w4a16`: quantizing the 14336x4096 weight, then the 64x14336x4096 GEMM with bf16 X).
+W8A8 variant at the same shapes (`int8_w8a8`), the 4-bit weight path at the decode shape
+(`w4a16`: quantizing the 14336x4096 weight, then the 64x14336x4096 GEMM with bf16 X) and the
+32B decoder layer's four FP8 linears at decode batch 256 on the weight update's codes
+(`decode_32b`).
 """
 import argparse
 import hashlib
@@ -235,8 +237,11 @@ def run_gpu(args):
     w4 = run_w4a16(torch, qr, st)
     del st, ops
     torch.cuda.empty_cache()
-    upd = run_weight_update(torch, qr)
-    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4
+    upd, codes = run_weight_update(torch, qr)
+    dec32 = run_decode_32b(torch, qr, codes)
+    del codes
+    torch.cuda.empty_cache()
+    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec32
 
 
 def run_norm_quant(torch, qr, st, iters=20):
@@ -369,13 +374,50 @@ def run_weight_update(torch, qr, iters=10):
         nbytes += n * k * (2 + 1 + 1) + 2 * nb * 4
     us = _median_us(torch, lambda: qr.qr_quant_w_128x128_batched(items), iters, flush=False)
     gbs = nbytes / (us * 1e-6) / 1e9
+    codes = [(q, s, n, k) for (_, n, k, _, q, s, _, _) in items]
     del ws, items
     torch.cuda.empty_cache()
-    return {"workload": "32B decoder layer weights (QKV 7168x5120, O 5120x5120, gate+up "
-                        "55296x5120, down 5120x27648) re-quantized 128x128 with transposed "
-                        "copies, one batched call",
-            "us": round(us, 1), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
-            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": 1}
+    upd = {"workload": "32B decoder layer weights (QKV 7168x5120, O 5120x5120, gate+up "
+                       "55296x5120, down 5120x27648) re-quantized 128x128 with transposed "
+                       "copies, one batched call",
+           "us": round(us, 1), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": 1}
+    return upd, codes
+
+
+def run_decode_32b(torch, qr, codes, iters=20):
+    """The 32B decoder layer's four linears at decode batch 256 on their 128x128 FP8 codes
+    (the weight update's output): 1x128 activation codes of X [256, K], then FProp with bf16
+    out.  Each GEMM is timed after a cache-evicting read, so its weight streams from HBM.
+    Algorithmic bytes = weight codes + block scales + activation codes and scales + bf16 Y."""
+    dev = "cuda:0"
+    M, g = 256, 128
+    names = ["qkv", "o", "gate_up", "down"]
+    gen = torch.Generator(device=dev).manual_seed(6101)
+    out, tot_us, tot_fl, tot_b = {}, 0.0, 0.0, 0
+    for name, (q, s, n, k) in zip(names, codes):
+        x = torch.randn((M, k), device=dev, generator=gen).to(torch.bfloat16)
+        qx, sx = qr.quant_act(x)[:2]
+        y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        nb = qr.qr_gemm_workspace_bytes(0, M, n, k)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        us = _median_us(torch, lambda: qr.qr_gemm_fp8_bsfprop(qx, sx, q, s, M, n, k, y,
+                                                             qr.QR_OUT_BF16, ws, nb), iters)
+        fl = gemm_flops(M, n, k)
+        by = n * k + (n // g) * (k // g) * 4 + M * k + M * (k // g) * 4 + M * n * 2
+        tf, gbs = fl / (us * 1e-6) / 1e12, by / (us * 1e-6) / 1e9
+        out[name] = {"shape": [M, n, k], "us": round(us, 2), "tflops": round(tf, 1),
+                     "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4)}
+        tot_us, tot_fl, tot_b = tot_us + us, tot_fl + fl, tot_b + by
+        del x, qx, sx, y, ws
+    out["layer"] = {"us": round(tot_us, 1), "tflops": round(tot_fl / (tot_us * 1e-6) / 1e12, 1),
+                    "gbs": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["workload"] = ("32B decoder layer at decode batch 256: QKV 5120->7168, O 5120->5120, "
+                       "gate+up 5120->55296, down 27648->5120; FP8 FProp, bf16 out, each "
+                       "after a cache-evicting read")
+    return out
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -434,7 +476,7 @@ def main():
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4 = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec32 = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -471,6 +513,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "weight_update": upd,
+        "decode_32b": dec32,
         "norm_quant": normq,
         "int8_w8a8": int8,
         "w4a16": w4,

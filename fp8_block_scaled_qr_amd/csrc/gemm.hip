@@ -37,9 +37,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 128;
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_ = 2>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NS = NS_;                         // LDS stages of the load ring
+    static_assert(NS >= 2, "at least two stages");
     static constexpr int THREADS = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;       // wave tile
     static constexpr int IM = TM / 16, JN = TN / 16;       // 16x16 sub-tiles per wave
@@ -142,9 +144,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     static_assert(DA * 8 * NW == T::BM && DB * 8 * NW == T::BN, "whole 1 KB loads per wave");
 
     // Two LDS stages per operand; the global loads write them directly (no register staging).
-    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][T::BM * kGroup];
-    __shared__ __attribute__((aligned(1024))) uint8_t smB[2][T::BN * kGroup];
-    __shared__ __attribute__((aligned(256))) float sS[2][T::BM + SB_SLOTS];
+    __shared__ __attribute__((aligned(1024))) uint8_t smA[T::NS][T::BM * kGroup];
+    __shared__ __attribute__((aligned(1024))) uint8_t smB[T::NS][T::BN * kGroup];
+    __shared__ __attribute__((aligned(256))) float sS[T::NS][T::BM + SB_SLOTS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index: uniform across the wave, so say so (scalar offsets stay scalar)
@@ -307,23 +309,39 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             promote(u);
     };
 
-    // ---- main loop: one 128-wide scale group per step, two LDS stages.  Step k first issues
-    // the loads of step k+1 into the other stage (free: every wave finished reading it before
-    // the last barrier), then computes from its own stage; before the barrier each wave waits
-    // for its own loads, so after it the next stage is complete.  Past the end of the K range
-    // the loads re-read the last group (clamped) into a stage that is never read.
+    // ---- main loop: one 128-wide scale group per step, a ring of NS LDS stages.  Step k
+    // first issues the loads of step k+NS-1 into the stage step k-1 used (free: every wave
+    // finished reading it before the last barrier), then computes from its own stage; before
+    // the barrier each wave waits for its own loads of step k+1 (loads retire in order, so it
+    // lets the NS-2 later steps' loads stay in flight), so after it the next stage is
+    // complete.  Past the end of the K range the loads re-read the last group (clamped) into
+    // stages that are never read.
     const int glast = ge - 1;
-    if (gb < ge)
-        issue_step(gb, 0);
-    vm_wait<0>();
+#pragma unroll
+    for (int p = 0; p < T::NS - 1; ++p)
+        issue_step(min(gb + p, glast), p);
+    // this wave's loads per step: its tile loads, plus one scale load on the scale waves
+    auto wait_next = [&]() {
+        constexpr int C = DA + DB;
+        if (T::NS == 2) {
+            vm_wait<0>();
+        } else if (sA_wave || sB_wave) {
+            vm_wait<(T::NS - 2) * (C + 1)>();
+        } else {
+            vm_wait<(T::NS - 2) * C>();
+        }
+    };
+    wait_next();   // step gb's loads
     stage_barrier();
+    int st = 0, st_load = T::NS - 1;
 #pragma nounroll
     for (int kg = gb; kg < ge; ++kg) {
-        const int st = (kg - gb) & 1;
-        issue_step(min(kg + 1, glast), st ^ 1);
+        issue_step(min(kg + T::NS - 1, glast), st_load);
         compute(smA[st], smB[st], sS[st]);
-        vm_wait<0>();   // this wave's loads of step k+1
+        wait_next();   // this wave's loads of step k+1
         stage_barrier();
+        st = st + 1 == T::NS ? 0 : st + 1;
+        st_load = st_load + 1 == T::NS ? 0 : st_load + 1;
     }
 
     // ---- epilogue: lane holds C[m][n..n+3] for each sub-tile
@@ -899,12 +917,20 @@ hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hi
 
 }  // namespace
 
+#ifndef QR_BIG_MIN_M
+#define QR_BIG_MIN_M 65
+#endif
+constexpr int64_t kCUs = 256;   // MI355X compute units: one 256x256 workgroup each
+
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
 {
     GemmPlan p;
-    // Large M: 256x256 tiles, 8 waves of 128x64 (the per-row B scales of WGrad fit too, now
-    // that the operand tiles go straight from memory to LDS without register staging).
-    if (M > 256)
+    // M > 64: 256x256 tiles, 8 waves of 128x64 (the per-row B scales of WGrad fit too, now
+    // that the operand tiles go straight from memory to LDS without register staging).  At
+    // decode batches of 65..256 rows this reads each weight panel once for all rows, where
+    // 128x128 or 256x64 tiles re-read the whole activation for every 128 or 64 weight rows
+    // (2.1x faster on a 32B layer's four linears at batch 256).
+    if (M >= QR_BIG_MIN_M)
         p.cfg = CFG_BIG4;
     else if (M <= 64 && bscale == BSCALE_BLOCK)
         p.cfg = CFG_SKINNY;   // decode: stream B once, no split
@@ -929,6 +955,16 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
             split = 16;
         if (split < 1)
             split = 1;
+        const int64_t kgps = (nk + split - 1) / split;
+        split = (nk + kgps - 1) / kgps;
+    }
+    // 256x256 tiles that would leave more than half of the CUs idle: split K so that the
+    // tiles' splits make one wave of at most one workgroup per CU (a decode batch of 256 rows
+    // against a 7168-wide weight has 28 tiles, 8 splits of 5 groups each)
+    if (p.cfg == CFG_BIG4 && tiles > 0 && tiles <= kCUs / 2 && nk > 1) {
+        split = kCUs / tiles;
+        if (split > nk)
+            split = nk;
         const int64_t kgps = (nk + split - 1) / split;
         split = (nk + kgps - 1) / kgps;
     }
