@@ -213,10 +213,12 @@ def test_gemm_int8(M, N, K, out):
     _check_int8(out_f64(y), oracle.gemm_int8(qa, sa, qb, sb), out)
 
 
-@pytest.mark.parametrize("M,N,K", [(8192, 4096, 4096), (64, 14336, 4096), (256, 5120, 27648)])
+@pytest.mark.parametrize("M,N,K", [(8192, 4096, 4096), (64, 14336, 4096), (256, 5120, 27648),
+                                   (256, 55296, 5120), (200, 32768, 256)])
 def test_gemm_int8_full_size_sampled(M, N, K):
-    """The 8B prefill shape, the 8B decode shape and the 32B down projection at batch 256, on
-    sampled outputs (every tile and both ragged ends hit)."""
+    """The 8B prefill shape, the 8B decode shape, the 32B down and gate+up projections at
+    batch 256, and a ragged-M batch on the 256x256 tiles (128 tiles, the smallest count that
+    takes them), on sampled outputs (every tile and both ragged ends hit)."""
     say("gemm_int8 full", M, N, K)
     qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
     y = out_f64(qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_BF16))
