@@ -462,9 +462,12 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
     const int64_t M = g.M, N = g.N, K = g.K;
     const int nk = g.nk;
     const int64_t nw0 = (int64_t)blockIdx.x * (16 * NW) + 16 * wn;   // this wave's first B row
-    // this wave's groups: [gbeg, gend); every split takes gps steps (uniform barriers)
-    const int gps = (nk + KS - 1) / KS;
-    const int gbeg = ks * gps, gend = min(nk, gbeg + gps);
+    // The workgroup's groups: [wbeg, wend), split blockIdx.y of g.split K splits across
+    // workgroups (g.kgps groups each).  This wave's: [gbeg, gend); every split inside the
+    // workgroup takes gps steps (uniform barriers).
+    const int wbeg = (int)blockIdx.y * g.kgps, wend = min(nk, wbeg + g.kgps);
+    const int gps = (max(wend - wbeg, 0) + KS - 1) / KS;
+    const int gbeg = wbeg + ks * gps, gend = min(wend, gbeg + gps);
 
     // B: this wave's 16 rows
     int64_t browsv = N - nw0;
@@ -634,7 +637,8 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
             }
     }
 
-    // epilogue: lane holds C[m][n..n+3], m = 16 t + lane % 16, n = nw0 + 4 (lane / 16)
+    // epilogue: lane holds C[m][n..n+3], m = 16 t + lane % 16, n = nw0 + 4 (lane / 16); with
+    // K split across workgroups, fp32 partials go to the workspace [split][M][N]
     const int64_t n = nw0 + 4 * lq;
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
@@ -643,8 +647,8 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
         if (m >= M || n >= N)
             continue;
         const v4f a = acc[t];
-        if (!OUT_BF16) {
-            float *c = reinterpret_cast<float *>(g.C) + m * N + n;
+        if (!OUT_BF16 || g.split > 1) {
+            float *c = reinterpret_cast<float *>(g.C) + (int64_t)blockIdx.y * M * N + m * N + n;
             if (vec_ok && n + 3 < N) {
                 *reinterpret_cast<float4 *>(c) = make_float4(a[0], a[1], a[2], a[3]);
             } else {
@@ -880,10 +884,11 @@ hipError_t launch_skinny(bool out_bf16, const GemmArgs &a, hipStream_t stream)
 {
     const int64_t blocks = (a.N + 16 * kSkinnyNW - 1) / (16 * kSkinnyNW);
     constexpr int threads = 64 * kSkinnyNW * kSkinnyKS;
+    const dim3 grid((unsigned)blocks, (unsigned)a.split);
     if (out_bf16)
-        k_gemm_skinny<MT, kSkinnyNW, kSkinnyKS, kSkinnyD, true><<<(unsigned)blocks, threads, 0, stream>>>(a);
+        k_gemm_skinny<MT, kSkinnyNW, kSkinnyKS, kSkinnyD, true><<<grid, threads, 0, stream>>>(a);
     else
-        k_gemm_skinny<MT, kSkinnyNW, kSkinnyKS, kSkinnyD, false><<<(unsigned)blocks, threads, 0, stream>>>(a);
+        k_gemm_skinny<MT, kSkinnyNW, kSkinnyKS, kSkinnyD, false><<<grid, threads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -945,6 +950,19 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t nk = K / kGroup;
     int64_t split = 1;
+#ifndef QR_SKINNY_SPLIT
+#define QR_SKINNY_SPLIT 1
+#endif
+    // Decode batches on narrow weights: fewer than half of the CUs would get a workgroup, so
+    // K is split across workgroups as well (at least 8 groups each, so the load ring stays
+    // full; the fp32 partials are small at M <= 64).  A 64x4096x4096 product gets 4 splits.
+    if (QR_SKINNY_SPLIT && p.cfg == CFG_SKINNY && tiles > 0 && tiles <= kCUs / 2 && nk >= 16) {
+        split = kCUs / tiles;
+        if (split > nk / 8)
+            split = nk / 8;
+        const int64_t kgps = (nk + split - 1) / split;
+        split = (nk + kgps - 1) / kgps;
+    }
     if (p.cfg != CFG_BIG4 && p.cfg != CFG_SKINNY && tiles > 0 && tiles < 512 &&
         nk > 0) {
         split = (512 + tiles - 1) / tiles;
@@ -993,13 +1011,14 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     a.split = plan.split;
     a.kgps = (a.nk + plan.split - 1) / plan.split;
     a.C = plan.split > 1 ? ws : C;
-    if (plan.cfg == CFG_SKINNY)
-        return M <= 16 ? launch_skinny<1>(out_bf16, a, stream)
-               : M <= 32 ? launch_skinny<2>(out_bf16, a, stream)
-                         : launch_skinny<4>(out_bf16, a, stream);
     const int blocks = a.tilesM * a.tilesN * plan.split;
     hipError_t e;
     switch (plan.cfg) {
+    case CFG_SKINNY:
+        e = M <= 16 ? launch_skinny<1>(out_bf16, a, stream)
+            : M <= 32 ? launch_skinny<2>(out_bf16, a, stream)
+                      : launch_skinny<4>(out_bf16, a, stream);
+        break;
     case CFG_BIG4: e = launch_t<CfgBig4>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M64: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M128: e = launch_t<CfgM128>(bscale, out_bf16, a, blocks, stream); break;

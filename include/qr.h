@@ -272,7 +272,11 @@ qr_status qr_gemm_fp8_bswgrad(const uint8_t *dyT, const float *sdyT, const uint8
                               qr_stream stream);
 
 /* Workspace bytes the GEMM entry point of `kind` needs for these sizes (0 if none).  The
- * sizes are the ones passed to that entry point.  Returns 0 for invalid arguments. */
+ * sizes are the ones passed to that entry point.  Returns 0 for invalid arguments.
+ * It is non-zero when the product is split over its contraction to occupy the GPU: up to
+ * 256 output rows (decode batches) against a narrow weight, or few 256x256 output tiles.  The
+ * splits' fp32 partial sums [split][rows][cols] are then added in split order, so results do
+ * not depend on timing. */
 size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 /*

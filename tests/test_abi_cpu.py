@@ -196,8 +196,12 @@ def test_gemm_validation(L, name):
     assert gemm(L, name, A, B, C, D, *dims, None, 1, None, 0) == NULL
     assert gemm(L, name, A + 4, B, C, D, *dims, E, 1, None, 0) == ALIGN
     assert gemm(L, name, A, B + 2, C, D, *dims, E, 1, None, 0) == ALIGN
-    assert gemm(L, name, A, B, C, D, *dims, A + 64, 1, None, 0) == ALIAS    # output over A
-    assert gemm(L, name, A, B, C, D, *dims, C, 0, None, 0) == ALIAS         # output over B
+    # 512^3 splits K over its four 256x256 tiles, so a (large enough) workspace is passed
+    ws, wsb = 6 << 40, qr.qr_gemm_workspace_bytes(0, 512, 512, 512)
+    assert wsb > 0
+    assert gemm(L, name, A, B, C, D, *dims, E, 1, None, 0) == WORKSPACE
+    assert gemm(L, name, A, B, C, D, *dims, A + 64, 1, ws, wsb) == ALIAS    # output over A
+    assert gemm(L, name, A, B, C, D, *dims, C, 0, ws, wsb) == ALIAS         # output over B
     z = list(dims)
     z[[0, 1, 2][contraction - 1]] = 0                                         # an output dim 0
     assert gemm(L, name, A, B, C, D, *z, E, 1, None, 0) == OK
@@ -205,10 +209,12 @@ def test_gemm_validation(L, name):
 
 def test_gemm_workspace(L):
     # mid-size M (65..256) splits K over a few tiles and needs a workspace; decode batches up
-    # to 64 rows stream the weight without a split; large shapes need none
+    # to 64 rows stream a wide weight without a split, and split K over a narrow one; large
+    # shapes need none
     nb = qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 200, 14336, 4096)
     assert nb > 0 and nb % (200 * 14336 * 4) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 4096) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 4096, 4096) == 4 * 64 * 4096 * 4
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 8192, 4096, 4096) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 200, 14336, 100) == 0    # invalid K
     assert qr.qr_gemm_workspace_bytes(9, 200, 14336, 4096) == 0

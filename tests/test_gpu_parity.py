@@ -459,7 +459,10 @@ def test_fprop_tiny_fp32_full():
                                    # decode batches (M <= 64): ragged N, group counts that
                                    # are not a multiple of the kernel's 8-group ring
                                    (5, 200, 1152), (17, 1000, 384), (33, 72, 640),
-                                   (64, 264, 1280), (16, 8, 128)])
+                                   (64, 264, 1280), (16, 8, 128),
+                                   # decode batches on narrow weights: K split across
+                                   # workgroups (2 and 3 splits, the last one shorter)
+                                   (40, 1000, 2304), (64, 520, 3200)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_fprop_shapes_full(M, N, K, out):
     x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 7, max(1, K // 100))
@@ -471,6 +474,16 @@ def test_fprop_decode_8b_sampled():
     lin = qr_synth.decode_8b()
     smp = sample_positions(lin.M, lin.N, 4096, 1)
     print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, smp, "decode_8b"))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 14336), (64, 5120, 27648)])
+def test_fprop_decode_narrow_sampled(M, N, K):
+    """Decode batch 64 against the 8B down projection and the 32B one: the weight is narrow,
+    so K is split across workgroups (4 and 3 splits); sampled outputs."""
+    x = qr_synth.normal_bf16(M + K, (M, K), 1.0, 11, max(1, K // 100))
+    w = qr_synth.normal_bf16(N + K, (N, K), 0.02)
+    smp = sample_positions(M, N, 4096, 5)
+    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, smp, f"{M}x{N}x{K}"))
 
 
 def test_fprop_prefill_8b_sampled():
@@ -551,7 +564,7 @@ def test_dgrad_wgrad_small_full(M, N, K):
         assert_gemm_close(out_f64(dw), Y, S, "wgrad", out == qr.QR_OUT_BF16)
 
 
-@pytest.mark.parametrize("M,N,K", [(48, 384, 520), (8, 128, 1000)])
+@pytest.mark.parametrize("M,N,K", [(48, 384, 520), (8, 128, 1000), (48, 2304, 384)])
 def test_dgrad_decode_batch_full(M, N, K):
     """DGrad with a small token count takes the skinny-M kernel; full comparison."""
     say("dgrad small M", M, N, K)
