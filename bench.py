@@ -27,8 +27,8 @@ decoder layer's four weights (`weight_update`, once per optimizer step), the nor
 activation quantize fused in (`norm_quant`, the producer of FProp's operand), the INT8
 W8A8 variant at the same shapes (`int8_w8a8`), the 4-bit weight path at the decode shape
 (`w4a16`: quantizing the 14336x4096 weight, then the 64x14336x4096 GEMM with bf16 X) and the
-32B decoder layer's four FP8 linears at decode batch 256 on the weight update's codes
-(`decode_32b`).
+8B decoder layer's four FP8 linears at decode batch 64 (`decode_8b`) and the 32B decoder
+layer's four at decode batch 256 on the weight update's codes (`decode_32b`).
 """
 import argparse
 import hashlib
@@ -237,11 +237,13 @@ def run_gpu(args):
     w4 = run_w4a16(torch, qr, st)
     del st, ops
     torch.cuda.empty_cache()
+    dec8 = run_decode_8b(torch, qr)
+    torch.cuda.empty_cache()
     upd, codes = run_weight_update(torch, qr)
     dec32 = run_decode_32b(torch, qr, codes)
     del codes
     torch.cuda.empty_cache()
-    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec32
+    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec8, dec32
 
 
 def run_norm_quant(torch, qr, st, iters=20):
@@ -385,6 +387,41 @@ def run_weight_update(torch, qr, iters=10):
     return upd, codes
 
 
+def run_decode_8b(torch, qr, iters=20):
+    """The 8B decoder layer's four linears at decode batch 64 (QKV 4096->6144, O 4096->4096,
+    gate+up 4096->28672, down 14336->4096): seeded N(0, 0.02) weights quantized 128x128, then
+    FProp on 1x128 activation codes, bf16 out, each after a cache-evicting read."""
+    dev = "cuda:0"
+    M, g = MD, 128
+    shapes = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096),
+              ("down", 4096, 14336)]
+    gen = torch.Generator(device=dev).manual_seed(6201)
+    out, tot_us, tot_b = {}, 0.0, 0
+    for name, n, k in shapes:
+        w = (torch.randn((n, k), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        q, s = qr.quant_w(w)[:2]
+        del w
+        x = torch.randn((M, k), device=dev, generator=gen).to(torch.bfloat16)
+        qx, sx = qr.quant_act(x)[:2]
+        y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        nb = qr.qr_gemm_workspace_bytes(0, M, n, k)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        us = _median_us(torch, lambda: qr.qr_gemm_fp8_bsfprop(qx, sx, q, s, M, n, k, y,
+                                                             qr.QR_OUT_BF16, ws, nb), iters)
+        by = n * k + (n // g) * (k // g) * 4 + M * k + M * (k // g) * 4 + M * n * 2
+        gbs = by / (us * 1e-6) / 1e9
+        out[name] = {"shape": [M, n, k], "us": round(us, 2), "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "k_splits": nb // (M * n * 4) if nb else 1}
+        tot_us, tot_b = tot_us + us, tot_b + by
+        del q, s, x, qx, sx, y, ws
+    out["layer"] = {"us": round(tot_us, 1), "gbs": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["workload"] = ("8B decoder layer at decode batch 64: QKV 4096->6144, O 4096->4096, "
+                       "gate+up 4096->28672, down 14336->4096; FP8 FProp, bf16 out, each after "
+                       "a cache-evicting read")
+    return out
+
+
 def run_decode_32b(torch, qr, codes, iters=20):
     """The 32B decoder layer's four linears at decode batch 256 on their 128x128 FP8 codes
     (the weight update's output): 1x128 activation codes of X [256, K], then FProp with bf16
@@ -476,7 +513,7 @@ def main():
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec32 = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec8, dec32 = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -513,6 +550,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "weight_update": upd,
+        "decode_8b": dec8,
         "decode_32b": dec32,
         "norm_quant": normq,
         "int8_w8a8": int8,
