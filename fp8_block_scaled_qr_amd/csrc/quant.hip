@@ -336,6 +336,23 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
             ++bi;
         }
     };
+    // The dual pass (rows and columns of one tile) holds too many registers to keep a second
+    // tile in flight and still fit three workgroups per CU: it loads each tile just before
+    // processing it, and the other resident workgroups cover the load latency (3 workgroups of
+    // 168 VGPRs with no prefetch beat 2 of 215 with prefetch: 33.8 against 36.7 us at
+    // 8192x4096, cache flushed).
+    if constexpr (MODE == (QMODE_ROW | QMODE_COL)) {
+        int64_t pi = first, bi = first / ngc, bj = first - bi * ngc;
+        int par = 0;
+        while (pi < pend) {
+            uint4 v[8];
+            prefetch(pi, bi, bj, v);
+            process(bi, bj, par, v);
+            par ^= 1;
+            advance(pi, bi, bj);
+        }
+        return;
+    }
     uint4 va[8], vb[8];
     int64_t pi = first, bi = first / ngc, bj = first - bi * ngc;
     int64_t np = pi, ni = bi, nj = bj;
@@ -367,7 +384,9 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
 // L2 before they are written back.  (The column pass keeps first(b) = b: with 128-column
 // tiles and a row of tiles a multiple of 8 long, a column band already stays on one XCD.)
 template <int MODE>
-__global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
+// At least 3 waves per SIMD (3 workgroups per CU): the register budget is 168 VGPRs, which
+// every mode meets without spilling.
+__global__ __launch_bounds__(256, 3) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ldx,
                                                     uint8_t *__restrict__ q,
                                                     float *__restrict__ s,
