@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kTile = 128;
 #ifndef QR_QUANT_WG_PER_CU
-#define QR_QUANT_WG_PER_CU 4
+#define QR_QUANT_WG_PER_CU 8
 #endif
 constexpr int kQuantWgPerCu = QR_QUANT_WG_PER_CU;   // resident workgroups per CU in the persistent grid
 
@@ -81,7 +81,7 @@ __device__ __forceinline__ void transpose8x8(const uint2 in[8], uint2 out[8])
 }
 
 // Barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its global
-// loads, so the next tile's prefetch stays in flight across it.
+// loads or stores.
 __device__ __forceinline__ void lds_barrier()
 {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -95,8 +95,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // The tile's eight 16-byte loads per thread as range-checked buffer loads: a row past `rows`
 // lies past the descriptor's extent and a column octet past `cols` takes an offset outside it,
-// so both read zeros without a branch (a branch around each load would make the compiler
-// wait for every outstanding load, the prefetch included, before the first use).
+// so both read zeros without a branch.
 __device__ __forceinline__ void load_tile(const uint16_t *__restrict__ x, int64_t rows,
                                           int64_t ldx, int64_t r0, int64_t col, bool colok,
                                           int oq, uint4 v[8])
@@ -116,9 +115,8 @@ __device__ __forceinline__ void load_tile(const uint16_t *__restrict__ x, int64_
     }
 }
 
-// The workgroup handles tiles first, first + stride, ... of x (row-major over the tile grid)
-// and prefetches the next tile's 32 KB into registers while it reduces, encodes and stores
-// the current one, so reads and writes overlap.  Every thread of the workgroup calls it.
+// The workgroup handles tiles first, first + stride, ... of x (row-major over the tile grid).
+// Every thread of the workgroup calls it.
 template <int MODE>
 __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int64_t rows,
                                             int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
@@ -313,21 +311,23 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
         }
     };
 
-    // Two register buffers in turn, so that the loads of one tile are always in flight while
-    // the other is processed (a copy between them at the end of each iteration would make the
-    // compiler wait for the new loads before the old data is used).
-    // Tile (bi, bj) is walked incrementally (no 64-bit division in the loop).  A tile past
-    // the end gets an empty descriptor (its loads return zeros without touching memory), so
-    // the loads are issued unconditionally and the compiler's wait counts stay exact.
-    // The walk visits linear tile indices first, first + stride, ... below pend (at most the
-    // tile count).
-    auto prefetch = [&](int64_t pi, int64_t bi, int64_t bj, uint4 (&v)[8]) {
-        const bool valid = pi < pend;
-        const int64_t c = bj * kTile + 8 * oc;
-        load_tile(x, valid ? rows : 0, ldx, valid ? bi * kTile : 0, c, c < cols, oq, v);
-    };
+    // One tile at a time: load it, then reduce, encode and store it.  The load latency is
+    // covered by the other workgroups resident on the CU, not by a second register buffer:
+    // without one every mode needs at most 168 VGPRs, so 3 to 8 workgroups fit per CU.  (A
+    // prefetch of the next tile into a second register set measured slower for every mode at
+    // 8192x4096: rows 25.1 against 23.0 us, columns 25.5 against 23.2, dual 36.7 against
+    // 33.6, weight blocks with the transposed copy 16.1 against 15.3.)
+    // Tile (bi, bj) is walked incrementally (no 64-bit division in the loop); the walk visits
+    // linear tile indices first, first + stride, ... below pend (at most the tile count).
     const int64_t dbi = stride / ngc, dbj = stride - dbi * ngc;
-    auto advance = [&](int64_t &pi, int64_t &bi, int64_t &bj) {
+    int64_t pi = first, bi = first / ngc, bj = first - bi * ngc;
+    int par = 0;
+    while (pi < pend) {
+        uint4 v[8];
+        const int64_t c = bj * kTile + 8 * oc;
+        load_tile(x, rows, ldx, bi * kTile, c, c < cols, oq, v);
+        process(bi, bj, par, v);
+        par ^= 1;
         pi += stride;
         bi += dbi;
         bj += dbj;
@@ -335,43 +335,6 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
             bj -= ngc;
             ++bi;
         }
-    };
-    // The dual pass (rows and columns of one tile) holds too many registers to keep a second
-    // tile in flight and still fit three workgroups per CU: it loads each tile just before
-    // processing it, and the other resident workgroups cover the load latency (3 workgroups of
-    // 168 VGPRs with no prefetch beat 2 of 215 with prefetch: 33.8 against 36.7 us at
-    // 8192x4096, cache flushed).
-    if constexpr (MODE == (QMODE_ROW | QMODE_COL)) {
-        int64_t pi = first, bi = first / ngc, bj = first - bi * ngc;
-        int par = 0;
-        while (pi < pend) {
-            uint4 v[8];
-            prefetch(pi, bi, bj, v);
-            process(bi, bj, par, v);
-            par ^= 1;
-            advance(pi, bi, bj);
-        }
-        return;
-    }
-    uint4 va[8], vb[8];
-    int64_t pi = first, bi = first / ngc, bj = first - bi * ngc;
-    int64_t np = pi, ni = bi, nj = bj;
-    prefetch(pi, bi, bj, va);
-    while (pi < pend) {
-        advance(np, ni, nj);
-        prefetch(np, ni, nj, vb);
-        process(bi, bj, 0, va);
-        pi = np;
-        bi = ni;
-        bj = nj;
-        if (pi >= pend)
-            break;
-        advance(np, ni, nj);
-        prefetch(np, ni, nj, va);
-        process(bi, bj, 1, vb);
-        pi = np;
-        bi = ni;
-        bj = nj;
     }
 }
 
