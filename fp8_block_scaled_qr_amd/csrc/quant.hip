@@ -29,6 +29,10 @@ constexpr int kTile = 128;
 #define QR_QUANT_WG_PER_CU 8
 #endif
 constexpr int kQuantWgPerCu = QR_QUANT_WG_PER_CU;   // resident workgroups per CU in the persistent grid
+#ifndef QR_SMALL_ROWS
+#define QR_SMALL_ROWS 256
+#endif
+constexpr int64_t kSmallRows = QR_SMALL_ROWS;   // row-group pass: up to this many rows, one wave per row slice
 
 __device__ __forceinline__ uint32_t absmax8(const uint4 &v)
 {
@@ -387,6 +391,33 @@ __global__ __launch_bounds__(256) void k_quant_w_batch(WeightTable tab)
     }
 }
 
+// 1x128 row groups of a few rows (decode activations): one wave per row and 512-column slice,
+// lanes 16 t .. 16 t + 15 on group t of the slice (8 columns each), so a 64 x 4096 activation
+// takes 512 waves instead of 32 half-empty 128-row tiles.  Same maxima, scales and encoder as
+// the tile kernel's row mode (the lifted quotient only for groups with a tiny scale; for the
+// others it is the same quotient).
+__global__ __launch_bounds__(256) void k_quant_rows_small(const uint16_t *__restrict__ x,
+                                                          int64_t rows, int64_t cols,
+                                                          int64_t ldx, uint8_t *__restrict__ q,
+                                                          float *__restrict__ s)
+{
+    const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
+    const int64_t ngc = (cols + kTile - 1) / kTile, nslice = (ngc + 3) / 4;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = wid / nslice, sl = wid - row * nslice;
+    if (row >= rows)
+        return;   // the whole wave; no barrier follows
+    const int64_t g = 4 * sl + sub, c = g * kTile + 8 * li;
+    const bool ok = c < cols;   // cols % 8 == 0: an octet is all in or out
+    const uint4 v = ok ? *reinterpret_cast<const uint4 *>(x + row * ldx + c) : make_uint4(0, 0, 0, 0);
+    const Scale sc = make_scale(row16_max(absmax8(v)));   // all 64 lanes take part
+    const uint2 c8 = tiny_scale(sc) ? encode8<true>(v, sc) : encode8<false>(v, sc);
+    if (ok)
+        *reinterpret_cast<uint2 *>(q + row * cols + c) = c8;
+    if (li == 0 && g < ngc)
+        s[row * ngc + g] = sc.s;
+}
+
 // ---------------------------------------------------------------- RMSNorm + 1x128 quantize
 
 __device__ __forceinline__ float sumsq8(const uint4 &v, float ss)
@@ -703,6 +734,12 @@ hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t 
     const int64_t nt = ngr * ngc;
     switch (mode) {
     case QMODE_ROW:
+        if (rows <= kSmallRows) {
+            const int64_t waves = rows * ((ngc + 3) / 4);
+            k_quant_rows_small<<<(unsigned)((waves + 3) / 4), 256, 0, stream>>>(x, rows, cols,
+                                                                               ld_x, q, s);
+            return hipGetLastError();
+        }
         return launch_mode<QMODE_ROW>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
     case QMODE_COL:
         return launch_mode<QMODE_COL>(x, rows, cols, ld_x, q, s, qT, sT, nt, stream);
