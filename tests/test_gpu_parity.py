@@ -313,6 +313,11 @@ def test_quant_strided_input():
     assert_bitexact(host(s), rs, "scales")
     assert_bitexact(host(qT), rqT, "colT codes")
     assert_bitexact(host(sT), rsT, "colT scales")
+    # rows only: 96 rows take the few-rows kernel (one wave per 512-column slice; the slice
+    # holds 3 of its 4 groups here)
+    q1, s1, _, _ = qr.quant_act(xd, row=True, col=False)
+    assert_bitexact(host(q1), rq, "codes, few-rows kernel")
+    assert_bitexact(host(s1), rs, "scales, few-rows kernel")
 
 
 def _groups_for_amax(amax_bits_list):
@@ -367,6 +372,10 @@ def test_quant_special_values():
     assert_bitexact(host(s), rs, "scales")
     assert_bitexact(host(qT), rqT, "colT codes")
     assert_bitexact(host(sT), rsT, "colT scales")
+    # rows only (16 rows: the few-rows kernel, incl. its lifted quotient for tiny scales)
+    q1, s1, _, _ = qr.quant_act(dev_bf16(x), row=True, col=False)
+    assert_bitexact(host(q1), rq, "codes, few-rows kernel")
+    assert_bitexact(host(s1), rs, "scales, few-rows kernel")
     w = np.ascontiguousarray(np.tile(x, (8, 1))[:128])
     qw, sw, _, _ = qr.quant_w(dev_bf16(w))
     rqw, rsw = oracle.quant_blocks(w)
