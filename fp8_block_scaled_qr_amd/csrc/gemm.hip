@@ -66,8 +66,6 @@ struct GemmArgs {
     int split, kgps;    // number of K splits, groups per split
 };
 
-constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past every descriptor's extent
-
 // The promotion of a unit's partial sum runs QR_PROMOTE_LAG MFMAs after the MFMA that made it,
 // so the VALU never waits on the MFMA result.
 #ifndef QR_PROMOTE_LAG
@@ -443,7 +441,6 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 template <int MT, int NW, int KS, int D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
 {
-    constexpr int THREADS = 64 * NW * KS;
     constexpr int KTHREADS = 64 * NW;                         // threads of one K split
     constexpr int AROWS = 16 * MT;
     constexpr int ACHUNKS = AROWS * 8;                        // 16-byte chunks per A group
