@@ -947,13 +947,10 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t nk = K / kGroup;
     int64_t split = 1;
-#ifndef QR_SKINNY_SPLIT
-#define QR_SKINNY_SPLIT 1
-#endif
     // Decode batches on narrow weights: fewer than half of the CUs would get a workgroup, so
     // K is split across workgroups as well (at least 8 groups each, so the load ring stays
     // full; the fp32 partials are small at M <= 64).  A 64x4096x4096 product gets 4 splits.
-    if (QR_SKINNY_SPLIT && p.cfg == CFG_SKINNY && tiles > 0 && tiles <= kCUs / 2 && nk >= 16) {
+    if (p.cfg == CFG_SKINNY && tiles > 0 && tiles <= kCUs / 2 && nk >= 16) {
         split = kCUs / tiles;
         if (split > nk / 8)
             split = nk / 8;
