@@ -603,12 +603,18 @@ def test_decode_32b_set_sampled(idx):
     print(_fprop_case(lin, x, rwf, qr.QR_OUT_BF16, smp, lin.name))
 
 
-def test_gemm_deterministic():
-    say("determinism")
-    lin = qr_synth.decode_8b()
-    x, w = lin.x(), lin.w()
+@pytest.mark.parametrize("M,N,K", [(64, 14336, 4096),    # decode, no split
+                                   (64, 4096, 14336),    # decode, K split across workgroups
+                                   (256, 7168, 5120),    # 256x256 tiles, 8 K splits
+                                   (200, 640, 1024)])    # ragged M, 3 tiles x 8 K splits
+def test_gemm_deterministic(M, N, K):
+    """Repeated calls give bit-identical outputs, also where K is split (the partial sums
+    are added in split order, never in arrival order)."""
+    say("determinism", M, N, K)
+    x = qr_synth.normal_bf16(M + 2 * K, (M, K), 1.0, 13, max(1, K // 100))
+    w = qr_synth.normal_bf16(N + 3 * K, (N, K), 0.02)
     qa, sa, _, _ = qr.quant_act(dev_bf16(x), row=True)
     qw, sw, _, _ = qr.quant_w(dev_bf16(w))
-    y1 = host(qr.gemm_fprop(qa, sa, qw, sw))
-    y2 = host(qr.gemm_fprop(qa, sa, qw, sw))
-    assert np.array_equal(y1, y2)
+    for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
+        ys = [host(qr.gemm_fprop(qa, sa, qw, sw, out_dtype=out)) for _ in range(3)]
+        assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2]), (M, N, K, out)
