@@ -292,7 +292,8 @@ def _median_us(torch, f, iters, flush=True):
 
 def run_int8(torch, qr, st, iters=20):
     """The INT8 W8A8 variant at the same shapes: the per-token quantize of X [8192, 4096], the
-    prefill GEMM 8192x4096x4096 and the decode GEMM 64x14336x4096 (bf16 out)."""
+    prefill GEMM 8192x4096x4096 and the decode GEMM 64x14336x4096 (bf16 out), then the 32B
+    layer's four linears at decode batch 256."""
     dev = "cuda:0"
     e = lambda *sh, dt: torch.empty(sh, dtype=dt, device=dev)
     i8, f32, bf = torch.int8, torch.float32, torch.bfloat16
@@ -323,6 +324,43 @@ def run_int8(torch, qr, st, iters=20):
     out["gemm_decode"] = {"shape": [MD, F, H], "us": round(us, 2), "bound": "hbm", "bytes": nb,
                           "achieved": round(nb / us / 1e3, 1), "unit": "GB/s",
                           "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del qwd, swd, qxd, sxd, yd
+    out["layer_32b_batch256"] = run_int8_32b(torch, qr, iters)
+    return out
+
+
+def run_int8_32b(torch, qr, iters):
+    """The 32B decoder layer's four linears at decode batch 256 in INT8 W8A8 (random codes
+    and positive scales; the GEMM's time does not depend on the values), bf16 out, each after
+    a cache-evicting read.  Algorithmic bytes = weight codes and scales + activation codes and
+    scales + bf16 Y."""
+    dev = "cuda:0"
+    M = 256
+    shapes = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 55296, 5120),
+              ("down", 5120, 27648)]
+    gen = torch.Generator(device=dev).manual_seed(6301)
+    out, tot_us, tot_b = {}, 0.0, 0
+    for name, n, k in shapes:
+        qw = torch.randint(-127, 127, (n, k), dtype=torch.int8, device=dev, generator=gen)
+        sw = torch.rand((n,), device=dev, generator=gen) * 1e-3 + 1e-4
+        qx = torch.randint(-127, 127, (M, k), dtype=torch.int8, device=dev, generator=gen)
+        sx = torch.rand((M,), device=dev, generator=gen) * 1e-2 + 1e-3
+        y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        nb = qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, M, n, k)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        us = _median_us(torch, lambda: qr.qr_gemm_int8_w8a8(qx, sx, qw, sw, M, n, k, y,
+                                                           qr.QR_OUT_BF16, ws, nb), iters)
+        by = n * k + n * 4 + M * k + M * 4 + M * n * 2
+        gbs = by / (us * 1e-6) / 1e9
+        out[name] = {"shape": [M, n, k], "us": round(us, 2), "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "k_splits": nb // (M * n * 4) if nb else 1}
+        tot_us, tot_b = tot_us + us, tot_b + by
+        del qw, sw, qx, sx, y, ws
+    out["layer"] = {"us": round(tot_us, 1), "gbs": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["workload"] = ("32B decoder layer at decode batch 256, INT8 W8A8: QKV 5120->7168, "
+                       "O 5120->5120, gate+up 5120->55296, down 27648->5120")
     return out
 
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libqr.so")
 QR_OK = 0
 QR_OUT_F32 = 0
 QR_OUT_BF16 = 1
-QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD = 0, 1, 2
+QR_GEMM_FPROP, QR_GEMM_DGRAD, QR_GEMM_WGRAD, QR_GEMM_INT8 = 0, 1, 2, 3
 
 # Every entry point include/qr.h declares.
 EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant_w_128x128",
@@ -70,7 +70,7 @@ def load():
     L.qr_rmsnorm_quant_1x128.restype = I32
     L.qr_quant_int8_rowwise.argtypes = [P, I64, I64, I64, P, P, P]
     L.qr_quant_int8_rowwise.restype = I32
-    L.qr_gemm_int8_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+    L.qr_gemm_int8_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
     L.qr_gemm_int8_w8a8.restype = I32
     L.qr_quant_w_nvfp4.argtypes = [P, I64, I64, I64, P, P, P, P, SZ, P]
     L.qr_quant_w_nvfp4.restype = I32
@@ -155,9 +155,8 @@ def qr_quant_int8_rowwise(x, rows, cols, ld_x, q, s, stream=None):
                                         _stream(stream)), "qr_quant_int8_rowwise")
 
 
-def qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, y_dtype, stream=None):
-    _check(load().qr_gemm_int8_w8a8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(y),
-                                    int(y_dtype), _stream(stream)), "qr_gemm_int8_w8a8")
+def qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, y_dtype, ws=None, ws_bytes=0, stream=None):
+    _gemm("qr_gemm_int8_w8a8", a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream)
 
 
 def qr_quant_w_nvfp4(w, n, k, ld_w, codes, bscale, tscale, ws, ws_bytes, stream=None):
@@ -285,7 +284,8 @@ def gemm_int8(a, sa, b, sb, out_dtype=QR_OUT_BF16, stream=None):
     M, K = a.shape
     N = b.shape[0]
     y = _out(M, N, out_dtype, a.device)
-    qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, out_dtype, stream)
+    ws, nb = _workspace(QR_GEMM_INT8, M, N, K, a.device)
+    qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, out_dtype, ws, nb, stream)
     return y
 
 

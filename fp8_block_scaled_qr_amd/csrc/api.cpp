@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -240,7 +240,7 @@ qr_status qr_quant_int8_rowwise(const void *x_bf16, int64_t rows, int64_t cols, 
 
 qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, const float *sb,
                             int64_t M, int64_t N, int64_t K, void *y, qr_out_dtype y_dtype,
-                            qr_stream stream)
+                            void *workspace, size_t workspace_bytes, qr_stream stream)
 {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
         return QR_ERR_SHAPE;
@@ -255,15 +255,25 @@ qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, c
     if (misaligned(a, 16) || misaligned(b, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
         misaligned(sb, 4))
         return QR_ERR_ALIGN;
+    const qr::GemmPlan plan = qr::plan_gemm_i8(M, N, K);
+    if (plan.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.ws_bytes)
+            return QR_ERR_WORKSPACE;
+        if (misaligned(workspace, 16))
+            return QR_ERR_ALIGN;
+    }
     const int64_t esz = y_dtype == QR_OUT_BF16 ? 2 : 4;
     const Range ry = span(y, M * N * esz);
+    const Range rw = span(workspace, plan.ws_bytes > 0 ? (int64_t)plan.ws_bytes : 0);
     const Range ins[4] = {span(a, M * K), span(sa, M * 4), span(b, N * K), span(sb, N * 4)};
     for (const Range &r : ins)
-        if (overlap(ry, r))
+        if (overlap(ry, r) || overlap(rw, r))
             return QR_ERR_ALIAS;
+    if (overlap(ry, rw))
+        return QR_ERR_ALIAS;
     // K == 0 (empty contraction) runs the same kernel: no step executes and zeros are stored
     return launch_status(qr::launch_gemm_i8(y_dtype == QR_OUT_BF16, a, sa, b, sb, M, N, K, y,
-                                            (hipStream_t)stream));
+                                            workspace, plan, (hipStream_t)stream));
 }
 
 qr_status qr_quant_w_nvfp4(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, uint8_t *codes,
@@ -447,6 +457,8 @@ size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K)
         return N % 128 || M == 0 || K == 0 || N == 0 ? 0 : qr::plan_gemm(qr::BSCALE_BLOCK, M, K, N).ws_bytes;
     case QR_GEMM_WGRAD:
         return M % 128 || N == 0 || K == 0 || M == 0 ? 0 : qr::plan_gemm(qr::BSCALE_ROW, N, K, M).ws_bytes;
+    case QR_GEMM_INT8:
+        return K % 128 || K > 131072 || M == 0 || N == 0 || K == 0 ? 0 : qr::plan_gemm_i8(M, N, K).ws_bytes;
     default:
         return 0;
     }

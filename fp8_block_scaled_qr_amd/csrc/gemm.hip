@@ -678,10 +678,11 @@ struct GemmI8Args {
     const float *sa;     // [M]
     const int8_t *B;     // [N, K]
     const float *sb;     // [N]
-    void *C;             // [M, N], fp32 or bf16
+    void *C;             // [M, N], fp32 or bf16; with split > 1 the int32 partials [split][M][N]
     int64_t M, N, K;
     int nk;              // K / 128
     int tilesM, tilesN;
+    int split, kgps;     // K splits across workgroups, groups per split
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -711,11 +712,13 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
     const int nb = gridDim.x;
     if ((nb & 7) == 0)
         bid = (bid & 7) * (nb >> 3) + (bid >> 3);   // a contiguous run of tiles per XCD
+    const int tiles = g.tilesM * g.tilesN;
+    const int split = bid / tiles;
     int tm, tn;
-    tile_of(bid, g.tilesM, g.tilesN, tm, tn);
+    tile_of(bid - split * tiles, g.tilesM, g.tilesN, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
     const int64_t M = g.M, N = g.N, K = g.K;
-    const int nk = g.nk;
+    const int gb = split * g.kgps, ge = min(g.nk, gb + g.kgps);   // this split's K groups
 
     auto swz = [](int row) { return (row & 7) ^ ((row >> 3) & 1); };
     const int frow = lane & 15, fq = lane >> 4;
@@ -789,14 +792,14 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
 
     // main loop: as the FP8 GEMM's (step k issues step k+1's loads into the other stage,
     // computes, waits for its own loads, then the barrier publishes the stage)
-    const int glast = nk - 1;
-    if (nk > 0)
-        issue_step(0, 0);
+    const int glast = ge - 1;
+    if (gb < ge)
+        issue_step(gb, 0);
     vm_wait<0>();
     stage_barrier();
 #pragma nounroll
-    for (int kg = 0; kg < nk; ++kg) {
-        const int st = kg & 1;
+    for (int kg = gb; kg < ge; ++kg) {
+        const int st = (kg - gb) & 1;
         issue_step(min(kg + 1, glast), st ^ 1);
         compute(smA[st], smB[st]);
         vm_wait<0>();
@@ -805,6 +808,29 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
 
     // epilogue: lane holds C[m][n .. n + 3] of each sub-tile
     const bool vec_ok = (N & 3) == 0;
+    if (g.split > 1) {
+        // this split's exact int32 partial sums; the scales are applied once, after the sum
+#pragma unroll
+        for (int i = 0; i < T::IM; ++i) {
+            const int64_t m = m0 + wm * T::TM + i * 16 + lr;
+            if (m >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < T::JN; ++j) {
+                const int64_t n = n0 + wn * T::TN + j * 16 + 4 * lq;
+                int32_t *c = reinterpret_cast<int32_t *>(g.C) + (int64_t)split * M * N + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    *reinterpret_cast<v4i *>(c) = acc[i][j];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            c[r] = acc[i][j][r];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < T::IM; ++i) {
         const int64_t m = m0 + wm * T::TM + i * 16 + lr;
@@ -843,6 +869,52 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
                 }
             }
         }
+    }
+}
+
+// Sum the INT8 GEMM's int32 K-split partials in split order (exact) and apply the row scales as
+// the unsplit epilogue does, so the output is the same as without the split.  Each thread takes
+// four adjacent outputs of one row when N % 4 == 0, else one.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_splitk_reduce_i8(const int32_t *__restrict__ ws,
+                                                          int64_t M, int64_t N, int split,
+                                                          const float *__restrict__ sa,
+                                                          const float *__restrict__ sb, void *out)
+{
+    const int64_t MN = M * N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if ((N & 3) == 0) {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN / 4; i += stride) {
+            v4i t = reinterpret_cast<const v4i *>(ws)[i];
+            for (int p = 1; p < split; ++p)
+                t += reinterpret_cast<const v4i *>(ws + p * MN)[i];
+            const int64_t m = (4 * i) / N, n = 4 * i - m * N;
+            const float am = sa[m];
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[r] = (float)t[r] * (am * sb[n + r]);
+            if (OUT_BF16) {
+                uint2 o;
+                o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+                o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+                reinterpret_cast<uint2 *>(out)[i] = o;
+            } else {
+                reinterpret_cast<float4 *>(out)[i] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        return;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+        int32_t t = ws[i];
+        for (int p = 1; p < split; ++p)
+            t += ws[p * MN + i];
+        const int64_t m = i / N, n = i - m * N;
+        const float v = (float)t * (sa[m] * sb[n]);
+        if (OUT_BF16)
+            reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)f32_to_bf16(v);
+        else
+            reinterpret_cast<float *>(out)[i] = v;
     }
 }
 
@@ -1033,30 +1105,61 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     return hipGetLastError();
 }
 
+// INT8 plan: cfg 1 = 256x256 tiles, 0 = 64x32 tiles.  256x256 tiles when they give at least
+// half of the CUs a workgroup (prefill and training sizes, and wide weights at decode batches
+// up to 256: 256x55296x5120 runs in 110 us instead of 225 on 64x32 tiles).  Below that, M > 64
+// still takes 256x256 tiles (each weight panel is read once for all rows) with K split across
+// workgroups so that the tiles' splits make one wave of at most one workgroup per CU, as the
+// FP8 plan does; M <= 64 takes 64x32 tiles, which fill the chip at any width, and splits K only
+// when even those leave half of the CUs idle (at least 8 groups per split).
+GemmPlan plan_gemm_i8(int64_t M, int64_t N, int64_t K)
+{
+    GemmPlan p;
+    const int64_t nk = K / kGroup;
+    const int64_t big_tiles = ((M + CfgBig4::BM - 1) / CfgBig4::BM) * ((N + CfgBig4::BN - 1) / CfgBig4::BN);
+    const int64_t small_tiles = ((M + CfgI8Small::BM - 1) / CfgI8Small::BM) *
+                                ((N + CfgI8Small::BN - 1) / CfgI8Small::BN);
+    p.cfg = big_tiles >= kCUs / 2 || M > 64 ? 1 : 0;
+    int64_t split = 1;
+    if (p.cfg == 1 && big_tiles > 0 && big_tiles < kCUs / 2 && nk > 1) {
+        split = kCUs / big_tiles;
+        if (split > nk)
+            split = nk;
+    } else if (p.cfg == 0 && small_tiles > 0 && small_tiles <= kCUs / 2 && nk >= 16) {
+        split = kCUs / small_tiles;
+        if (split > nk / 8)
+            split = nk / 8;
+    }
+    if (split > 1) {
+        const int64_t kgps = (nk + split - 1) / split;
+        split = (nk + kgps - 1) / kgps;
+    }
+    p.split = (int)split;
+    p.ws_bytes = split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+    return p;
+}
+
 hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const int8_t *B,
-                          const float *sb, int64_t M, int64_t N, int64_t K, void *C,
-                          hipStream_t stream)
+                          const float *sb, int64_t M, int64_t N, int64_t K, void *C, void *ws,
+                          const GemmPlan &plan, hipStream_t stream)
 {
     GemmI8Args a;
     a.A = A;
     a.sa = sa;
     a.B = B;
     a.sb = sb;
-    a.C = C;
+    a.C = plan.split > 1 ? ws : C;
     a.M = M;
     a.N = N;
     a.K = K;
     a.nk = (int)(K / kGroup);
-    // 256x256 tiles when they give at least half of the CUs a workgroup (prefill and training
-    // sizes, and wide weights at decode batches up to 256: 256x55296x5120 runs in 110 us
-    // instead of 225 on 64x32 tiles), else 64x32 tiles, which fill the chip at any M (this
-    // entry point takes no workspace, so there is no K split)
-    const int64_t big_tiles = ((M + CfgBig4::BM - 1) / CfgBig4::BM) * ((N + CfgBig4::BN - 1) / CfgBig4::BN);
-    const bool big = big_tiles >= 128;
+    a.split = plan.split;
+    a.kgps = (a.nk + plan.split - 1) / plan.split;
+    const bool big = plan.cfg == 1;
     const int bm = big ? CfgBig4::BM : CfgI8Small::BM, bn = big ? CfgBig4::BN : CfgI8Small::BN;
     a.tilesM = (int)((M + bm - 1) / bm);
     a.tilesN = (int)((N + bn - 1) / bn);
-    const unsigned blocks = (unsigned)(a.tilesM * a.tilesN);
+    const unsigned blocks = (unsigned)(a.tilesM * a.tilesN * plan.split);
     if (big) {
         if (out_bf16)
             k_gemm_i8<CfgBig4, true><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
@@ -1068,6 +1171,20 @@ hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const
         else
             k_gemm_i8<CfgI8Small, false><<<blocks, CfgI8Small::THREADS, 0, stream>>>(a);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.split <= 1)
+        return e;
+    const int64_t MN = M * N;
+    int64_t rb = (((N & 3) == 0 ? MN / 4 : MN) + 255) / 256;
+    if (rb > 8192)
+        rb = 8192;
+    if (rb < 1)
+        rb = 1;
+    const int32_t *wsi = static_cast<const int32_t *>(ws);
+    if (out_bf16)
+        k_splitk_reduce_i8<true><<<(unsigned)rb, 256, 0, stream>>>(wsi, M, N, plan.split, sa, sb, C);
+    else
+        k_splitk_reduce_i8<false><<<(unsigned)rb, 256, 0, stream>>>(wsi, M, N, plan.split, sa, sb, C);
     return hipGetLastError();
 }
 

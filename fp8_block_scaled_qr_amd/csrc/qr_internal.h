@@ -55,10 +55,19 @@ hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w
                            const float *s, uint16_t *w_out, int64_t ld_out, float *gain,
                            hipStream_t stream);
 
+// A GEMM's launch plan.
+struct GemmPlan {
+    int cfg;        // tile configuration index
+    int split;      // number of K splits (1 = none)
+    size_t ws_bytes;
+};
+
 // INT8 W8A8: C[m, n] = sa[m] * sb[n] * sum_k A[m, k] B[n, k] (int8 codes, K % 128 == 0).
+// With plan.split > 1, ws holds the int32 partials [split][M][N] (plan.ws_bytes).
+GemmPlan plan_gemm_i8(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const int8_t *B,
-                          const float *sb, int64_t M, int64_t N, int64_t K, void *C,
-                          hipStream_t stream);
+                          const float *sb, int64_t M, int64_t N, int64_t K, void *C, void *ws,
+                          const GemmPlan &plan, hipStream_t stream);
 
 // 4-bit weights: w [n, k] (ld) -> codes [n, k/2], E4M3 block scales [n, k/16], tensor scale;
 // partial: kNvfp4Partials words of scratch (the first pass's maxima).
@@ -79,12 +88,6 @@ hipError_t launch_quant_int8_rows(const uint16_t *x, int64_t rows, int64_t cols,
 enum : int {
     BSCALE_BLOCK = 0,  // sb [ceil(N/128), K/128]: one scale per 128x128 block of B
     BSCALE_ROW = 1,    // sb [N, K/128]: one scale per row of B and 128-group of K
-};
-
-struct GemmPlan {
-    int cfg;        // tile configuration index
-    int split;      // number of K splits (1 = none)
-    size_t ws_bytes;
 };
 
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K);

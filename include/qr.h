@@ -75,7 +75,12 @@ enum {
 
 typedef enum { QR_OUT_F32 = 0, QR_OUT_BF16 = 1 } qr_out_dtype;
 
-typedef enum { QR_GEMM_FPROP = 0, QR_GEMM_DGRAD = 1, QR_GEMM_WGRAD = 2 } qr_gemm_kind;
+typedef enum {
+    QR_GEMM_FPROP = 0,   /* qr_gemm_fp8_bsfprop   */
+    QR_GEMM_DGRAD = 1,   /* qr_gemm_fp8_bsdgrad   */
+    QR_GEMM_WGRAD = 2,   /* qr_gemm_fp8_bswgrad   */
+    QR_GEMM_INT8 = 3     /* qr_gemm_int8_w8a8     */
+} qr_gemm_kind;
 
 typedef void *qr_stream; /* hipStream_t */
 
@@ -158,12 +163,16 @@ qr_status qr_quant_int8_rowwise(const void *x_bf16, int64_t rows, int64_t cols, 
  *   a  int8 [M, K] with sa [M] (qr_quant_int8_rowwise of the activation)
  *   b  int8 [N, K] with sb [N] (qr_quant_int8_rowwise of the weight W[N, K])
  *   y  [M, N], fp32 or bf16 per y_dtype.
- * Size rules: M, N >= 0; K % 128 == 0 and K <= 131072 (the sum stays within int32).  a, b, y
- * 16-byte aligned, sa, sb 4-byte aligned; y must not overlap an input.  No workspace.
+ * workspace: device scratch of at least qr_gemm_workspace_bytes(QR_GEMM_INT8, M, N, K) bytes
+ *   (may be NULL when that is 0); it then holds the splits' exact int32 partial sums, which
+ *   are added before the scaling, so the result is the same as without a split.
+ * Size rules: M, N >= 0; K % 128 == 0 and K <= 131072 (the sum stays within int32).  a, b, y,
+ * workspace 16-byte aligned, sa, sb 4-byte aligned; neither y nor the workspace may overlap an
+ * input or each other.
  */
 qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, const float *sb,
                             int64_t M, int64_t N, int64_t K, void *y, qr_out_dtype y_dtype,
-                            qr_stream stream);
+                            void *workspace, size_t workspace_bytes, qr_stream stream);
 
 /*
  * Norm and activation quantize in one pass (the producer of the FProp operand).  The norm in
@@ -275,8 +284,8 @@ qr_status qr_gemm_fp8_bswgrad(const uint8_t *dyT, const float *sdyT, const uint8
  * sizes are the ones passed to that entry point.  Returns 0 for invalid arguments.
  * It is non-zero when the product is split over its contraction to occupy the GPU: up to
  * 256 output rows (decode batches) against a narrow weight, or few 256x256 output tiles.  The
- * splits' fp32 partial sums [split][rows][cols] are then added in split order, so results do
- * not depend on timing. */
+ * splits' partial sums [split][rows][cols] (fp32; int32 for QR_GEMM_INT8) are then added in
+ * split order, so results do not depend on timing. */
 size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 /*

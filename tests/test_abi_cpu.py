@@ -44,7 +44,7 @@ def test_exports_match_header(L):
 
 
 def test_status_strings_and_version(L):
-    assert qr.abi_version() == 1
+    assert qr.abi_version() == 2
     for st in range(8):
         assert qr.status_string(st)
     assert "unknown" in qr.status_string(99)
@@ -116,13 +116,20 @@ def test_int8_validation(L):
     assert f(A, 4, 128, 128, B, B + 256, None) == ALIAS                  # scales over codes
     assert f(A, 0, 128, 128, B, C, None) == OK
     g = L.qr_gemm_int8_w8a8
-    assert g(A, B, C, D, 64, 64, 100, E, 1, None) == SHAPE               # K % 128
-    assert g(A, B, C, D, 64, 64, 131072 + 128, E, 1, None) == SHAPE      # int32 range
-    assert g(A, B, C, D, 64, 64, 128, E, 7, None) == ARG                 # output dtype
-    assert g(None, B, C, D, 64, 64, 128, E, 1, None) == NULL
-    assert g(A, B, C + 4, D, 64, 64, 128, E, 1, None) == ALIGN
-    assert g(A, B, C, D, 64, 64, 128, A + 1024, 1, None) == ALIAS        # y over a
-    assert g(A, B, C, D, 0, 64, 128, E, 1, None) == OK
+    assert g(A, B, C, D, 64, 64, 100, E, 1, None, 0, None) == SHAPE               # K % 128
+    assert g(A, B, C, D, 64, 64, 131072 + 128, E, 1, None, 0, None) == SHAPE      # int32 range
+    assert g(A, B, C, D, 64, 64, 128, E, 7, None, 0, None) == ARG                 # output dtype
+    assert g(None, B, C, D, 64, 64, 128, E, 1, None, 0, None) == NULL
+    assert g(A, B, C + 4, D, 64, 64, 128, E, 1, None, 0, None) == ALIGN
+    assert g(A, B, C, D, 64, 64, 128, A + 1024, 1, None, 0, None) == ALIAS        # y over a
+    assert g(A, B, C, D, 0, 64, 128, E, 1, None, 0, None) == OK
+    # a split product (few 256x256 tiles) needs the workspace for its int32 partials
+    W, nb = 6 << 40, qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 256, 5120, 27648)
+    assert g(A, B, C, D, 256, 5120, 27648, E, 1, None, 0, None) == WORKSPACE
+    assert g(A, B, C, D, 256, 5120, 27648, E, 1, W, nb - 1, None) == WORKSPACE
+    assert g(A, B, C, D, 256, 5120, 27648, E, 1, W + 8, nb, None) == ALIGN
+    assert g(A, B, C, D, 256, 5120, 27648, E, 1, C + 4096, nb, None) == ALIAS     # ws over b
+    assert g(A, B, C, D, 256, 5120, 27648, E, 1, E + 4096, nb, None) == ALIAS     # ws over y
 
 
 def test_fp4_validation(L):
@@ -224,6 +231,13 @@ def test_gemm_workspace(L):
     # DGrad / WGrad sizes are passed as given to their entry points
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_DGRAD, 200, 4096, 14336) > 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_WGRAD, 8192, 4096, 4096) == 0
+    # INT8: int32 partials; 256 rows against a 5120-wide weight give 20 tiles x 12 splits, a
+    # 64-row batch against a 4096-wide one 128 narrow tiles x 2 splits
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 256, 5120, 27648) == 12 * 256 * 5120 * 4
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 4096, 14336) == 2 * 64 * 4096 * 4
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 14336, 4096) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 8192, 4096, 4096) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 64, 131072 + 128) == 0  # invalid K
 
 
 def test_uaq_validation(L):

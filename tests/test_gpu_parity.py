@@ -203,22 +203,39 @@ def _check_int8(y, Y, out):
     assert np.all(err <= rel * np.abs(Y)), float(np.max(err / np.maximum(np.abs(Y), 1e-300)))
 
 
+def _int8_scaled_exact(qa, sa, qb, sb):
+    """The entry point's definition in binary32: float(exact integer sum) * (sa[m] * sb[n])."""
+    S = qa.astype(np.int64) @ qb.astype(np.int64).T
+    assert np.abs(S).max(initial=0) < 2 ** 31
+    scale = sa.astype(np.float32)[:, None] * sb.astype(np.float32)[None, :]
+    return S.astype(np.float32) * scale
+
+
+# (77, 200, 384), (300, 264, 256), (520, 304, 384): 256x256 tiles with K split 3, 2, 3 ways;
+# (64, 512, 4096) and (40, 1000, 2304): 64x32 tiles split 4 and 2 ways; the rest unsplit
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (64, 1000, 1024), (1, 128, 128),
-                                   (300, 264, 256), (520, 304, 384), (17, 72, 640)])
+                                   (300, 264, 256), (520, 304, 384), (17, 72, 640),
+                                   (64, 512, 4096), (40, 1000, 2304)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_gemm_int8(M, N, K, out):
     say("gemm_int8", M, N, K, out)
     qa, sa, qb, sb = _int8_case(M, N, K, M + N + K)
     y = qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=out)
     _check_int8(out_f64(y), oracle.gemm_int8(qa, sa, qb, sb), out)
+    if out == qr.QR_OUT_F32:
+        # split or not, the integer sum is exact and scaled once: equal bits
+        assert np.array_equal(y.cpu().numpy(), _int8_scaled_exact(qa, sa, qb, sb))
 
 
 @pytest.mark.parametrize("M,N,K", [(8192, 4096, 4096), (64, 14336, 4096), (256, 5120, 27648),
-                                   (256, 55296, 5120), (200, 32768, 256)])
+                                   (256, 55296, 5120), (200, 32768, 256), (256, 7168, 5120),
+                                   (64, 4096, 14336)])
 def test_gemm_int8_full_size_sampled(M, N, K):
-    """The 8B prefill shape, the 8B decode shape, the 32B down and gate+up projections at
-    batch 256, and a ragged-M batch on the 256x256 tiles (128 tiles, the smallest count that
-    takes them), on sampled outputs (every tile and both ragged ends hit)."""
+    """The 8B prefill shape, the 8B decode shape, the 32B down (K split 12 ways) and gate+up
+    projections at batch 256, a ragged-M batch on the 256x256 tiles (128 tiles, the smallest
+    count that takes them without a split), the 32B QKV at batch 256 (split 8 ways) and the 8B
+    down at batch 64 (narrow tiles, split 2 ways), on sampled outputs (every tile and both
+    ragged ends hit)."""
     say("gemm_int8 full", M, N, K)
     qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
     y = out_f64(qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_BF16))
