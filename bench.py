@@ -4,8 +4,9 @@
 One step is one pass of the whole linear-layer path over one batch of seeded synthetic
 input, at the 8B-layer shapes (hidden 4096, 8192 tokens; decode FFN 14336 at batch 64):
 
-  uaq_fold        W [4096, 4096] / s (per input column), gain * s        (one-time op; timed)
-  quant_w         128x128 blocks of the folded W, plus the transposed copy for DGrad
+  fold_quant_w    W' = W [4096, 4096] / s (per input column), gain * s, and the 128x128
+                  blocks of W' plus the transposed copy for DGrad, in one pass over W
+                  (the fold is a one-time op; timed)
   quant_x_dual    1x128 rows of X [8192, 4096] for FProp and its 128x1 columns (transposed)
                   for WGrad, one read (X is the norm output carrying s); the column codes are
                   the FP8 activations kept for the backward
@@ -62,10 +63,8 @@ def op_table():
     """Algorithmic work of each op: ('mfma', flops) or ('hbm', bytes), minimum traffic."""
     g = 128
     return {
-        # read W bf16 + s + gain, write W' bf16 + gain
-        "uaq_fold": ("hbm", H * H * 2 * 2 + H * 4 * 3),
-        # read bf16, write codes twice + scales twice
-        "quant_w": ("hbm", H * H * 2 + 2 * H * H + 2 * (H // g) ** 2 * 4),
+        # read W bf16 + s + gain; write W' bf16 + gain, codes twice + block scales twice
+        "fold_quant_w": ("hbm", H * H * 2 * 2 + H * 4 * 3 + 2 * H * H + 2 * (H // g) ** 2 * 4),
         # read X once, write row codes + scales and transposed column codes + scales
         "quant_x_dual": ("hbm", T * H * 2 + 2 * T * H + T * (H // g) * 4 + H * (T // g) * 4),
         "fprop": ("mfma", gemm_flops(T, H, H)),
@@ -162,8 +161,8 @@ class Step:
     def ops(self):
         qr, BF = self.qr, self.qr.QR_OUT_BF16
         return [
-            ("uaq_fold", lambda: qr.qr_uaq_fold(self.W, H, H, H, self.s, self.Wf, self.gain)),
-            ("quant_w", lambda: qr.qr_quant_w_128x128(self.Wf, H, H, H, self.qW, self.sW, self.qWT, self.sWT)),
+            ("fold_quant_w", lambda: qr.qr_uaq_fold_quant_w_128x128(
+                self.W, H, H, H, self.s, self.Wf, self.gain, self.qW, self.sW, self.qWT, self.sWT)),
             ("quant_x_dual", lambda: qr.qr_quant_act_1x128(self.X, T, H, H, self.qX, self.sX, self.qXT,
                                                            self.sXT)),
             ("fprop", lambda: qr.qr_gemm_fp8_bsfprop(self.qX, self.sX, self.qW, self.sW, T, H, H, self.Y, BF,

@@ -26,7 +26,7 @@ EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant
            "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_quant_int8_rowwise",
            "qr_gemm_int8_w8a8", "qr_quant_w_nvfp4", "qr_gemm_w4a16", "qr_gemm_fp8_bsfprop",
            "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes",
-           "qr_uaq_fold")
+           "qr_uaq_fold", "qr_uaq_fold_quant_w_128x128")
 QR_MAX_WEIGHT_BATCH = 4096
 QR_NVFP4_WORKSPACE_BYTES = 4096
 
@@ -84,6 +84,8 @@ def load():
     L.qr_gemm_workspace_bytes.restype = SZ
     L.qr_uaq_fold.argtypes = [P, I64, I64, I64, P, P, P, P]
     L.qr_uaq_fold.restype = I32
+    L.qr_uaq_fold_quant_w_128x128.argtypes = [P, I64, I64, I64, P, P, P, P, P, P, P, P]
+    L.qr_uaq_fold_quant_w_128x128.restype = I32
     _lib = L
     return L
 
@@ -196,6 +198,13 @@ def qr_gemm_workspace_bytes(kind, M, N, K) -> int:
 def qr_uaq_fold(w, n, k, ld_w, s, w_out, gain=None, stream=None):
     _check(load().qr_uaq_fold(_ptr(w), n, k, ld_w, _ptr(s), _ptr(w_out), _ptr(gain),
                               _stream(stream)), "qr_uaq_fold")
+
+
+def qr_uaq_fold_quant_w_128x128(w, n, k, ld_w, s, w_out, gain, q, sq, qT=None, sqT=None,
+                                stream=None):
+    _check(load().qr_uaq_fold_quant_w_128x128(_ptr(w), n, k, ld_w, _ptr(s), _ptr(w_out),
+                                              _ptr(gain), _ptr(q), _ptr(sq), _ptr(qT), _ptr(sqT),
+                                              _stream(stream)), "qr_uaq_fold_quant_w_128x128")
 
 
 # ------------------------------------------------------------------ allocating helpers
@@ -358,3 +367,20 @@ def uaq_fold(w, s, gain=None, inplace=False, stream=None):
     out = w if inplace else torch.empty((n, k), dtype=w.dtype, device=w.device)
     qr_uaq_fold(w, n, k, w.stride(0), s, out, gain, stream)
     return out
+
+
+def uaq_fold_quant_w(w, s, gain=None, transposed=False, inplace=False, stream=None):
+    """The fold and the 128x128 quantization in one pass.  Returns (w_folded, q, sq, qT, sqT)
+    (qT, sqT None unless transposed); gain (fp32, may be None) is updated in place."""
+    import torch
+    n, k = w.shape
+    dev = w.device
+    out = w if inplace else torch.empty((n, k), dtype=w.dtype, device=dev)
+    q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    sq = torch.empty((_cdiv(n, 128), _cdiv(k, 128)), dtype=torch.float32, device=dev)
+    qT = sqT = None
+    if transposed:
+        qT = torch.empty((k, n), dtype=torch.uint8, device=dev)
+        sqT = torch.empty((_cdiv(k, 128), _cdiv(n, 128)), dtype=torch.float32, device=dev)
+    qr_uaq_fold_quant_w_128x128(w, n, k, w.stride(0), s, out, gain, q, sq, qT, sqT, stream)
+    return out, q, sq, qT, sqT

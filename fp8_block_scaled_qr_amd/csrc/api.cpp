@@ -491,4 +491,39 @@ qr_status qr_uaq_fold(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, co
                                              gain_inout, (hipStream_t)stream));
 }
 
+qr_status qr_uaq_fold_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w,
+                                       const float *s, void *w_out_bf16, float *gain_inout,
+                                       uint8_t *q, float *sq, uint8_t *qT, float *sqT,
+                                       qr_stream stream)
+{
+    const qr_status st = check_weight(w_bf16, n, k, ld_w, q, sq, qT, sqT);
+    if (st != QR_OK || n == 0 || k == 0)
+        return st;
+    if (!s || !w_out_bf16)
+        return QR_ERR_NULL;
+    if (misaligned(w_out_bf16, 16) || misaligned(s, 16) || misaligned(gain_inout, 4))
+        return QR_ERR_ALIGN;
+    const bool inplace = w_out_bf16 == w_bf16;
+    const int64_t ld_out = inplace ? ld_w : k;
+    const int64_t nblk = cdiv(n, 128) * cdiv(k, 128);
+    const Range rw = span(w_bf16, strided_bytes(n, k, ld_w, 2)), rs = span(s, k * 4);
+    const Range outs[6] = {span(w_out_bf16, strided_bytes(n, k, ld_out, 2)),
+                           span(gain_inout, gain_inout ? k * 4 : 0),
+                           span(q, n * k), span(sq, nblk * 4), span(qT, n * k),
+                           span(sqT, nblk * 4)};
+    for (int i = 0; i < 6; ++i) {
+        if ((i != 0 || !inplace) && overlap(outs[i], rw))
+            return QR_ERR_ALIAS;
+        if (overlap(outs[i], rs))
+            return QR_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j]))
+                return QR_ERR_ALIAS;
+    }
+    return launch_status(qr::launch_fold_quant_w(static_cast<const uint16_t *>(w_bf16), n, k, ld_w,
+                                                 s, static_cast<uint16_t *>(w_out_bf16), ld_out,
+                                                 gain_inout, q, sq, qT, sqT,
+                                                 (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -13,6 +13,7 @@ enum : int {
     QMODE_COL = 2,    // 128x1 column groups, codes and scales stored transposed
     QMODE_BLK = 4,    // 128x128 blocks, codes in input layout
     QMODE_BLKT = 8,   // 128x128 blocks, transposed copy of codes and scales
+    QMODE_FOLD = 16,  // the UAQ fold applied to each tile before it is quantized
 };
 
 // One pass over x [rows, cols] (ld_x) in 128x128 tiles.
@@ -23,6 +24,13 @@ enum : int {
 hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t *q, float *s, uint8_t *qT, float *sT,
                              hipStream_t stream);
+
+// UAQ fold and 128x128 quantization in one pass: w_out [n, k] (ld_out) = RN_bf16(w / fs[c]),
+// gain[c] = RN32(gain[c] * fs[c]) if gain, then q / s (and qT / sT if qT) of w_out as
+// launch_quant_tile's BLK (| BLKT) would produce them.  w_out may equal w (ld_out == ld_w).
+hipError_t launch_fold_quant_w(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                               const float *fs, uint16_t *w_out, int64_t ld_out, float *gain,
+                               uint8_t *q, float *s, uint8_t *qT, float *sT, hipStream_t stream);
 
 // One weight of a batched 128x128 quantization (BLK, plus BLKT when qT is used).
 struct WeightDesc {

@@ -97,6 +97,104 @@ __device__ __forceinline__ void lds_barrier()
 constexpr int kBufFlags = 0x00020000;     // raw buffer, range-checked per lane
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// ---------------------------------------------------------------- UAQ fold
+
+// RN_bf16(w / s), general case: the quotient is formed in binary64 (correctly rounded) and
+// rounded to bf16 directly from there.  When w / s is not a bf16 midpoint it lies at least
+// ~2^-33 (relative) from every midpoint (w has 8 significant bits, s 24), far more than
+// binary64's rounding error, so this equals rounding the exact quotient once.  (Rounding
+// through binary32 first would not: binary32's 2^-24 step can land exactly on a midpoint.)
+__device__ __forceinline__ uint16_t fold1(uint32_t wbits, float s)
+{
+    const float wv = __uint_as_float(wbits << 16);
+    const double d = (double)wv / (double)s;
+    const double a = fabs(d);
+    double rv = 0.0;
+    if (a != 0.0) {
+        int e = ilogb(a);
+        if (e < -126)
+            e = -126;                                   // bf16 subnormal spacing 2^-133
+        rv = ldexp(rint(ldexp(a, 7 - e)), e - 7);       // 8 significant bits, ties to even
+    }
+    const uint32_t fb = __float_as_uint((float)rv);    // exact (or overflow to inf)
+    return (uint16_t)((fb >> 16) | (wbits & 0x8000u));
+}
+
+// RN_bf16(w / s) for s > 0 with r = RN32(1 / s); `col_ok` says 2^-120 <= s < 2^121.
+// z = |w| / s is bracketed without division: q = RN32(|w| * r) is within (2u + u^2) z of z
+// (u = 2^-24: one rounding in r, one in the product), i.e. within 2.01 binary32 ulps of q.
+// Let lo be q truncated to bf16 and hi = lo + one bf16 ulp.  Then z lies between the bf16
+// midpoint below lo and the one above hi, so it rounds to lo or hi, and only its side of
+// their midpoint m = lo + ulp / 2 is left to decide.  That is the sign of |w| - m * s, taken
+// exactly from one FMA: |w| and m * s are multiples of 2^(E_w - 32) or coarser, so with
+// |w| >= 2^-90 a non-zero difference is at least 2^-122 and its rounding keeps its sign; zero
+// would be the tie (even neighbour).  `slow` flags the elements outside those ranges (tiny or
+// huge quotients or weights, s out of range, non-finite w), which take the binary64 route;
+// zero weights give the signed zero directly.
+__device__ __forceinline__ uint32_t fold_fast(uint32_t wbits, float s, float r, bool col_ok,
+                                              uint32_t &slow)
+{
+    const float a = __uint_as_float((wbits & 0x7FFFu) << 16);
+    const uint32_t qb = __float_as_uint(a * r);
+    const uint32_t ew = (wbits >> 7) & 0xFFu, eq = qb >> 23;
+    const uint32_t lo = qb & 0xFFFF0000u;
+    const float d = fmaf(-__uint_as_float(lo | 0x8000u), s, a);
+    const uint32_t up = d > 0.0f ? 1u : (d == 0.0f ? (lo >> 16) & 1u : 0u);
+    const bool zero = (wbits & 0x7FFFu) == 0;            // +-0 / s = +-0 for s > 0
+    const bool ok = col_ok && ew >= 37u && eq - 27u <= 220u;
+    slow = (ok || zero) ? 0u : 1u;
+    return zero ? wbits : (((lo >> 16) + up) | (wbits & 0x8000u));
+}
+
+// The fold's per-lane constants for 8 adjacent columns: s, r = RN32(1 / s) (correctly
+// rounded) and whether s lies in the fast route's range.
+struct Fold8 {
+    float s[8], r[8];
+    bool ok[8];
+};
+
+__device__ __forceinline__ void fold8_setup(const float *__restrict__ s, int64_t c, Fold8 &f)
+{
+    const float4 s0 = *reinterpret_cast<const float4 *>(s + c);
+    const float4 s1 = *reinterpret_cast<const float4 *>(s + c + 4);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        f.s[j] = sv[j];
+        f.r[j] = __fdiv_rn(1.0f, sv[j]);
+        f.ok[j] = (__float_as_uint(sv[j]) >> 23) - 7u <= 240u;   // 2^-120 <= s < 2^121
+    }
+}
+
+// RN_bf16(w / s) of 8 adjacent bf16 weights (one 16-byte chunk); the binary64 route only for
+// chunks that hold an element outside the fast route's ranges.
+__device__ __forceinline__ uint4 fold8(const uint4 &v, const Fold8 &f)
+{
+    const uint32_t wb[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                            v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    uint32_t res[8], sl[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        res[j] = fold_fast(wb[j], f.s[j], f.r[j], f.ok[j], sl[j]);
+    if (sl[0] | sl[1] | sl[2] | sl[3] | sl[4] | sl[5] | sl[6] | sl[7]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (sl[j])
+                res[j] = fold1(wb[j], f.s[j]);
+    }
+    return make_uint4(res[0] | (res[1] << 16), res[2] | (res[3] << 16),
+                      res[4] | (res[5] << 16), res[6] | (res[7] << 16));
+}
+
+// The fold ahead of a 128x128 weight quantization: the tile's bf16 values are replaced by
+// RN_bf16(w / s[c]) before the block maxima, written to out, and the gain is scaled by s once.
+struct FoldArgs {
+    const float *s = nullptr;   // [cols]
+    uint16_t *out = nullptr;    // [rows, cols], leading dimension ldo (may equal the input)
+    int64_t ldo = 0;
+    float *gain = nullptr;      // [cols] or nullptr
+};
+
 // The tile's eight 16-byte loads per thread as range-checked buffer loads: a row past `rows`
 // lies past the descriptor's extent and a column octet past `cols` takes an offset outside it,
 // so both read zeros without a branch.
@@ -126,12 +224,13 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
                                             int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
                                             float *__restrict__ s, uint8_t *__restrict__ qT,
                                             float *__restrict__ sT, int64_t first, int64_t stride,
-                                            int64_t pend)
+                                            int64_t pend, const FoldArgs fa = FoldArgs{})
 {
     constexpr bool ROW = (MODE & QMODE_ROW) != 0;
     constexpr bool COL = (MODE & QMODE_COL) != 0;
     constexpr bool BLK = (MODE & QMODE_BLK) != 0;
     constexpr bool BLKT = (MODE & QMODE_BLKT) != 0;
+    constexpr bool FOLD = (MODE & QMODE_FOLD) != 0;
     constexpr bool ANYBLK = BLK || BLKT;
 
     __shared__ uint32_t red_col[4][kTile];
@@ -330,6 +429,24 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int6
         uint4 v[8];
         const int64_t c = bj * kTile + 8 * oc;
         load_tile(x, rows, ldx, bi * kTile, c, c < cols, oq, v);
+        if (FOLD && c < cols) {
+            // this thread's 8 columns of the tile's rows 8 oq .. 8 oq + 7 (only this thread
+            // reads or writes them, so out may be the input itself)
+            Fold8 f;
+            fold8_setup(fa.s, c, f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v[j] = fold8(v[j], f);
+                const int64_t r = bi * kTile + 8 * oq + j;
+                if (r < rows)
+                    *reinterpret_cast<uint4 *>(fa.out + r * fa.ldo + c) = v[j];
+            }
+            if (fa.gain && bi == 0 && oq == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    fa.gain[c + j] = fa.gain[c + j] * f.s[j];
+            }
+        }
         process(bi, bj, par, v);
         par ^= 1;
         pi += stride;
@@ -369,6 +486,21 @@ __global__ __launch_bounds__(256, 3) void k_quant_tile(const uint16_t *__restric
         first = (xcd + 8 * (l / ngc)) * ngc + l % ngc;
     }
     quant_tiles<MODE>(x, rows, cols, ldx, q, s, qT, sT, first, G, nt);
+}
+
+// The UAQ fold and the 128x128 weight quantization in one pass (MODE = BLK | FOLD, plus BLKT
+// for the transposed copy): each tile is folded in registers, written out, and quantized.
+template <int MODE>
+__global__ __launch_bounds__(256, 3) void k_fold_quant_w(const uint16_t *__restrict__ x,
+                                                      int64_t rows, int64_t cols, int64_t ldx,
+                                                      uint8_t *__restrict__ q,
+                                                      float *__restrict__ s,
+                                                      uint8_t *__restrict__ qT,
+                                                      float *__restrict__ sT, FoldArgs fa)
+{
+    const int64_t ngc = (cols + kTile - 1) / kTile;
+    const int64_t nt = ((rows + kTile - 1) / kTile) * ngc;
+    quant_tiles<MODE>(x, rows, cols, ldx, q, s, qT, sT, blockIdx.x, gridDim.x, nt, fa);
 }
 
 // A list of weights quantized in one persistent launch (a weight update re-quantizes every
@@ -587,55 +719,6 @@ __global__ __launch_bounds__(256) void k_quant_int8_rows(const uint16_t *__restr
     }
 }
 
-// ---------------------------------------------------------------- UAQ fold
-
-// RN_bf16(w / s), general case: the quotient is formed in binary64 (correctly rounded) and
-// rounded to bf16 directly from there.  When w / s is not a bf16 midpoint it lies at least
-// ~2^-33 (relative) from every midpoint (w has 8 significant bits, s 24), far more than
-// binary64's rounding error, so this equals rounding the exact quotient once.  (Rounding
-// through binary32 first would not: binary32's 2^-24 step can land exactly on a midpoint.)
-__device__ __forceinline__ uint16_t fold1(uint32_t wbits, float s)
-{
-    const float wv = __uint_as_float(wbits << 16);
-    const double d = (double)wv / (double)s;
-    const double a = fabs(d);
-    double rv = 0.0;
-    if (a != 0.0) {
-        int e = ilogb(a);
-        if (e < -126)
-            e = -126;                                   // bf16 subnormal spacing 2^-133
-        rv = ldexp(rint(ldexp(a, 7 - e)), e - 7);       // 8 significant bits, ties to even
-    }
-    const uint32_t fb = __float_as_uint((float)rv);    // exact (or overflow to inf)
-    return (uint16_t)((fb >> 16) | (wbits & 0x8000u));
-}
-
-// RN_bf16(w / s) for s > 0 with r = RN32(1 / s); `col_ok` says 2^-120 <= s < 2^121.
-// z = |w| / s is bracketed without division: q = RN32(|w| * r) is within (2u + u^2) z of z
-// (u = 2^-24: one rounding in r, one in the product), i.e. within 2.01 binary32 ulps of q.
-// Let lo be q truncated to bf16 and hi = lo + one bf16 ulp.  Then z lies between the bf16
-// midpoint below lo and the one above hi, so it rounds to lo or hi, and only its side of
-// their midpoint m = lo + ulp / 2 is left to decide.  That is the sign of |w| - m * s, taken
-// exactly from one FMA: |w| and m * s are multiples of 2^(E_w - 32) or coarser, so with
-// |w| >= 2^-90 a non-zero difference is at least 2^-122 and its rounding keeps its sign; zero
-// would be the tie (even neighbour).  `slow` flags the elements outside those ranges (tiny or
-// huge quotients or weights, s out of range, non-finite w), which take the binary64 route;
-// zero weights give the signed zero directly.
-__device__ __forceinline__ uint32_t fold_fast(uint32_t wbits, float s, float r, bool col_ok,
-                                              uint32_t &slow)
-{
-    const float a = __uint_as_float((wbits & 0x7FFFu) << 16);
-    const uint32_t qb = __float_as_uint(a * r);
-    const uint32_t ew = (wbits >> 7) & 0xFFu, eq = qb >> 23;
-    const uint32_t lo = qb & 0xFFFF0000u;
-    const float d = fmaf(-__uint_as_float(lo | 0x8000u), s, a);
-    const uint32_t up = d > 0.0f ? 1u : (d == 0.0f ? (lo >> 16) & 1u : 0u);
-    const bool zero = (wbits & 0x7FFFu) == 0;            // +-0 / s = +-0 for s > 0
-    const bool ok = col_ok && ew >= 37u && eq - 27u <= 220u;
-    slow = (ok || zero) ? 0u : 1u;
-    return zero ? wbits : (((lo >> 16) + up) | (wbits & 0x8000u));
-}
-
 // One wave covers 64 consecutive 8-column chunks of a row (1 KB of bf16); the grid's y
 // dimension and the 4 waves of a workgroup walk the rows, so each lane forms the reciprocals
 // of its 8 columns once and reuses them for every row it folds.
@@ -646,32 +729,9 @@ __global__ __launch_bounds__(256) void k_uaq_fold(const uint16_t *w, int64_t n, 
     const int64_t kc = ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63)) * 8;
     if (kc >= k)
         return;
-    const float4 s0 = *reinterpret_cast<const float4 *>(s + kc);
-    const float4 s1 = *reinterpret_cast<const float4 *>(s + kc + 4);
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    float rv[8];
-    bool ok[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        rv[j] = __fdiv_rn(1.0f, sv[j]);                 // correctly rounded
-        ok[j] = (__float_as_uint(sv[j]) >> 23) - 7u <= 240u;   // 2^-120 <= s < 2^121
-    }
-    auto fold_chunk = [&](uint4 v) {
-        const uint32_t wb[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                                v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-        uint32_t res[8], sl[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            res[j] = fold_fast(wb[j], sv[j], rv[j], ok[j], sl[j]);
-        if (sl[0] | sl[1] | sl[2] | sl[3] | sl[4] | sl[5] | sl[6] | sl[7]) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (sl[j])
-                    res[j] = fold1(wb[j], sv[j]);
-        }
-        return make_uint4(res[0] | (res[1] << 16), res[2] | (res[3] << 16),
-                          res[4] | (res[5] << 16), res[6] | (res[7] << 16));
-    };
+    Fold8 f;
+    fold8_setup(s, kc, f);
+    auto fold_chunk = [&](const uint4 &v) { return fold8(v, f); };
     const int64_t step = (int64_t)gridDim.y * 4;
     int64_t row = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
     for (; row + 3 * step < n; row += 4 * step) {       // four rows in flight per lane
@@ -690,7 +750,7 @@ __global__ __launch_bounds__(256) void k_uaq_fold(const uint16_t *w, int64_t n, 
     if (gain && blockIdx.y == 0 && threadIdx.x < 64) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            gain[kc + j] = gain[kc + j] * sv[j];
+            gain[kc + j] = gain[kc + j] * f.s[j];
     }
 }
 
@@ -752,6 +812,30 @@ hipError_t launch_quant_tile(int mode, const uint16_t *x, int64_t rows, int64_t 
     default:
         return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_fold_quant_w(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                               const float *fs, uint16_t *w_out, int64_t ld_out, float *gain,
+                               uint8_t *q, float *s, uint8_t *qT, float *sT, hipStream_t stream)
+{
+    const int64_t nt = ((n + kTile - 1) / kTile) * ((k + kTile - 1) / kTile);
+    if (nt == 0)
+        return hipSuccess;
+    FoldArgs fa;
+    fa.s = fs;
+    fa.out = w_out;
+    fa.ldo = ld_out;
+    fa.gain = gain;
+    constexpr int BT = QMODE_BLK | QMODE_BLKT | QMODE_FOLD, B = QMODE_BLK | QMODE_FOLD;
+    const void *fn = qT ? reinterpret_cast<const void *>(&k_fold_quant_w<BT>)
+                        : reinterpret_cast<const void *>(&k_fold_quant_w<B>);
+    const int64_t limit = persistent_grid(fn);
+    const dim3 grid((unsigned)(nt < limit ? nt : limit));
+    if (qT)
+        k_fold_quant_w<BT><<<grid, 256, 0, stream>>>(w, n, k, ld_w, q, s, qT, sT, fa);
+    else
+        k_fold_quant_w<B><<<grid, 256, 0, stream>>>(w, n, k, ld_w, q, s, qT, sT, fa);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_w_batch(const WeightDesc *descs, int count, bool transposed,

@@ -301,6 +301,22 @@ size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K);
 qr_status qr_uaq_fold(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, const float *s,
                       void *w_out_bf16, float *gain_inout, qr_stream stream);
 
+/*
+ * UAQ fold followed by the 128x128 weight quantization, in one pass over w [QURL: s folded
+ * into the weights once; JET / DeepSeek-V3 fine-grained quantization: 128x128 weight blocks].
+ * The outputs equal those of qr_uaq_fold(w, n, k, ld_w, s, w_out, gain_inout) followed by
+ * qr_quant_w_128x128(w_out, n, k, ld_out, q, sq, qT, sqT), bit for bit, where ld_out is ld_w
+ * in place and k otherwise; w is read once and the folded weight is not read back.
+ *   w, s, w_out, gain_inout as for qr_uaq_fold; q, sq, qT, sqT as for qr_quant_w_128x128.
+ * Size rules: those of both entry points (n % 8 == 0, k % 8 == 0, ld_w % 8 == 0, ld_w >= k,
+ * ld_w < 2^22, ceil(n/128) <= 65535).  Alignment: w, w_out, s, q, qT 16 bytes; sq, sqT,
+ * gain_inout 4 bytes.  No output may overlap w (except w_out in place), s or another output.
+ */
+qr_status qr_uaq_fold_quant_w_128x128(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w,
+                                       const float *s, void *w_out_bf16, float *gain_inout,
+                                       uint8_t *q, float *sq, uint8_t *qT, float *sqT,
+                                       qr_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 15, declared
+    assert len(declared) == 16, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -130,6 +130,27 @@ def test_int8_validation(L):
     assert g(A, B, C, D, 256, 5120, 27648, E, 1, W + 8, nb, None) == ALIGN
     assert g(A, B, C, D, 256, 5120, 27648, E, 1, C + 4096, nb, None) == ALIAS     # ws over b
     assert g(A, B, C, D, 256, 5120, 27648, E, 1, E + 4096, nb, None) == ALIAS     # ws over y
+
+
+def test_fold_quant_w_validation(L):
+    f = L.qr_uaq_fold_quant_w_128x128
+    F = 6 << 40
+    # (w, n, k, ld_w, s, w_out, gain, q, sq, qT, sqT, stream)
+    assert f(A, 128, 100, 104, B, C, None, D, E, None, None, None) == SHAPE   # k % 8
+    assert f(A, 100, 128, 128, B, C, None, D, E, None, None, None) == SHAPE   # n % 8
+    assert f(A, 128, 128, 120, B, C, None, D, E, None, None, None) == SHAPE   # ld < k
+    assert f(A, 128, 128, 128, B, C, None, None, E, None, None, None) == NULL  # codes
+    assert f(A, 128, 128, 128, B, C, None, D, E, F, None, None) == NULL        # qT without sT
+    assert f(A, 128, 128, 128, None, C, None, D, E, None, None, None) == NULL  # s
+    assert f(A, 128, 128, 128, B, None, None, D, E, None, None, None) == NULL  # w_out
+    assert f(A, 128, 128, 128, B + 4, C, None, D, E, None, None, None) == ALIGN   # s 16-byte
+    assert f(A, 128, 128, 128, B, C + 8, None, D, E, None, None, None) == ALIGN   # w_out
+    assert f(A, 128, 128, 128, B, C, E + 2, D, E + 1024, None, None, None) == ALIGN  # gain
+    assert f(A, 128, 128, 128, B, A + 256, None, D, E, None, None, None) == ALIAS  # w_out over w
+    assert f(A, 128, 128, 128, B, C, B + 16, D, E, None, None, None) == ALIAS     # gain over s
+    assert f(A, 128, 128, 128, B, C, None, C + 64, E, None, None, None) == ALIAS  # q over w_out
+    assert f(A, 128, 128, 128, B, C, None, D, E, D + 64, E + 1024, None) == ALIAS  # qT over q
+    assert f(A, 0, 128, 128, B, C, None, D, E, None, None, None) == OK
 
 
 def test_fp4_validation(L):

@@ -425,6 +425,49 @@ def test_uaq_fold_random_and_near_midpoints():
     assert_bitexact(host(wd), ro, "folded weight in place")
 
 
+@pytest.mark.parametrize("n,k,transposed", [(296, 520, True), (136, 1040, False), (8, 8, True),
+                                            (4096, 4096, True)])
+def test_uaq_fold_quant_w_fused(n, k, transposed):
+    """The fold and the 128x128 quantization in one pass against the oracle's fold followed
+    by its block quantizer, bit for bit (folded weight, gain, codes, scales and the transposed
+    copy), on ragged tile grids and the 8B step's 4096x4096 weight; rare routes included
+    (signed zeros, bf16 subnormals, scales outside [2^-120, 2^121), quotients far from 1).
+    Then in place, and against the two separate entry points on the GPU."""
+    say("fold+quant_w", n, k, transposed)
+    rng = np.random.default_rng(n + 3 * k)
+    w = qr_synth.normal_bf16(81 + n, (n, k), 0.02)
+    s = rng.uniform(1.5, 4.0, k).astype(np.float32)
+    flat = w.reshape(-1)
+    pick = rng.choice(flat.size, size=max(1, flat.size // 50), replace=False)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8040, 0x007F, 0x0080, 0x3F80], np.uint16)
+    flat[pick] = specials[rng.integers(0, specials.size, pick.size)]
+    s[:8] = np.array([2.0 ** -121, 1e-30, 2.0 ** 121, 1e30, 2.0 ** 127, np.float32(3.4e38),
+                      1.0, 2.0 ** -60], np.float32)
+    gain = rng.uniform(0.5, 2.0, k).astype(np.float32)
+    ro, rg = oracle.uaq_fold(w, s, gain)
+    rq, rs = oracle.quant_blocks(ro)
+    wd, sd, gd = dev_bf16(w), dev(s), dev(gain.copy())
+    out, q, sq, qT, sqT = qr.uaq_fold_quant_w(wd, sd, gd, transposed=transposed)
+    assert_bitexact(host(out), ro, "folded weight")
+    assert_bitexact(host(gd), rg, "gain")
+    assert_bitexact(host(q), rq, "codes")
+    assert_bitexact(host(sq), rs, "block scales")
+    if transposed:
+        assert_bitexact(host(qT), np.ascontiguousarray(rq.T), "transposed codes")
+        assert_bitexact(host(sqT), np.ascontiguousarray(rs.T), "transposed scales")
+    # the separate entry points give the same bits
+    f2 = qr.uaq_fold(wd, sd)
+    q2, s2, qT2, sT2 = qr.quant_w(f2, transposed=transposed)
+    assert torch.equal(f2, out) and torch.equal(q2, q) and torch.equal(s2, sq)
+    if transposed:
+        assert torch.equal(qT2, qT) and torch.equal(sT2, sqT)
+    # in place, no gain
+    out3, q3, sq3, _, _ = qr.uaq_fold_quant_w(wd, sd, None, transposed=False, inplace=True)
+    assert out3.data_ptr() == wd.data_ptr()
+    assert_bitexact(host(wd), ro, "folded weight in place")
+    assert torch.equal(q3, q) and torch.equal(sq3, sq)
+
+
 @pytest.mark.parametrize("n,k", [(37, 520), (301, 1040), (1, 8)])
 def test_uaq_fold_edges_and_ragged(n, k):
     """Ragged grids (rows not a multiple of 4, columns not a multiple of 512, several trips of
