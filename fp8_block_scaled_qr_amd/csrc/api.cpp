@@ -250,7 +250,7 @@ qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, c
         return QR_ERR_ARG;
     if (M == 0 || N == 0)
         return QR_OK;
-    if (!a || !sa || !b || !sb || !y)
+    if (!sa || !sb || !y || (K > 0 && (!a || !b)))   // K == 0 reads no codes
         return QR_ERR_NULL;
     if (misaligned(a, 16) || misaligned(b, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
         misaligned(sb, 4))

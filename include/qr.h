@@ -166,9 +166,10 @@ qr_status qr_quant_int8_rowwise(const void *x_bf16, int64_t rows, int64_t cols, 
  * workspace: device scratch of at least qr_gemm_workspace_bytes(QR_GEMM_INT8, M, N, K) bytes
  *   (may be NULL when that is 0); it then holds the splits' exact int32 partial sums, which
  *   are added before the scaling, so the result is the same as without a split.
- * Size rules: M, N >= 0; K % 128 == 0 and K <= 131072 (the sum stays within int32).  a, b, y,
- * workspace 16-byte aligned, sa, sb 4-byte aligned; neither y nor the workspace may overlap an
- * input or each other.
+ * Size rules: M, N >= 0; K % 128 == 0 and K <= 131072 (the sum stays within int32); with
+ * K == 0, a and b may be NULL and y = 0 (for finite scales).  a, b, y, workspace 16-byte
+ * aligned, sa, sb 4-byte aligned; neither y nor the workspace may overlap an input or each
+ * other.
  */
 qr_status qr_gemm_int8_w8a8(const int8_t *a, const float *sa, const int8_t *b, const float *sb,
                             int64_t M, int64_t N, int64_t K, void *y, qr_out_dtype y_dtype,

@@ -227,6 +227,30 @@ def test_gemm_int8(M, N, K, out):
         assert np.array_equal(y.cpu().numpy(), _int8_scaled_exact(qa, sa, qb, sb))
 
 
+def test_gemm_int8_empty_zero_k_and_workspace_reuse():
+    """K = 0 stores zeros, M = 0 is a no-op; then one workspace serves a split product and a
+    smaller split product after it (every partial is rewritten by each call, so nothing of the
+    first call leaks into the second)."""
+    say("gemm_int8 empty / K=0 / workspace reuse")
+    a = torch.zeros((4, 0), dtype=torch.int8, device="cuda")
+    y = torch.full((4, 8), 7.0, device="cuda")
+    qr.qr_gemm_int8_w8a8(a, torch.ones(4, device="cuda"), a, torch.ones(8, device="cuda"),
+                         4, 8, 0, y, qr.QR_OUT_F32)
+    assert float(y.abs().max()) == 0.0
+    qr.qr_gemm_int8_w8a8(None, None, None, None, 0, 8, 128, y, qr.QR_OUT_F32)   # M = 0
+    shapes = [(300, 264, 1024), (100, 136, 512)]
+    nb = max(qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, *sh) for sh in shapes)
+    assert all(qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, *sh) > 0 for sh in shapes)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for M, N, K in shapes:
+        qa, sa, qb, sb = _int8_case(M, N, K, 7 * M + N)
+        yd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        qr.qr_gemm_int8_w8a8(dev(qa), dev(sa), dev(qb), dev(sb), M, N, K, yd, qr.QR_OUT_F32,
+                             ws, nb)
+        assert np.array_equal(yd.cpu().numpy(), _int8_scaled_exact(qa, sa, qb, sb))
+        _check_int8(out_f64(yd), oracle.gemm_int8(qa, sa, qb, sb), qr.QR_OUT_F32)
+
+
 @pytest.mark.parametrize("M,N,K", [(8192, 4096, 4096), (64, 14336, 4096), (256, 5120, 27648),
                                    (256, 55296, 5120), (200, 32768, 256), (256, 7168, 5120),
                                    (64, 4096, 14336)])
