@@ -212,10 +212,11 @@ def _int8_scaled_exact(qa, sa, qb, sb):
 
 
 # (77, 200, 384), (300, 264, 256), (520, 304, 384): 256x256 tiles with K split 3, 2, 3 ways;
-# (64, 512, 4096) and (40, 1000, 2304): 64x32 tiles split 4 and 2 ways; the rest unsplit
+# (64, 512, 4096) and (40, 1000, 2304): 64x32 tiles split 4 and 2 ways; (130, 201, 512): an odd
+# N on a 4-way split (scalar partial stores and sums); the rest unsplit
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (64, 1000, 1024), (1, 128, 128),
                                    (300, 264, 256), (520, 304, 384), (17, 72, 640),
-                                   (64, 512, 4096), (40, 1000, 2304)])
+                                   (64, 512, 4096), (40, 1000, 2304), (130, 201, 512)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_gemm_int8(M, N, K, out):
     say("gemm_int8", M, N, K, out)
@@ -490,6 +491,30 @@ def test_uaq_fold_quant_w_fused(n, k, transposed):
     assert out3.data_ptr() == wd.data_ptr()
     assert_bitexact(host(wd), ro, "folded weight in place")
     assert torch.equal(q3, q) and torch.equal(sq3, sq)
+
+
+def test_uaq_fold_quant_w_fused_strided():
+    """A weight that is a column slice of a wider buffer (ld_w = 448 > k = 384): out of place
+    (W' dense) and in place (W' keeps ld_w; the columns past k stay untouched)."""
+    say("fold+quant_w strided")
+    n, k, ld = 256, 384, 448
+    rng = np.random.default_rng(17)
+    full = qr_synth.normal_bf16(91, (n, ld), 0.02)
+    w = np.ascontiguousarray(full[:, :k])
+    s = rng.uniform(1.5, 4.0, k).astype(np.float32)
+    ro, _ = oracle.uaq_fold(w, s)
+    rq, rs = oracle.quant_blocks(ro)
+    fd = dev_bf16(full)
+    out, q, sq, qT, sqT = qr.uaq_fold_quant_w(fd[:, :k], dev(s), None, transposed=True)
+    assert_bitexact(host(out), ro, "folded weight")
+    assert_bitexact(host(q), rq, "codes")
+    assert_bitexact(host(sq), rs, "block scales")
+    assert_bitexact(host(qT), np.ascontiguousarray(rq.T), "transposed codes")
+    out2, q2, sq2, _, _ = qr.uaq_fold_quant_w(fd[:, :k], dev(s), None, inplace=True)
+    h = host(fd)
+    assert_bitexact(np.ascontiguousarray(h[:, :k]), ro, "folded weight in place")
+    assert_bitexact(np.ascontiguousarray(h[:, k:]), np.ascontiguousarray(full[:, k:]), "tail")
+    assert torch.equal(q2, q) and torch.equal(sq2, sq)
 
 
 @pytest.mark.parametrize("n,k", [(37, 520), (301, 1040), (1, 8)])
