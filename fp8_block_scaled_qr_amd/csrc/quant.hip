@@ -220,7 +220,7 @@ __device__ __forceinline__ void load_tile(const uint16_t *__restrict__ x, int64_
 // The workgroup handles tiles first, first + stride, ... of x (row-major over the tile grid).
 // Every thread of the workgroup calls it.
 template <int MODE>
-__device__ __forceinline__ void quant_tiles(const uint16_t *__restrict__ x, int64_t rows,
+__device__ __forceinline__ void quant_tiles(const uint16_t *x, int64_t rows,
                                             int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
                                             float *__restrict__ s, uint8_t *__restrict__ qT,
                                             float *__restrict__ sT, int64_t first, int64_t stride,
@@ -490,8 +490,10 @@ __global__ __launch_bounds__(256, 3) void k_quant_tile(const uint16_t *__restric
 
 // The UAQ fold and the 128x128 weight quantization in one pass (MODE = BLK | FOLD, plus BLKT
 // for the transposed copy): each tile is folded in registers, written out, and quantized.
+// x is not restrict-qualified here or in quant_tiles: in place, the folded values go back to
+// x's own memory.
 template <int MODE>
-__global__ __launch_bounds__(256, 3) void k_fold_quant_w(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(256, 3) void k_fold_quant_w(const uint16_t *x,
                                                       int64_t rows, int64_t cols, int64_t ldx,
                                                       uint8_t *__restrict__ q,
                                                       float *__restrict__ s,
