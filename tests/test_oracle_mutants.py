@@ -3,7 +3,8 @@ the oracle source (a wrong rounding rule, a dropped saturation, a lost sign of z
 transposed or shifted scale index, a wrong constant, a reciprocal in place of the division, a
 dropped absolute value, a double rounding, an off-by-one group, a wrong mean, a dropped eps
 or gain in the norm, INT8 ties away from zero, a wrong INT8 divisor or scale index, an E2M1 tie to the odd code,
-a wrong FP4 tensor divisor, a dropped FP4 block scale) and runs the pin suite on that
+a wrong FP4 tensor divisor, a dropped FP4 block scale, 128x128 block codes formed with the
+amax, half the scale or a per-element scale instead of the block scale) and runs the pin suite on that
 copy, which must fail.  CPU only: the copies live in a temporary directory and the HIP library
 is not involved."""
 import os
@@ -42,6 +43,16 @@ MUTANTS = {
     "nvfp4_tensor_divisor": ("float t = amax / 2688.0f;", "float t = amax / 2048.0f;"),
     "w4a16_no_block_scale": ("double w = orc_e2m1_decode(c) * orc_e4m3_decode(bscale[n * (K / 16) + kk / 16]);",
                              "double w = orc_e2m1_decode(c);"),
+    "block_codes_divide_by_amax": (
+        "q[r * k + c] = orc_quantize_value(orc_bf16_to_f32(w[r * ld + c]), sc);",
+        "q[r * k + c] = orc_quantize_value(orc_bf16_to_f32(w[r * ld + c]), amax);"),
+    "block_codes_half_scale": (
+        "q[r * k + c] = orc_quantize_value(orc_bf16_to_f32(w[r * ld + c]), sc);",
+        "q[r * k + c] = orc_quantize_value(orc_bf16_to_f32(w[r * ld + c]), sc * 0.5f);"),
+    "block_codes_element_scale": (
+        "q[r * k + c] = orc_quantize_value(orc_bf16_to_f32(w[r * ld + c]), sc);",
+        "q[r * k + c] = orc_quantize_value(orc_bf16_to_f32(w[r * ld + c]), "
+        "orc_group_scale(fabsf(orc_bf16_to_f32(w[r * ld + c]))));"),
     "column_group_short": ("int64_t r0 = g * GROUP, r1 = r0 + GROUP < rows ? r0 + GROUP : rows;",
                            "int64_t r0 = g * GROUP, r1 = r0 + GROUP - 1 < rows ? "
                            "r0 + GROUP - 1 : rows;"),

@@ -229,6 +229,82 @@ def test_block_quant_of_transpose_is_transpose():
     assert np.array_equal(qt, q.T) and np.array_equal(st, s.T)
 
 
+def _weight_with_special_blocks():
+    """Ragged bf16 weight (partial blocks in both directions) with one outlier block (x1000),
+    one tiny-amax block (x2^-120: its scale is a binary32 subnormal), one all-zero block and
+    one block of negative zeros and tiny negatives (their quotients round to the signed zero)."""
+    w = qr_synth.normal_bf16(33, (392, 264), 0.02)
+    f = bf16_f32(w)
+    f[128:256, 0:128] *= np.float32(1000.0)
+    f[0:128, 128:256] *= np.float32(2.0 ** -120)
+    f[256:384, 128:256] = 0.0
+    f[256:392, 256:264] = -0.0
+    f[260, 258] = np.float32(-2.0 ** -40)          # tiny next to the block's amax below
+    f[300, 260] = np.float32(3.0)
+    return qr_synth.f32_to_bf16_bits(f)
+
+
+def test_block_codes_against_library_division_and_torch_cast():
+    """The 128x128 codes, rebuilt from library routines only: the block amax by numpy, the
+    scale and the quotient by numpy's IEEE binary32 division, the code by torch's
+    float8_e4m3fn cast below 448 and saturation at or above it (Jet-RL notes, fine-grained
+    GEMM quantization: weights in 128x128 blocks, one scale each)."""
+    w = _weight_with_special_blocks()
+    q, s = oracle.quant_blocks(w)
+    f = bf16_f32(w)
+    n, k = f.shape
+    nbi, nbj = -(-n // 128), -(-k // 128)
+    s_ref = np.empty((nbi, nbj), np.float32)
+    for bi in range(nbi):
+        for bj in range(nbj):
+            blk = f[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            s_ref[bi, bj] = np.float32(np.abs(blk).max()) / np.float32(448.0)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert s_ref[0, 1] < np.finfo(np.float32).tiny and s_ref[0, 1] > 0   # subnormal scale
+    assert s_ref[2, 1] == 0 and s_ref[1, 0] > 100 * s_ref[0, 0]
+    s_el = np.repeat(np.repeat(s_ref, 128, axis=0), 128, axis=1)[:n, :k]
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        v = np.where(s_el == 0, f, f / s_el).astype(np.float32)
+    ref = np.where(np.signbit(v), np.uint8(0xFE), np.uint8(0x7E))
+    small = np.abs(v) < 448
+    ref[small] = torch.from_numpy(v[small]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.argwhere(q != ref)
+    assert bad.size == 0, [(tuple(i), hex(q[tuple(i)]), hex(ref[tuple(i)])) for i in bad[:8]]
+    # the zero block keeps each element's sign of zero; the amax element of each block is +-448
+    assert np.all(q[256:384, 128:256] == 0x00) and np.all(q[256:392, 256:264][f[256:392, 256:264] == 0] == 0x80)
+    assert q[260, 258] == 0x80
+    for bi in range(nbi):
+        for bj in range(nbj):
+            blk = f[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            if s_ref[bi, bj] > 0:
+                i, j = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
+                assert q[bi * 128 + i, bj * 128 + j] in (0x7E, 0xFE)
+
+
+def test_block_codes_exact_rationals_subsample():
+    """Every 37th code of the special-block weight against the exact rational quotient
+    rounded once to binary32, then the nearest E4M3 value by search."""
+    w = _weight_with_special_blocks()
+    q, s = oracle.quant_blocks(w)
+    f = bf16_f32(w)
+    n, k = f.shape
+    flat = np.arange(n * k)
+    picks = np.concatenate([flat[::37], [128 * k + 5, 5 * k + 130, 260 * k + 258, 300 * k + 260]])
+    for idx in picks:
+        r, c = divmod(int(idx), k)
+        x = float(f[r, c])
+        amax = Fraction(float(np.abs(f[r // 128 * 128:(r // 128 + 1) * 128,
+                                       c // 128 * 128:(c // 128 + 1) * 128]).max()))
+        sc = rn32(amax / 448)
+        assert Fraction(float(s[r // 128, c // 128])) == sc
+        if sc == 0:
+            xv = x
+        else:
+            qv = rn32(Fraction(x) / sc)
+            xv = float(qv) if qv != 0 else (-0.0 if np.signbit(x) else 0.0)
+        assert q[r, c] == e4m3_nearest(xv), (r, c, x, hex(q[r, c]))
+
+
 def test_block_scale_is_max_of_row_group_amax():
     """A 128x128 block's amax is the max over its 128 rows' 1x128 amaxes, and s = amax/448 is
     monotone, so the block scale equals the max of the row-group scales."""
