@@ -9,6 +9,12 @@ raises.
 Each ``qr_*`` function takes preallocated outputs (like the C ABI).  The ``quant_act``,
 ``quant_w``, ``gemm_*`` and ``uaq_fold`` helpers allocate the outputs with torch and call the
 ``qr_*`` function.
+
+Before a pointer crosses the boundary, each tensor argument is checked: it must live on a GPU,
+have one of the element types the argument takes, have a contiguous last dimension, be
+contiguous where the C call takes no leading dimension for it, and span at least the bytes the
+call will touch from its first element.  A failed check raises ValueError (TypeError for a
+non-tensor) and nothing is launched; the C ABI then validates sizes, alignment and aliasing.
 """
 import ctypes
 import os
@@ -102,6 +108,77 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_KINDS = {}
+
+
+def _kinds(kind):
+    """Element types an argument of the given kind accepts."""
+    if not _KINDS:
+        import torch
+        _KINDS.update({
+            "bf16": (torch.bfloat16, torch.int16, torch.uint16),   # bf16 or its bit patterns
+            "f32": (torch.float32,),
+            "fp8": (torch.uint8, torch.float8_e4m3fn),               # E4M3 codes
+            "u8": (torch.uint8,),
+            "i8": (torch.int8,),
+            "any": None,
+        })
+    return _KINDS[kind]
+
+
+def _arg(t, name, kind, nbytes=0, dense=False):
+    """Device pointer of tensor argument t after the checks in the module docstring; None stays
+    None (the C ABI decides whether NULL is allowed)."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor is on {t.device}; the library takes GPU memory only")
+    _check_layout(t, name, kind, nbytes, dense)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_layout(t, name, kind, nbytes, dense):
+    """The element-type, contiguity and extent checks of _arg (independent of the device)."""
+    kinds = _kinds(kind)
+    if kinds is not None and t.dtype not in kinds:
+        raise ValueError(f"{name}: dtype {t.dtype} not accepted (expected one of {kinds})")
+    if t.numel() > 0:
+        if t.dim() > 0 and t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous (stride 1)")
+        if dense and not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous (the call takes no leading dimension)")
+        span = 1 + sum((d - 1) * st for d, st in zip(t.shape, t.stride()))
+        have = span * t.element_size()
+    else:
+        have = 0
+    if have < nbytes:
+        raise ValueError(f"{name}: spans {have} bytes from its first element; the call needs "
+                         f"{nbytes}")
+
+
+def _need(*dims):
+    """Product of the sizes, or 0 when any is not positive (the C ABI then launches nothing or
+    rejects the shape)."""
+    p = 1
+    for d in dims:
+        if d <= 0:
+            return 0
+        p *= int(d)
+    return p
+
+
+def _strided(rows, cols, ld, elem):
+    """Bytes of a row-major [rows, cols] tensor with leading dimension ld."""
+    return 0 if rows <= 0 or cols <= 0 else ((rows - 1) * ld + cols) * elem
+
+
+def _out_kind(y_dtype):
+    return "bf16" if int(y_dtype) == QR_OUT_BF16 else "f32"
+
+
 def _stream(stream):
     if stream is not None:
         return ctypes.c_void_p(int(stream))
@@ -114,22 +191,34 @@ def _check(status, where):
         raise QRError(status, where)
 
 
-def _bits16(t):
-    """bf16 tensors travel as 16-bit patterns; accept bfloat16 or int16/uint16 views."""
-    return t
-
-
 # ------------------------------------------------------------------ C-ABI mirrors
 
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
 def qr_quant_act_1x128(x, rows, cols, ld_x, q_row, s_row, q_colT, s_colT, stream=None):
-    _check(load().qr_quant_act_1x128(_ptr(x), rows, cols, ld_x, _ptr(q_row), _ptr(s_row),
-                                     _ptr(q_colT), _ptr(s_colT), _stream(stream)),
-           "qr_quant_act_1x128")
+    n, g = _need(rows, cols), _cdiv(cols, 128)
+    _check(load().qr_quant_act_1x128(
+        _arg(x, "x", "bf16", _strided(rows, cols, ld_x, 2)), rows, cols, ld_x,
+        _arg(q_row, "q_row", "fp8", n, True), _arg(s_row, "s_row", "f32", _need(rows, g) * 4, True),
+        _arg(q_colT, "q_colT", "fp8", n, True),
+        _arg(s_colT, "s_colT", "f32", _need(cols, _cdiv(rows, 128)) * 4, True),
+        _stream(stream)), "qr_quant_act_1x128")
+
+
+def _weight_args(w, n, k, ld_w, q, s, qT, sT, where=""):
+    nb = _need(_cdiv(n, 128), _cdiv(k, 128)) * 4 if n > 0 and k > 0 else 0
+    return (_arg(w, where + "w", "bf16", _strided(n, k, ld_w, 2)),
+            _arg(q, where + "q", "fp8", _need(n, k), True), _arg(s, where + "s", "f32", nb, True),
+            _arg(qT, where + "qT", "fp8", _need(n, k), True),
+            _arg(sT, where + "sT", "f32", nb, True))
 
 
 def qr_quant_w_128x128(w, n, k, ld_w, q, s, qT, sT, stream=None):
-    _check(load().qr_quant_w_128x128(_ptr(w), n, k, ld_w, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
-                                     _stream(stream)), "qr_quant_w_128x128")
+    pw, pq, ps, pqT, psT = _weight_args(w, n, k, ld_w, q, s, qT, sT)
+    _check(load().qr_quant_w_128x128(pw, n, k, ld_w, pq, ps, pqT, psT, _stream(stream)),
+           "qr_quant_w_128x128")
 
 
 def qr_quant_w_128x128_batched(items, stream=None):
@@ -137,80 +226,135 @@ def qr_quant_w_128x128_batched(items, stream=None):
     be None)."""
     arr = (qr_weight_desc * max(1, len(items)))()
     for i, (w, n, k, ld_w, q, s_, qT, sT) in enumerate(items):
-        arr[i] = qr_weight_desc(None if w is None else w.data_ptr(), n, k, ld_w,
-                                None if q is None else q.data_ptr(),
-                                None if s_ is None else s_.data_ptr(),
-                                None if qT is None else qT.data_ptr(),
-                                None if sT is None else sT.data_ptr())
+        ptrs = _weight_args(w, n, k, ld_w, q, s_, qT, sT, f"items[{i}].")
+        vals = [None if p is None else p.value for p in ptrs]
+        arr[i] = qr_weight_desc(vals[0], n, k, ld_w, *vals[1:])
     _check(load().qr_quant_w_128x128_batched(arr, len(items), _stream(stream)),
            "qr_quant_w_128x128_batched")
 
 
 def qr_rmsnorm_quant_1x128(h, rows, cols, ld_h, gain, eps, y, q_row, s_row, stream=None):
-    _check(load().qr_rmsnorm_quant_1x128(_ptr(h), rows, cols, ld_h, _ptr(gain), float(eps),
-                                         _ptr(y), _ptr(q_row), _ptr(s_row), _stream(stream)),
-           "qr_rmsnorm_quant_1x128")
+    n = _need(rows, cols)
+    _check(load().qr_rmsnorm_quant_1x128(
+        _arg(h, "h", "bf16", _strided(rows, cols, ld_h, 2)), rows, cols, ld_h,
+        _arg(gain, "gain", "f32", _need(cols) * 4, True), float(eps),
+        _arg(y, "y", "bf16", n * 2, True), _arg(q_row, "q_row", "fp8", n, True),
+        _arg(s_row, "s_row", "f32", _need(rows, _cdiv(cols, 128)) * 4, True), _stream(stream)),
+        "qr_rmsnorm_quant_1x128")
 
 
 def qr_quant_int8_rowwise(x, rows, cols, ld_x, q, s, stream=None):
-    _check(load().qr_quant_int8_rowwise(_ptr(x), rows, cols, ld_x, _ptr(q), _ptr(s),
-                                        _stream(stream)), "qr_quant_int8_rowwise")
+    _check(load().qr_quant_int8_rowwise(
+        _arg(x, "x", "bf16", _strided(rows, cols, ld_x, 2)), rows, cols, ld_x,
+        _arg(q, "q", "i8", _need(rows, cols), True), _arg(s, "s", "f32", _need(rows) * 4, True),
+        _stream(stream)), "qr_quant_int8_rowwise")
 
 
 def qr_gemm_int8_w8a8(a, sa, b, sb, M, N, K, y, y_dtype, ws=None, ws_bytes=0, stream=None):
-    _gemm("qr_gemm_int8_w8a8", a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream)
+    f = load().qr_gemm_int8_w8a8
+    esz = 2 if int(y_dtype) == QR_OUT_BF16 else 4
+    _check(f(_arg(a, "a", "i8", _need(M, K), True), _arg(sa, "sa", "f32", _need(M) * 4, True),
+             _arg(b, "b", "i8", _need(N, K), True), _arg(sb, "sb", "f32", _need(N) * 4, True),
+             M, N, K, _arg(y, "y", _out_kind(y_dtype), _need(M, N) * esz, True), int(y_dtype),
+             _arg(ws, "ws", "any", int(ws_bytes), True), int(ws_bytes), _stream(stream)),
+           "qr_gemm_int8_w8a8")
 
 
 def qr_quant_w_nvfp4(w, n, k, ld_w, codes, bscale, tscale, ws, ws_bytes, stream=None):
-    _check(load().qr_quant_w_nvfp4(_ptr(w), n, k, ld_w, _ptr(codes), _ptr(bscale), _ptr(tscale),
-                                   _ptr(ws), int(ws_bytes), _stream(stream)), "qr_quant_w_nvfp4")
+    _check(load().qr_quant_w_nvfp4(
+        _arg(w, "w", "bf16", _strided(n, k, ld_w, 2)), n, k, ld_w,
+        _arg(codes, "codes", "u8", _need(n, k) // 2, True),
+        _arg(bscale, "bscale", "u8", _need(n, k) // 16, True),
+        _arg(tscale, "tscale", "f32", 4, True), _arg(ws, "ws", "any", int(ws_bytes), True),
+        int(ws_bytes), _stream(stream)), "qr_quant_w_nvfp4")
 
 
 def qr_gemm_w4a16(x, codes, bscale, tscale, M, N, K, y, y_dtype, stream=None):
-    _check(load().qr_gemm_w4a16(_ptr(x), _ptr(codes), _ptr(bscale), _ptr(tscale), M, N, K,
-                                _ptr(y), int(y_dtype), _stream(stream)), "qr_gemm_w4a16")
-
-
-def _gemm(name, a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream):
-    f = getattr(load(), name)
-    _check(f(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(y), int(y_dtype), _ptr(ws),
-             int(ws_bytes), _stream(stream)), name)
+    esz = 2 if int(y_dtype) == QR_OUT_BF16 else 4
+    _check(load().qr_gemm_w4a16(
+        _arg(x, "x", "bf16", _need(M, K) * 2, True),
+        _arg(codes, "codes", "u8", _need(N, K) // 2, True),
+        _arg(bscale, "bscale", "u8", _need(N, K) // 16, True),
+        _arg(tscale, "tscale", "f32", 4 if _need(M, N) else 0, True), M, N, K,
+        _arg(y, "y", _out_kind(y_dtype), _need(M, N) * esz, True), int(y_dtype),
+        _stream(stream)), "qr_gemm_w4a16")
 
 
 def qr_gemm_fp8_bsfprop(a, sa, b, sb, M, N, K, y, y_dtype, ws=None, ws_bytes=0, stream=None):
-    _gemm("qr_gemm_fp8_bsfprop", a, sa, b, sb, M, N, K, y, y_dtype, ws, ws_bytes, stream)
+    f = load().qr_gemm_fp8_bsfprop
+    esz = 2 if int(y_dtype) == QR_OUT_BF16 else 4
+    live = _need(M, N) > 0
+    nk = K // 128 if K > 0 else 0
+    _check(f(_arg(a, "a", "fp8", _need(M, K) if live else 0, True),
+             _arg(sa, "sa", "f32", _need(M, nk) * 4 if live else 0, True),
+             _arg(b, "b", "fp8", _need(N, K) if live else 0, True),
+             _arg(sb, "sb", "f32", _need(_cdiv(N, 128), nk) * 4 if live else 0, True),
+             M, N, K, _arg(y, "y", _out_kind(y_dtype), _need(M, N) * esz, True), int(y_dtype),
+             _arg(ws, "ws", "any", int(ws_bytes), True), int(ws_bytes), _stream(stream)),
+           "qr_gemm_fp8_bsfprop")
 
 
 def qr_gemm_fp8_bsdgrad(dy, sdy, wT, swT, M, N, K, dx, dx_dtype, ws=None, ws_bytes=0,
                         stream=None):
-    _gemm("qr_gemm_fp8_bsdgrad", dy, sdy, wT, swT, M, N, K, dx, dx_dtype, ws, ws_bytes, stream)
+    """dX [M, K] = dY [M, N] . W [N, K], with the transposed weight copy wT [K, N]."""
+    f = load().qr_gemm_fp8_bsdgrad
+    esz = 2 if int(dx_dtype) == QR_OUT_BF16 else 4
+    live = _need(M, K) > 0
+    nn = N // 128 if N > 0 else 0
+    _check(f(_arg(dy, "dy", "fp8", _need(M, N) if live else 0, True),
+             _arg(sdy, "sdy", "f32", _need(M, nn) * 4 if live else 0, True),
+             _arg(wT, "wT", "fp8", _need(K, N) if live else 0, True),
+             _arg(swT, "swT", "f32", _need(_cdiv(K, 128), nn) * 4 if live else 0, True),
+             M, N, K, _arg(dx, "dx", _out_kind(dx_dtype), _need(M, K) * esz, True),
+             int(dx_dtype), _arg(ws, "ws", "any", int(ws_bytes), True), int(ws_bytes),
+             _stream(stream)), "qr_gemm_fp8_bsdgrad")
 
 
 def qr_gemm_fp8_bswgrad(dyT, sdyT, xT, sxT, M, N, K, dw, dw_dtype, ws=None, ws_bytes=0,
                         stream=None):
-    _gemm("qr_gemm_fp8_bswgrad", dyT, sdyT, xT, sxT, M, N, K, dw, dw_dtype, ws, ws_bytes, stream)
+    """dW [N, K] = dY^T . X over M tokens, with dY^T [N, M] and X^T [K, M] (128x1 groups)."""
+    f = load().qr_gemm_fp8_bswgrad
+    esz = 2 if int(dw_dtype) == QR_OUT_BF16 else 4
+    live = _need(N, K) > 0
+    nm = M // 128 if M > 0 else 0
+    _check(f(_arg(dyT, "dyT", "fp8", _need(N, M) if live else 0, True),
+             _arg(sdyT, "sdyT", "f32", _need(N, nm) * 4 if live else 0, True),
+             _arg(xT, "xT", "fp8", _need(K, M) if live else 0, True),
+             _arg(sxT, "sxT", "f32", _need(K, nm) * 4 if live else 0, True),
+             M, N, K, _arg(dw, "dw", _out_kind(dw_dtype), _need(N, K) * esz, True),
+             int(dw_dtype), _arg(ws, "ws", "any", int(ws_bytes), True), int(ws_bytes),
+             _stream(stream)), "qr_gemm_fp8_bswgrad")
 
 
 def qr_gemm_workspace_bytes(kind, M, N, K) -> int:
     return int(load().qr_gemm_workspace_bytes(int(kind), M, N, K))
 
 
+def _same_ptr(a, b):
+    return a is not None and b is not None and a.data_ptr() == b.data_ptr()
+
+
 def qr_uaq_fold(w, n, k, ld_w, s, w_out, gain=None, stream=None):
-    _check(load().qr_uaq_fold(_ptr(w), n, k, ld_w, _ptr(s), _ptr(w_out), _ptr(gain),
-                              _stream(stream)), "qr_uaq_fold")
+    ld_out = ld_w if _same_ptr(w_out, w) else k
+    _check(load().qr_uaq_fold(
+        _arg(w, "w", "bf16", _strided(n, k, ld_w, 2)), n, k, ld_w,
+        _arg(s, "s", "f32", _need(n, k) and k * 4, True),
+        _arg(w_out, "w_out", "bf16", _strided(n, k, ld_out, 2)),
+        _arg(gain, "gain", "f32", _need(n, k) and k * 4, True), _stream(stream)), "qr_uaq_fold")
 
 
 def qr_uaq_fold_quant_w_128x128(w, n, k, ld_w, s, w_out, gain, q, sq, qT=None, sqT=None,
                                 stream=None):
-    _check(load().qr_uaq_fold_quant_w_128x128(_ptr(w), n, k, ld_w, _ptr(s), _ptr(w_out),
-                                              _ptr(gain), _ptr(q), _ptr(sq), _ptr(qT), _ptr(sqT),
-                                              _stream(stream)), "qr_uaq_fold_quant_w_128x128")
+    ld_out = ld_w if _same_ptr(w_out, w) else k
+    pw, pq, ps, pqT, psT = _weight_args(w, n, k, ld_w, q, sq, qT, sqT)
+    _check(load().qr_uaq_fold_quant_w_128x128(
+        pw, n, k, ld_w, _arg(s, "s", "f32", _need(n, k) and k * 4, True),
+        _arg(w_out, "w_out", "bf16", _strided(n, k, ld_out, 2)),
+        _arg(gain, "gain", "f32", _need(n, k) and k * 4, True), pq, ps, pqT, psT,
+        _stream(stream)), "qr_uaq_fold_quant_w_128x128")
 
 
 # ------------------------------------------------------------------ allocating helpers
-
-def _cdiv(a, b):
-    return (a + b - 1) // b
 
 
 def quant_act(x, row=True, col=False, stream=None):

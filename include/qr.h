@@ -35,6 +35,14 @@
  *   - Dequantized value = code value * group scale.  GEMMs accumulate in fp32 with the scale
  *     product applied once per 128-element contraction group; outputs are fp32 or bf16
  *     (round to nearest even).
+ *   - Domain of the FP8 GEMMs' accuracy bound (|y - Y| <= 2e-3 * sum_k |a_k b_k| per output,
+ *     Y the exact result): the binary32 product sA * sB of two non-zero group scales that
+ *     meet in an output must be at least 2^-126 (binary32's smallest normal), i.e. their
+ *     group amax values must multiply to at least about 2^-108.4, and every output and
+ *     partial sum must stay below 2^128.  Zero groups (scale 0) are always exact.  Outside
+ *     that range the scale product or the output leaves binary32's normal range and the
+ *     bound can fail; nothing is reported.  For bf16 inputs it holds whenever every group
+ *     amax lies in [2^-54, 2^56] and the outputs fit binary32.
  *   - Inputs must be finite.  Non-finite input is not detected on the GPU; the results are
  *     then undefined, but every access stays in bounds.
  *
@@ -297,14 +305,16 @@ size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K);
  *   s      fp32 [k], every s[c] finite and > 0 (not checked on the GPU).
  *   gain   fp32 [k] or NULL: the gain of the norm that feeds this layer.
  * Run once, before training; the fold is NOT idempotent (a second call divides by s again).
- * Size rules: n, k >= 0; k % 8 == 0, ld_w % 8 == 0; w, w_out 16-byte aligned.
+ * Size rules: n, k >= 0; k % 8 == 0, ld_w % 8 == 0; w, w_out and s 16-byte aligned, gain_inout
+ * 4-byte aligned.  w_out must not overlap s or gain_inout, nor gain_inout w or s.
  */
 qr_status qr_uaq_fold(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, const float *s,
                       void *w_out_bf16, float *gain_inout, qr_stream stream);
 
 /*
- * UAQ fold followed by the 128x128 weight quantization, in one pass over w [QURL: s folded
- * into the weights once; JET / DeepSeek-V3 fine-grained quantization: 128x128 weight blocks].
+ * UAQ fold followed by the 128x128 weight quantization, in one pass over w [QURL, key design
+ * 1: s folded into the weights once; JET, fine-grained GEMM quantization scheme: 128x128
+ * weight blocks].
  * The outputs equal those of qr_uaq_fold(w, n, k, ld_w, s, w_out, gain_inout) followed by
  * qr_quant_w_128x128(w_out, n, k, ld_out, q, sq, qT, sqT), bit for bit, where ld_out is ld_w
  * in place and k otherwise; w is read once and the folded weight is not read back.

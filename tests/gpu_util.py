@@ -40,19 +40,20 @@ def assert_bitexact(gpu: np.ndarray, ref: np.ndarray, what: str):
 
 
 def assert_gemm_close(gpu: np.ndarray, Y: np.ndarray, S: np.ndarray, what: str,
-                      bf16_out: bool = False):
+                      bf16_out: bool = False, literal: bool = False):
     """Element-wise |gpu - Y| <= GEMM_TOL * S against the unrounded fp64 oracle Y.
 
     The tolerance covers the fp32 accumulation.  A bf16 output adds one more rounding of that
     fp32 value y (nearest even, at most 2^-8 |y| with |y| <= |Y| + GEMM_TOL * S), which on its
     own can exceed GEMM_TOL * S wherever |Y| / S > ~0.5; for bf16 outputs that rounding is
-    added to the bound.  Returns (max err/S, max |Y|/S)."""
+    added to the bound, unless `literal` asks for the bare GEMM_TOL * S (the named workloads,
+    whose |Y| / S stays far below 0.5).  Returns (max err/S, max |Y|/S)."""
     gpu = np.asarray(gpu, np.float64)
     assert gpu.shape == Y.shape == S.shape, (what, gpu.shape, Y.shape)
     assert np.all(np.isfinite(gpu)), what
     err = np.abs(gpu - Y)
     lim = GEMM_TOL * S
-    if bf16_out:
+    if bf16_out and not literal:
         lim = lim + 2.0 ** -8 * (np.abs(Y) + GEMM_TOL * S)
     bad = np.flatnonzero(err.ravel() > lim.ravel())
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -80,3 +81,114 @@ def sample_positions(M, N, count, seed, tile=128):
     mi.append(rng.integers(0, M, en.size))
     ni.append(en)
     return np.concatenate(mi).astype(np.int64), np.concatenate(ni).astype(np.int64)
+
+
+# ------------------------------------------------------------------ guarded outputs
+
+GUARD = 4096          # bytes of pattern before and after every output buffer
+GUARD_BYTE = 0xA5     # also the initial content of the output itself, so an element the
+                      # kernel never writes cannot pass a bit-exact comparison by chance
+
+
+def guarded_empty(shape, dtype, checks):
+    """An output tensor inside a larger buffer whose guard bands (and body) hold GUARD_BYTE;
+    appends a closure to `checks` that asserts the bands are untouched."""
+    shape = tuple(int(d) for d in shape)
+    elem = torch.empty((), dtype=dtype).element_size()
+    nbytes = int(np.prod(shape, dtype=np.int64)) * elem
+    raw = torch.full((nbytes + 2 * GUARD,), GUARD_BYTE, dtype=torch.uint8, device="cuda:0")
+    body = raw[GUARD:GUARD + nbytes]
+    t = body.view(dtype).view(shape) if nbytes else torch.empty(shape, dtype=dtype, device="cuda:0")
+
+    def check(what="output"):
+        torch.cuda.synchronize()
+        lo = raw[:GUARD].cpu().numpy()
+        hi = raw[GUARD + nbytes:].cpu().numpy()
+        assert np.all(lo == GUARD_BYTE), f"{what} {shape}: write before the buffer"
+        assert np.all(hi == GUARD_BYTE), f"{what} {shape}: write past the buffer"
+
+    checks.append(check)
+    return t
+
+
+def _run_checks(checks):
+    for c in checks:
+        c()
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def g_quant_act(qr, x, row=True, col=False):
+    """qr.quant_act with guarded outputs (checked after the call)."""
+    rows, cols = x.shape
+    ch = []
+    q = s = qT = sT = None
+    if row:
+        q = guarded_empty((rows, cols), torch.uint8, ch)
+        s = guarded_empty((rows, _cdiv(cols, 128)), torch.float32, ch)
+    if col:
+        qT = guarded_empty((cols, rows), torch.uint8, ch)
+        sT = guarded_empty((cols, _cdiv(rows, 128)), torch.float32, ch)
+    qr.qr_quant_act_1x128(x, rows, cols, x.stride(0), q, s, qT, sT)
+    _run_checks(ch)
+    return q, s, qT, sT
+
+
+def g_quant_w(qr, w, transposed=False):
+    n, k = w.shape
+    ch = []
+    q = guarded_empty((n, k), torch.uint8, ch)
+    s = guarded_empty((_cdiv(n, 128), _cdiv(k, 128)), torch.float32, ch)
+    qT = sT = None
+    if transposed:
+        qT = guarded_empty((k, n), torch.uint8, ch)
+        sT = guarded_empty((_cdiv(k, 128), _cdiv(n, 128)), torch.float32, ch)
+    qr.qr_quant_w_128x128(w, n, k, w.stride(0), q, s, qT, sT)
+    _run_checks(ch)
+    return q, s, qT, sT
+
+
+def _od(qr, out_dtype):
+    return qr.QR_OUT_BF16 if out_dtype is None else out_dtype
+
+
+def _g_out_ws(qr, kind, M, N, K, out_dtype, rows, cols, ch):
+    if out_dtype is None:
+        out_dtype = qr.QR_OUT_BF16
+    dt = torch.bfloat16 if out_dtype == qr.QR_OUT_BF16 else torch.float32
+    y = guarded_empty((rows, cols), dt, ch)
+    nb = qr.qr_gemm_workspace_bytes(kind, M, N, K)
+    ws = guarded_empty((nb,), torch.uint8, ch) if nb else None
+    return y, ws, nb
+
+
+def g_gemm_fprop(qr, a, sa, b, sb, out_dtype=None):
+    M, K = a.shape
+    N = b.shape[0]
+    ch = []
+    y, ws, nb = _g_out_ws(qr, qr.QR_GEMM_FPROP, M, N, K, out_dtype, M, N, ch)
+    qr.qr_gemm_fp8_bsfprop(a, sa, b, sb, M, N, K, y, _od(qr, out_dtype), ws, nb)
+    _run_checks(ch)
+    return y
+
+
+def g_gemm_dgrad(qr, dy, sdy, wT, swT, out_dtype=None):
+    M, N = dy.shape
+    K = wT.shape[0]
+    ch = []
+    dx, ws, nb = _g_out_ws(qr, qr.QR_GEMM_DGRAD, M, N, K, out_dtype, M, K, ch)
+    qr.qr_gemm_fp8_bsdgrad(dy, sdy, wT, swT, M, N, K, dx, _od(qr, out_dtype), ws, nb)
+    _run_checks(ch)
+    return dx
+
+
+def g_gemm_wgrad(qr, dyT, sdyT, xT, sxT, out_dtype=None):
+    N, M = dyT.shape
+    K = xT.shape[0]
+    ch = []
+    dw, ws, nb = _g_out_ws(qr, qr.QR_GEMM_WGRAD, M, N, K, out_dtype, N, K, ch)
+    qr.qr_gemm_fp8_bswgrad(dyT, sdyT, xT, sxT, M, N, K, dw, _od(qr, out_dtype), ws, nb)
+    _run_checks(ch)
+    return dw

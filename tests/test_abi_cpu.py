@@ -271,3 +271,51 @@ def test_uaq_validation(L):
     assert f(A, 4, 128, 128, B, A + 256, None, None) == ALIAS          # partial overlap
     assert f(A, 4, 128, 128, B, C, B, None) == ALIAS                   # gain over s
     assert f(A, 0, 128, 128, B, C, D, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    """Every binding entry point raises before the call when handed host memory (a host
+    pointer in a kernel would fault the device)."""
+    import torch
+    x = torch.zeros((8, 128), dtype=torch.bfloat16)
+    codes = torch.zeros((8, 128), dtype=torch.uint8)
+    sc = torch.zeros((8, 1), dtype=torch.float32)
+    y = torch.zeros((8, 128), dtype=torch.float32)
+    calls = [
+        lambda: qr.qr_quant_act_1x128(x, 8, 128, 128, codes, sc, None, None),
+        lambda: qr.qr_quant_w_128x128(x, 8, 128, 128, codes, sc, None, None),
+        lambda: qr.qr_quant_w_128x128_batched([(x, 8, 128, 128, codes, sc, None, None)]),
+        lambda: qr.qr_rmsnorm_quant_1x128(x, 8, 128, 128, sc, 1e-6, None, codes, sc),
+        lambda: qr.qr_quant_int8_rowwise(x, 8, 128, 128, codes.view(torch.int8), sc),
+        lambda: qr.qr_gemm_fp8_bsfprop(codes, sc, codes, sc, 8, 128, 128, y, qr.QR_OUT_F32),
+        lambda: qr.qr_gemm_fp8_bsdgrad(codes, sc, codes, sc, 8, 128, 128, y, qr.QR_OUT_F32),
+        lambda: qr.qr_gemm_fp8_bswgrad(codes, sc, codes, sc, 128, 8, 8, y, qr.QR_OUT_F32),
+        lambda: qr.qr_uaq_fold(x, 8, 128, 128, sc, x),
+        lambda: qr.quant_act(x), lambda: qr.quant_w(x), lambda: qr.gemm_fprop(codes, sc, codes, sc),
+    ]
+    for c in calls:
+        with pytest.raises(ValueError, match="GPU memory only"):
+            c()
+    with pytest.raises(TypeError):
+        qr.qr_quant_act_1x128(123, 8, 128, 128, None, None, None, None)
+
+
+def test_binding_layout_checks():
+    """The dtype, contiguity and extent checks the binding applies to every tensor argument."""
+    import torch
+    w = torch.zeros((256, 640), dtype=torch.bfloat16)
+    qr._check_layout(w[:, 64:448], "w", "bf16", (255 * 640 + 384) * 2, False)   # strided rows ok
+    with pytest.raises(ValueError, match="last dimension"):
+        qr._check_layout(w[:, ::2], "w", "bf16", 2, False)                       # column stride 2
+    with pytest.raises(ValueError, match="contiguous"):
+        qr._check_layout(w[:, :128], "q", "bf16", 2, True)                        # dense required
+    with pytest.raises(ValueError, match="spans"):
+        qr._check_layout(w[:2], "w", "bf16", 3 * 640 * 2, False)                  # too short
+    with pytest.raises(ValueError, match="dtype"):
+        qr._check_layout(w.float(), "x", "bf16", 0, False)
+    with pytest.raises(ValueError, match="dtype"):
+        qr._check_layout(torch.zeros(4, dtype=torch.int8), "q", "fp8", 0, True)
+    qr._check_layout(torch.zeros(4, dtype=torch.int16), "x", "bf16", 8, True)     # bit patterns
+    qr._check_layout(torch.zeros(0, dtype=torch.float32), "ws", "any", 0, True)   # empty, none needed
+    with pytest.raises(ValueError, match="spans"):
+        qr._check_layout(torch.zeros(0, dtype=torch.uint8), "ws", "any", 16, True)

@@ -2,8 +2,9 @@
 
 Codes and scales must match bit for bit; GEMM outputs must satisfy
 |gpu - oracle| <= 2e-3 * sum_k |a_k b_k| per element against the unrounded fp64 oracle.
-Small cases compare every element; the full-size workloads compare the quantizers in full and
-the GEMMs on sampled outputs that the oracle computes one by one.
+Every output is compared in full, at the named workloads' full sizes too (there with the bare
+2e-3 bound, no allowance for the bf16 output rounding); a few extra shapes are sampled.
+Quantizer and GEMM outputs sit between guard bands whose pattern must survive each call.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,8 @@ import torch
 import fp8_block_scaled_qr_amd as qr
 import oracle
 import qr_synth
-from gpu_util import (assert_bitexact, assert_gemm_close, dev, dev_bf16, host, out_f64,
+from gpu_util import (assert_bitexact, assert_gemm_close, dev, dev_bf16, g_gemm_dgrad,
+                      g_gemm_fprop, g_gemm_wgrad, g_quant_act, g_quant_w, host, out_f64,
                       sample_positions)
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +41,7 @@ ACT_SHAPES = [(256, 512, "tiny_fprop X"), (77, 200, "ragged rows and partial gro
 def test_quant_rows(rows, cols, name):
     say("quant_rows", rows, cols, name)
     x = qr_synth.normal_bf16(rows * 7 + cols, (rows, cols), 1.0, 99, max(1, cols // 100))
-    q, s, _, _ = qr.quant_act(dev_bf16(x), row=True, col=False)
+    q, s, _, _ = g_quant_act(qr, dev_bf16(x), row=True, col=False)
     rq, rs = oracle.quant_rows(x)
     assert_bitexact(host(q), rq, "codes")
     assert_bitexact(host(s), rs, "scales")
@@ -57,7 +59,7 @@ def test_quant_dual_and_colT(rows, cols, name):
     x = (qr_synth.backward_8b_dy() if rows == 8192 else
          qr_synth.normal_bf16(rows + cols, (rows, cols), std, 5, 2))
     xd = dev_bf16(x)
-    q, s, qT, sT = qr.quant_act(xd, row=True, col=True)
+    q, s, qT, sT = g_quant_act(qr, xd, row=True, col=True)
     rq, rs = oracle.quant_rows(x)
     rqT, rsT = oracle.quant_cols_T(x)
     assert_bitexact(host(q), rq, "row codes")
@@ -65,7 +67,7 @@ def test_quant_dual_and_colT(rows, cols, name):
     assert_bitexact(host(qT), rqT, "colT codes")
     assert_bitexact(host(sT), rsT, "colT scales")
     # column-only pass (X's WGrad operand) gives the same column outputs
-    _, _, qT2, sT2 = qr.quant_act(xd, row=False, col=True)
+    _, _, qT2, sT2 = g_quant_act(qr, xd, row=False, col=True)
     assert_bitexact(host(qT2), rqT, "colT-only codes")
     assert_bitexact(host(sT2), rsT, "colT-only scales")
 
@@ -79,7 +81,7 @@ W_SHAPES = [(512, 512, "tiny_fprop W"), (200, 136, "ragged blocks"),
 def test_quant_w(n, k, name):
     say("quant_w", n, k, name)
     w = qr_synth.normal_bf16(n + 3 * k, (n, k), 0.02)
-    q, s, qT, sT = qr.quant_w(dev_bf16(w), transposed=True)
+    q, s, qT, sT = g_quant_w(qr, dev_bf16(w), transposed=True)
     rq, rs = oracle.quant_blocks(w)
     assert_bitexact(host(q), rq, "codes")
     assert_bitexact(host(s), rs, "scales")
@@ -255,18 +257,16 @@ def test_gemm_int8_empty_zero_k_and_workspace_reuse():
 @pytest.mark.parametrize("M,N,K", [(8192, 4096, 4096), (64, 14336, 4096), (256, 5120, 27648),
                                    (256, 55296, 5120), (200, 32768, 256), (256, 7168, 5120),
                                    (64, 4096, 14336)])
-def test_gemm_int8_full_size_sampled(M, N, K):
+def test_gemm_int8_full_size(M, N, K):
     """The 8B prefill shape, the 8B decode shape, the 32B down (K split 12 ways) and gate+up
     projections at batch 256, a ragged-M batch on the 256x256 tiles (128 tiles, the smallest
     count that takes them without a split), the 32B QKV at batch 256 (split 8 ways) and the 8B
-    down at batch 64 (narrow tiles, split 2 ways), on sampled outputs (every tile and both
-    ragged ends hit)."""
+    down at batch 64 (narrow tiles, split 2 ways); every output."""
     say("gemm_int8 full", M, N, K)
     qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
     y = out_f64(qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_BF16))
-    mi, ni = sample_positions(M, N, 4096, seed=M + N)
-    Y = oracle.gemm_int8(qa, sa, qb, sb, sample=(mi, ni))
-    _check_int8(y[mi, ni], Y, qr.QR_OUT_BF16)
+    Y = oracle.gemm_int8(qa, sa, qb, sb)
+    _check_int8(y, Y, qr.QR_OUT_BF16)
 
 
 FP4_W = [(64, 128), (200, 96), (1, 32), (4096, 4096), (14336, 4096)]
@@ -347,7 +347,7 @@ def test_quant_strided_input():
     say("quant strided ld")
     big = qr_synth.normal_bf16(11, (96, 640), 1.0)
     xd = dev_bf16(big)[:, 64:64 + 384]          # ld = 640, cols = 384
-    q, s, qT, sT = qr.quant_act(xd, row=True, col=True)
+    q, s, qT, sT = g_quant_act(qr, xd, row=True, col=True)
     sub = np.ascontiguousarray(big[:, 64:448])
     rq, rs = oracle.quant_rows(sub)
     rqT, rsT = oracle.quant_cols_T(sub)
@@ -357,7 +357,7 @@ def test_quant_strided_input():
     assert_bitexact(host(sT), rsT, "colT scales")
     # rows only: 96 rows take the few-rows kernel (one wave per 512-column slice; the slice
     # holds 3 of its 4 groups here)
-    q1, s1, _, _ = qr.quant_act(xd, row=True, col=False)
+    q1, s1, _, _ = g_quant_act(qr, xd, row=True, col=False)
     assert_bitexact(host(q1), rq, "codes, few-rows kernel")
     assert_bitexact(host(s1), rs, "scales, few-rows kernel")
 
@@ -389,7 +389,7 @@ def test_codes_every_bf16_for_sampled_scales():
     x = _groups_for_amax(np.array(picks, np.uint16))
     for r0 in range(0, x.shape[0], 1 << 19):
         part = np.ascontiguousarray(x[r0:r0 + (1 << 19)])
-        q, s, _, _ = qr.quant_act(dev_bf16(part), row=True)
+        q, s, _, _ = g_quant_act(qr, dev_bf16(part), row=True)
         rq, rs = oracle.quant_rows(part)
         assert_bitexact(host(s), rs, "scales")
         assert_bitexact(host(q), rq, "codes")
@@ -407,7 +407,7 @@ def test_quant_special_values():
     x[6, ::2] = 0x7F7F                                 # max finite bf16 and its negative
     x[6, 1::2] = 0xFF7F
     x[7, :] = qr_synth.f32_to_bf16_bits((np.arange(256) - 128).astype(np.float32) * 2.0 ** -130)
-    q, s, qT, sT = qr.quant_act(dev_bf16(x), row=True, col=True)
+    q, s, qT, sT = g_quant_act(qr, dev_bf16(x), row=True, col=True)
     rq, rs = oracle.quant_rows(x)
     rqT, rsT = oracle.quant_cols_T(x)
     assert_bitexact(host(q), rq, "codes")
@@ -415,11 +415,11 @@ def test_quant_special_values():
     assert_bitexact(host(qT), rqT, "colT codes")
     assert_bitexact(host(sT), rsT, "colT scales")
     # rows only (16 rows: the few-rows kernel, incl. its lifted quotient for tiny scales)
-    q1, s1, _, _ = qr.quant_act(dev_bf16(x), row=True, col=False)
+    q1, s1, _, _ = g_quant_act(qr, dev_bf16(x), row=True, col=False)
     assert_bitexact(host(q1), rq, "codes, few-rows kernel")
     assert_bitexact(host(s1), rs, "scales, few-rows kernel")
     w = np.ascontiguousarray(np.tile(x, (8, 1))[:128])
-    qw, sw, _, _ = qr.quant_w(dev_bf16(w))
+    qw, sw, _, _ = g_quant_w(qr, dev_bf16(w))
     rqw, rsw = oracle.quant_blocks(w)
     assert_bitexact(host(qw), rqw, "block codes")
     assert_bitexact(host(sw), rsw, "block scales")
@@ -482,7 +482,7 @@ def test_uaq_fold_quant_w_fused(n, k, transposed):
         assert_bitexact(host(sqT), np.ascontiguousarray(rs.T), "transposed scales")
     # the separate entry points give the same bits
     f2 = qr.uaq_fold(wd, sd)
-    q2, s2, qT2, sT2 = qr.quant_w(f2, transposed=transposed)
+    q2, s2, qT2, sT2 = g_quant_w(qr, f2, transposed=transposed)
     assert torch.equal(f2, out) and torch.equal(q2, q) and torch.equal(s2, sq)
     if transposed:
         assert torch.equal(qT2, qT) and torch.equal(sT2, sqT)
@@ -544,12 +544,12 @@ def test_uaq_fold_edges_and_ragged(n, k):
 
 # ================================================================= GEMMs
 
-def _fprop_case(lin, x, w, out_dtype, sample=None, name=""):
+def _fprop_case(lin, x, w, out_dtype, sample=None, name="", literal=False):
     say("fprop", lin.M if lin else x.shape, name)
     xd, wd = dev_bf16(x), dev_bf16(w)
-    qa, sa, _, _ = qr.quant_act(xd, row=True)
-    qw, sw, _, _ = qr.quant_w(wd)
-    y = qr.gemm_fprop(qa, sa, qw, sw, out_dtype=out_dtype)
+    qa, sa, _, _ = g_quant_act(qr, xd, row=True)
+    qw, sw, _, _ = g_quant_w(qr, wd)
+    y = g_gemm_fprop(qr, qa, sa, qw, sw, out_dtype=out_dtype)
     ra, rsa = oracle.quant_rows(x)
     rw, rsw = oracle.quant_blocks(w)
     assert_bitexact(host(qa), ra, "A codes")
@@ -558,15 +558,15 @@ def _fprop_case(lin, x, w, out_dtype, sample=None, name=""):
     bf = out_dtype == qr.QR_OUT_BF16
     if sample is None:
         Y, S = oracle.fprop(ra, rsa, rw, rsw)
-        return assert_gemm_close(yg, Y, S, name, bf)
+        return assert_gemm_close(yg, Y, S, name, bf, literal)
     mi, ni = sample
     Y, S = oracle.fprop(ra, rsa, rw, rsw, sample=(mi, ni))
-    return assert_gemm_close(yg[mi, ni], Y, S, name, bf)
+    return assert_gemm_close(yg[mi, ni], Y, S, name, bf, literal)
 
 
 def test_fprop_tiny_fp32_full():
     lin = qr_synth.tiny_fprop()
-    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_F32, name="tiny_fprop"))
+    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_F32, name="tiny_fprop", literal=True))
 
 
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (1, 128, 128), (300, 264, 256),
@@ -580,7 +580,13 @@ def test_fprop_tiny_fp32_full():
                                    (64, 264, 1280), (16, 8, 128),
                                    # decode batches on narrow weights: K split across
                                    # workgroups (2 and 3 splits, the last one shorter)
-                                   (40, 1000, 2304), (64, 520, 3200)])
+                                   (40, 1000, 2304), (64, 520, 3200),
+                                   # N % 4 != 0: the scalar tail of every output store (256x256
+                                   # tiles with and without a K split, the decode kernel with
+                                   # and without one, the split reduction over an odd M * N)
+                                   (77, 77, 384), (2048, 4097, 128), (300, 201, 256),
+                                   (5, 13, 1152), (40, 14337, 256), (64, 1001, 2304),
+                                   (1, 3, 128)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_fprop_shapes_full(M, N, K, out):
     x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 7, max(1, K // 100))
@@ -588,26 +594,72 @@ def test_fprop_shapes_full(M, N, K, out):
     print(_fprop_case(None, x, w, out, name=f"{M}x{N}x{K}"))
 
 
-def test_fprop_decode_8b_sampled():
+def test_fprop_decode_8b_full():
     lin = qr_synth.decode_8b()
-    smp = sample_positions(lin.M, lin.N, 4096, 1)
-    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, smp, "decode_8b"))
+    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, None, "decode_8b", literal=True))
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 14336), (64, 5120, 27648)])
-def test_fprop_decode_narrow_sampled(M, N, K):
+def test_fprop_decode_narrow_full(M, N, K):
     """Decode batch 64 against the 8B down projection and the 32B one: the weight is narrow,
-    so K is split across workgroups (4 and 3 splits); sampled outputs."""
+    so K is split across workgroups; every output."""
     x = qr_synth.normal_bf16(M + K, (M, K), 1.0, 11, max(1, K // 100))
     w = qr_synth.normal_bf16(N + K, (N, K), 0.02)
-    smp = sample_positions(M, N, 4096, 5)
-    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, smp, f"{M}x{N}x{K}"))
+    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, None, f"{M}x{N}x{K}", literal=True))
 
 
-def test_fprop_prefill_8b_sampled():
+def test_fprop_prefill_8b_full():
     lin = qr_synth.prefill_8b()
-    smp = sample_positions(lin.M, lin.N, 4096, 2)
-    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, smp, "prefill_8b"))
+    print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, None, "prefill_8b", literal=True))
+
+
+def _pow2_scaled(bits, exps, axis):
+    """bf16 tensor with slice i along `axis` (rows or columns) multiplied by 2^exps[i % len]
+    (exact in bf16 while the result stays normal)."""
+    f = qr_synth.bf16_bits_to_f32(bits).astype(np.float64)
+    e = np.array([exps[i % len(exps)] for i in range(f.shape[axis])], np.float64)
+    f = f * (2.0 ** (e[:, None] if axis == 0 else e[None, :]))
+    return qr_synth.f32_to_bf16_bits(f.astype(np.float32))
+
+
+def test_fprop_extreme_group_scales():
+    """Group scales far from 1 inside the documented domain (every product sA * sB of two
+    non-zero group scales at least 2^-126, every output below 2^128), zero groups (scale 0)
+    and groups of negative zeros (codes 0x80): rows of A carry 2^-54 .. 2^60, 128-row blocks
+    of the weight 2^-50 .. 2^56, so the scale products span about 2^-123 .. 2^101."""
+    say("fprop extreme scales")
+    M, N, K = 300, 384, 768
+    x = _pow2_scaled(qr_synth.normal_bf16(61, (M, K), 1.0, 62, 8), [-54, -30, 0, 30, 60], 0)
+    x[3::7, 256:384] = 0x0000                          # a zero group per 7th row
+    x[5::7, 512:640] = 0x8000                          # a group of negative zeros
+    w = _pow2_scaled(qr_synth.normal_bf16(63, (N, K), 0.02), [-50] * 128 + [0] * 128 + [56] * 128, 0)
+    w[128:256, 384:512] = 0x0000                       # a zero weight block
+    for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
+        print(_fprop_case(None, x, w, out, None, f"extreme scales out={out}"))
+    # the tile path with a K split over the same operands (M <= 256: 2 tiles of 256x256)
+    print(_fprop_case(None, np.ascontiguousarray(x[:200]), w, qr.QR_OUT_F32, None,
+                      "extreme scales, K split"))
+
+
+def test_wgrad_extreme_group_scales():
+    """WGrad's outer-product promotion with per-channel scales 2^-50 .. 2^56 on both operands,
+    a zero token group and a group of negative zeros, compared in full."""
+    say("wgrad extreme scales")
+    M, N, K = 384, 264, 520
+    dy = _pow2_scaled(qr_synth.normal_bf16(65, (M, N), 1e-3), [-40, -10, 0, 20, 50], 1)
+    x = _pow2_scaled(qr_synth.normal_bf16(66, (M, K), 1.0, 67, 5), [-50, 0, 30, 56], 1)
+    dy[128:256, 7::11] = 0x0000
+    x[256:384, 3::13] = 0x8000
+    _, _, qdyT, sdyT = g_quant_act(qr, dev_bf16(dy), row=False, col=True)
+    _, _, qxT, sxT = g_quant_act(qr, dev_bf16(x), row=False, col=True)
+    rdyT, rsdyT = oracle.quant_cols_T(dy)
+    rxT, rsxT = oracle.quant_cols_T(x)
+    assert_bitexact(host(qdyT), rdyT, "dY^T codes")
+    assert_bitexact(host(qxT), rxT, "X^T codes")
+    Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT)
+    for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
+        dw = g_gemm_wgrad(qr, qdyT, sdyT, qxT, sxT, out_dtype=out)
+        print("wgrad extreme", assert_gemm_close(out_f64(dw), Y, S, "wgrad", out == qr.QR_OUT_BF16))
 
 
 def test_fprop_empty_and_zero_k():
@@ -627,27 +679,28 @@ def _backward_operands():
     return x, w, dy
 
 
-def test_backward_8b_dgrad_wgrad_sampled():
+def test_backward_8b_dgrad_wgrad_full():
     say("backward_8b")
     x, w, dy = _backward_operands()
     xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
-    qdy, sdy, qdyT, sdyT = qr.quant_act(dyd, row=True, col=True)
-    _, _, qxT, sxT = qr.quant_act(xd, row=False, col=True)
-    _, _, qwT, swT = qr.quant_w(wd, transposed=True)
-    dx = qr.gemm_dgrad(qdy, sdy, qwT, swT)
-    dw = qr.gemm_wgrad(qdyT, sdyT, qxT, sxT)
+    qdy, sdy, qdyT, sdyT = g_quant_act(qr, dyd, row=True, col=True)
+    _, _, qxT, sxT = g_quant_act(qr, xd, row=False, col=True)
+    _, _, qwT, swT = g_quant_w(qr, wd, transposed=True)
+    dx = g_gemm_dgrad(qr, qdy, sdy, qwT, swT)
+    dw = g_gemm_wgrad(qr, qdyT, sdyT, qxT, sxT)
     rdy, rsdy = oracle.quant_rows(dy)
     rdyT, rsdyT = oracle.quant_cols_T(dy)
     rxT, rsxT = oracle.quant_cols_T(x)
     rw, rsw = oracle.quant_blocks(w)
     assert_bitexact(host(qwT), np.ascontiguousarray(rw.T), "W^T codes")
     assert_bitexact(host(qxT), rxT, "X^T codes")
-    smp = sample_positions(8192, 4096, 4096, 3)
-    Y, S = oracle.dgrad(rdy, rsdy, rw, rsw, sample=smp)
-    print("dgrad", assert_gemm_close(out_f64(dx)[smp], Y, S, "dgrad", True))
-    smp = sample_positions(4096, 4096, 4096, 4)
-    Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT, sample=smp)
-    print("wgrad", assert_gemm_close(out_f64(dw)[smp], Y, S, "wgrad", True))
+    assert_bitexact(host(qdy), rdy, "dY row codes")
+    assert_bitexact(host(qdyT), rdyT, "dY^T codes")
+    Y, S = oracle.dgrad(rdy, rsdy, rw, rsw)
+    print("dgrad", assert_gemm_close(out_f64(dx), Y, S, "dgrad", True, literal=True))
+    del Y, S
+    Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT)
+    print("wgrad", assert_gemm_close(out_f64(dw), Y, S, "wgrad", True, literal=True))
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (384, 200, 384), (128, 77, 1024),
@@ -666,16 +719,16 @@ def test_dgrad_wgrad_small_full(M, N, K):
     dy_p[:, :N] = dy
     w = np.zeros((n_pad, K), np.uint16)
     w[:N] = qr_synth.normal_bf16(N * K, (N, K), 0.02)
-    qdy, sdy, qdyT, sdyT = qr.quant_act(dev_bf16(dy_p), row=True, col=True)
-    _, _, qxT, sxT = qr.quant_act(dev_bf16(x), row=False, col=True)
-    _, _, qwT, swT = qr.quant_w(dev_bf16(w), transposed=True)
+    qdy, sdy, qdyT, sdyT = g_quant_act(qr, dev_bf16(dy_p), row=True, col=True)
+    _, _, qxT, sxT = g_quant_act(qr, dev_bf16(x), row=False, col=True)
+    _, _, qwT, swT = g_quant_w(qr, dev_bf16(w), transposed=True)
     for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
-        dx = qr.gemm_dgrad(qdy, sdy, qwT, swT, out_dtype=out)
+        dx = g_gemm_dgrad(qr, qdy, sdy, qwT, swT, out_dtype=out)
         rdy, rsdy = oracle.quant_rows(dy_p)
         rw, rsw = oracle.quant_blocks(w)
         Y, S = oracle.dgrad(rdy, rsdy, rw, rsw)
         assert_gemm_close(out_f64(dx), Y, S, "dgrad", out == qr.QR_OUT_BF16)
-        dw = qr.gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=out)
+        dw = g_gemm_wgrad(qr, qdyT, sdyT, qxT, sxT, out_dtype=out)
         rdyT, rsdyT = oracle.quant_cols_T(dy_p)
         rxT, rsxT = oracle.quant_cols_T(x)
         Y, S = oracle.wgrad(rdyT, rsdyT, rxT, rsxT)
@@ -688,18 +741,18 @@ def test_dgrad_decode_batch_full(M, N, K):
     say("dgrad small M", M, N, K)
     dy = qr_synth.normal_bf16(M + N + 5, (M, N), 1e-3)
     w = qr_synth.normal_bf16(N * K + 5, (N, K), 0.02)
-    qdy, sdy, _, _ = qr.quant_act(dev_bf16(dy), row=True)
-    _, _, qwT, swT = qr.quant_w(dev_bf16(w), transposed=True)
+    qdy, sdy, _, _ = g_quant_act(qr, dev_bf16(dy), row=True)
+    _, _, qwT, swT = g_quant_w(qr, dev_bf16(w), transposed=True)
     rdy, rsdy = oracle.quant_rows(dy)
     rw, rsw = oracle.quant_blocks(w)
     for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
-        dx = qr.gemm_dgrad(qdy, sdy, qwT, swT, out_dtype=out)
+        dx = g_gemm_dgrad(qr, qdy, sdy, qwT, swT, out_dtype=out)
         Y, S = oracle.dgrad(rdy, rsdy, rw, rsw)
         assert_gemm_close(out_f64(dx), Y, S, "dgrad", out == qr.QR_OUT_BF16)
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 3])
-def test_decode_32b_set_sampled(idx):
+def test_decode_32b_set_full(idx):
     lin = qr_synth.decode_32b_set()[idx]
     say("decode_32b", lin.name, lin.M, lin.N, lin.K)
     w, s, x = lin.w(), lin.uaq_s(), lin.x()
@@ -708,8 +761,7 @@ def test_decode_32b_set_sampled(idx):
     rwf, _ = oracle.uaq_fold(w, s)
     assert_bitexact(host(wf), rwf, "folded W")
     del wd
-    smp = sample_positions(lin.M, lin.N, 4096, 10 + idx)
-    print(_fprop_case(lin, x, rwf, qr.QR_OUT_BF16, smp, lin.name))
+    print(_fprop_case(lin, x, rwf, qr.QR_OUT_BF16, None, lin.name, literal=True))
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 14336, 4096),    # decode, no split
@@ -722,8 +774,8 @@ def test_gemm_deterministic(M, N, K):
     say("determinism", M, N, K)
     x = qr_synth.normal_bf16(M + 2 * K, (M, K), 1.0, 13, max(1, K // 100))
     w = qr_synth.normal_bf16(N + 3 * K, (N, K), 0.02)
-    qa, sa, _, _ = qr.quant_act(dev_bf16(x), row=True)
-    qw, sw, _, _ = qr.quant_w(dev_bf16(w))
+    qa, sa, _, _ = g_quant_act(qr, dev_bf16(x), row=True)
+    qw, sw, _, _ = g_quant_w(qr, dev_bf16(w))
     for out in (qr.QR_OUT_F32, qr.QR_OUT_BF16):
-        ys = [host(qr.gemm_fprop(qa, sa, qw, sw, out_dtype=out)) for _ in range(3)]
+        ys = [host(g_gemm_fprop(qr, qa, sa, qw, sw, out_dtype=out)) for _ in range(3)]
         assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2]), (M, N, K, out)
