@@ -32,9 +32,10 @@ EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant
            "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_quant_int8_rowwise",
            "qr_gemm_int8_w8a8", "qr_quant_w_nvfp4", "qr_gemm_w4a16", "qr_gemm_fp8_bsfprop",
            "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes",
-           "qr_uaq_fold", "qr_uaq_fold_quant_w_128x128")
+           "qr_uaq_fold", "qr_uaq_fold_quant_w_128x128", "qr_gemm_fp8_bsfprop_noalloc")
 QR_MAX_WEIGHT_BATCH = 4096
 QR_NVFP4_WORKSPACE_BYTES = 4096
+QR_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class qr_weight_desc(ctypes.Structure):
@@ -86,6 +87,8 @@ def load():
         f = getattr(L, name)
         f.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
         f.restype = I32
+    L.qr_gemm_fp8_bsfprop_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+    L.qr_gemm_fp8_bsfprop_noalloc.restype = I32
     L.qr_gemm_workspace_bytes.argtypes = [I32, I64, I64, I64]
     L.qr_gemm_workspace_bytes.restype = SZ
     L.qr_uaq_fold.argtypes = [P, I64, I64, I64, P, P, P, P]
@@ -292,6 +295,20 @@ def qr_gemm_fp8_bsfprop(a, sa, b, sb, M, N, K, y, y_dtype, ws=None, ws_bytes=0, 
              M, N, K, _arg(y, "y", _out_kind(y_dtype), _need(M, N) * esz, True), int(y_dtype),
              _arg(ws, "ws", "any", int(ws_bytes), True), int(ws_bytes), _stream(stream)),
            "qr_gemm_fp8_bsfprop")
+
+
+def qr_gemm_fp8_bsfprop_noalloc(a, sa, b, sb, M, N, K, y, y_dtype, stream=None):
+    """FProp without a workspace: split partial sums go to the library's device scratch."""
+    f = load().qr_gemm_fp8_bsfprop_noalloc
+    esz = 2 if int(y_dtype) == QR_OUT_BF16 else 4
+    live = _need(M, N) > 0
+    nk = K // 128 if K > 0 else 0
+    _check(f(_arg(a, "a", "fp8", _need(M, K) if live else 0, True),
+             _arg(sa, "sa", "f32", _need(M, nk) * 4 if live else 0, True),
+             _arg(b, "b", "fp8", _need(N, K) if live else 0, True),
+             _arg(sb, "sb", "f32", _need(_cdiv(N, 128), nk) * 4 if live else 0, True),
+             M, N, K, _arg(y, "y", _out_kind(y_dtype), _need(M, N) * esz, True), int(y_dtype),
+             _stream(stream)), "qr_gemm_fp8_bsfprop_noalloc")
 
 
 def qr_gemm_fp8_bsdgrad(dy, sdy, wT, swT, M, N, K, dx, dx_dtype, ws=None, ws_bytes=0,

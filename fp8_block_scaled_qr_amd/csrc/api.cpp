@@ -9,7 +9,8 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
+static_assert(qr::kNoAllocScratchBytes == QR_NOALLOC_SCRATCH_BYTES, "scratch size in qr.h");
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -71,9 +72,12 @@ qr_status check_weight(const void *w_bf16, int64_t n, int64_t k, int64_t ld_w, c
     return QR_OK;
 }
 
+// scratch: the K-split partials go to the library's own device scratch instead of a caller
+// workspace (the allocation-free entry point): ws is then unused and the plan's workspace must
+// fit the scratch.
 qr_status check_gemm(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                      int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype, void *ws,
-                     size_t ws_bytes, int bscale, int64_t sb_rows)
+                     size_t ws_bytes, int bscale, int64_t sb_rows, bool scratch = false)
 {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
         return QR_ERR_SHAPE;
@@ -96,10 +100,15 @@ qr_status check_gemm(const uint8_t *a, const float *sa, const uint8_t *b, const 
     const int64_t nk = K / 128;
     const int64_t esz = y_dtype == QR_OUT_BF16 ? 2 : 4;
     const qr::GemmPlan plan = qr::plan_gemm(bscale, M, N, K);
-    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
+    if (scratch) {
+        if (plan.ws_bytes > qr::kNoAllocScratchBytes)
+            return QR_ERR_SCRATCH;
+        ws = nullptr;
+    } else if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) {
         return QR_ERR_WORKSPACE;
+    }
     const Range ry = span(y, M * N * esz);
-    const Range rw = span(ws, plan.ws_bytes > 0 ? (int64_t)plan.ws_bytes : 0);
+    const Range rw = span(ws, ws && plan.ws_bytes > 0 ? (int64_t)plan.ws_bytes : 0);
     const Range ins[4] = {span(a, M * K), span(sa, M * nk * 4), span(b, N * K),
                           span(sb, sb_rows * nk * 4)};
     for (const Range &r : ins)
@@ -139,6 +148,10 @@ const char *qr_status_string(qr_status status)
     case QR_ERR_WORKSPACE: return "QR_ERR_WORKSPACE: the workspace is smaller than required";
     case QR_ERR_LAUNCH: return "QR_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case QR_ERR_ARG: return "QR_ERR_ARG: an enumerated argument is out of range";
+    case QR_ERR_SCRATCH:
+        return "QR_ERR_SCRATCH: the product's K-split partial sums exceed the allocation-free "
+               "entry point's scratch (QR_NOALLOC_SCRATCH_BYTES); use qr_gemm_fp8_bsfprop with a "
+               "workspace";
     default: return "unknown qr_status";
     }
 }
@@ -444,6 +457,23 @@ qr_status qr_gemm_fp8_bswgrad(const uint8_t *dyT, const float *sdyT, const uint8
     // and per-row B scales
     return run_gemm(qr::BSCALE_ROW, dyT, sdyT, xT, sxT, N, K, M, dw, (int32_t)dw_dtype,
                     workspace, workspace_bytes, stream);
+}
+
+qr_status qr_gemm_fp8_bsfprop_noalloc(const uint8_t *a, const float *sa, const uint8_t *b,
+                                      const float *sb, int64_t M, int64_t N, int64_t K, void *y,
+                                      qr_out_dtype y_dtype, qr_stream stream)
+{
+    const int bscale = qr::BSCALE_BLOCK;
+    qr_status st = check_gemm(a, sa, b, sb, M, N, K, y, (int32_t)y_dtype, nullptr, 0, bscale,
+                              cdiv(N, 128), /*scratch=*/true);
+    if (st != QR_OK || M == 0 || N == 0)
+        return st;
+    const qr::GemmPlan plan = qr::plan_gemm(bscale, M, N, K);
+    void *ws = nullptr;
+    if (plan.ws_bytes > 0 && qr::noalloc_scratch(&ws) != hipSuccess)
+        return QR_ERR_LAUNCH;
+    return launch_status(qr::launch_gemm(bscale, y_dtype == QR_OUT_BF16, a, sa, b, sb, M, N, K, y,
+                                         ws, plan, (hipStream_t)stream));
 }
 
 size_t qr_gemm_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K)

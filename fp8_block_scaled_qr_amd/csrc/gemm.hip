@@ -28,7 +28,42 @@
 #include "qr_device.h"
 #include "qr_internal.h"
 
+#include <mutex>
+
+// Scratch of the allocation-free FProp entry point: the K-split partial sums [split][M][N]
+// (fp32) go here instead of a caller workspace.  One copy per GPU, held until the process
+// ends.  In host code this name is only a stand-in for the device object: its device address
+// comes from hipGetSymbolAddress (noalloc_scratch below) and only that address is used.
+static __device__ __align__(256) uint8_t scratch[qr::kNoAllocScratchBytes];
+
 namespace qr {
+
+namespace {
+constexpr int kMaxDevices = 64;
+}
+
+hipError_t noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // first call on this device, with it current: its own copy of the array
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 namespace {
 

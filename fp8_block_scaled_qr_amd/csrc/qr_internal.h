@@ -100,6 +100,12 @@ enum : int {
 
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K);
 
+// Size of the file-scope device scratch that the allocation-free FProp uses for its K-split
+// partial sums, and its device address on the current device (looked up on the first call
+// per device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // A [M, K] codes, sa [M, K/128]; B [N, K] codes, sb per `bscale`; C [M, N] (out_bf16 ? bf16 : f32).
 hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float *sa,
                        const uint8_t *B, const float *sb, int64_t M, int64_t N, int64_t K,

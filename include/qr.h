@@ -78,7 +78,8 @@ enum {
     QR_ERR_ALIAS = 4,       /* an output overlaps an input or another output               */
     QR_ERR_WORKSPACE = 5,   /* workspace smaller than qr_gemm_workspace_bytes() requires   */
     QR_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch                    */
-    QR_ERR_ARG = 7          /* an enumerated argument is out of range                      */
+    QR_ERR_ARG = 7,         /* an enumerated argument is out of range                      */
+    QR_ERR_SCRATCH = 8      /* the allocation-free GEMM's scratch is too small for the call  */
 };
 
 typedef enum { QR_OUT_F32 = 0, QR_OUT_BF16 = 1 } qr_out_dtype;
@@ -288,6 +289,25 @@ qr_status qr_gemm_fp8_bswgrad(const uint8_t *dyT, const float *sdyT, const uint8
                               const float *sxT, int64_t M, int64_t N, int64_t K, void *dw,
                               qr_out_dtype dw_dtype, void *workspace, size_t workspace_bytes,
                               qr_stream stream);
+
+/*
+ * FProp without any allocation: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * size rules, alignment, aliasing and results as qr_gemm_fp8_bsfprop, bit for bit, minus the
+ * workspace: where that call would need one (qr_gemm_workspace_bytes(QR_GEMM_FPROP, M, N, K)
+ * > 0), the K-split partial sums go to a device scratch array inside the library instead,
+ * QR_NOALLOC_SCRATCH_BYTES per GPU, held from the first such call on a GPU until the process
+ * ends.  A product whose partial sums do not fit returns QR_ERR_SCRATCH and launches nothing.
+ * The call allocates nothing and calls no allocating routine.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in time on one GPU
+ * (other streams, other threads) race and must be serialized by the caller; calls on one
+ * stream are ordered and safe.  The scratch keeps the last call's partial sums; every call
+ * writes all of the partial sums it reads, so nothing needs clearing.
+ */
+#define QR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qr_status qr_gemm_fp8_bsfprop_noalloc(const uint8_t *a, const float *sa, const uint8_t *b,
+                                      const float *sb, int64_t M, int64_t N, int64_t K, void *y,
+                                      qr_out_dtype y_dtype, qr_stream stream);
 
 /* Workspace bytes the GEMM entry point of `kind` needs for these sizes (0 if none).  The
  * sizes are the ones passed to that entry point.  Returns 0 for invalid arguments.

@@ -12,7 +12,7 @@ import pytest
 import fp8_block_scaled_qr_amd as qr
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, LAUNCH, ARG = range(8)
+OK, NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, LAUNCH, ARG, SCRATCH = range(9)
 
 A = 1 << 40          # fake, 16-byte aligned device addresses far apart
 B = 2 << 40
@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 16, declared
+    assert len(declared) == 17, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -44,8 +44,8 @@ def test_exports_match_header(L):
 
 
 def test_status_strings_and_version(L):
-    assert qr.abi_version() == 2
-    for st in range(8):
+    assert qr.abi_version() == 3
+    for st in range(9):
         assert qr.status_string(st)
     assert "unknown" in qr.status_string(99)
 
@@ -319,3 +319,32 @@ def test_binding_layout_checks():
     qr._check_layout(torch.zeros(0, dtype=torch.float32), "ws", "any", 0, True)   # empty, none needed
     with pytest.raises(ValueError, match="spans"):
         qr._check_layout(torch.zeros(0, dtype=torch.uint8), "ws", "any", 16, True)
+
+
+def test_gemm_noalloc_validation(L):
+    """The allocation-free FProp validates like qr_gemm_fp8_bsfprop (no workspace argument)."""
+    f = L.qr_gemm_fp8_bsfprop_noalloc
+    assert f(A, B, C, D, 8, 128, 100, E, 1, None) == SHAPE           # K % 128
+    assert f(A, B, C, D, -1, 128, 128, E, 1, None) == SHAPE
+    assert f(A, B, C, D, 8, 128, 128, E, 2, None) == ARG              # output dtype
+    assert f(None, B, C, D, 8, 128, 128, E, 1, None) == NULL
+    assert f(A, B, C, D, 8, 128, 128, None, 1, None) == NULL
+    assert f(A + 4, B, C, D, 8, 128, 128, E, 1, None) == ALIGN
+    assert f(A, B, C, D, 8, 128, 128, A + 512, 1, None) == ALIAS      # y inside a
+    assert f(A, B, C, D, 0, 128, 128, E, 1, None) == OK               # empty: nothing launched
+    assert f(None, None, None, None, 8, 0, 128, E, 1, None) == OK
+
+
+def test_noalloc_scratch_holds_every_fprop_plan(L):
+    """Every FProp plan's K-split partial sums fit the allocation-free entry point's scratch:
+    a split is planned only while its workgroups fit one wave over the chip (at most 256 tiles
+    of 256 x 256 fp32, or of 64 rows x 64 columns on the decode kernel)."""
+    cap = qr.QR_NOALLOC_SCRATCH_BYTES
+    worst = 0
+    for M in (1, 16, 33, 64, 65, 100, 128, 200, 256, 257, 384, 512, 1000, 2048, 8192):
+        for N in (8, 200, 1024, 4096, 5120, 7168, 14336, 27648, 32512, 32768, 55296):
+            for K in (128, 1024, 4096, 5120, 14336, 27648):
+                nb = L.qr_gemm_workspace_bytes(0, M, N, K)
+                worst = max(worst, nb)
+                assert nb <= cap, (M, N, K, nb)
+    assert worst > cap // 2                                           # the bound is tight
