@@ -162,24 +162,36 @@ __device__ __forceinline__ void tile_of(int pos, int tilesM, int tilesN, int &tm
     tn = idx / rows;
 }
 
+#ifndef QR_SCALE_CHUNK
+#define QR_SCALE_CHUNK 4
+#endif
+
 template <class T, int BSCALE, bool OUT_BF16>
 __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 {
-    // Scales staged per step: BM row scales of A, then the B scales (BN row scales, or the
-    // tile's per-block scales; a scale load fills 64 slots, extras duplicate the last one).
+    // Scale slots: BM row scales of A, then the B scales (BN row scales, or the tile's
+    // per-block scales; a scale load fills 64 slots, extras duplicate the last one).
     constexpr int NSB = BSCALE == BSCALE_ROW ? T::BN : (T::BN >= kGroup ? T::BN / kGroup : 1);
     constexpr int NW = T::WM * T::WN;
-    constexpr int NSA_I = T::BM / 64;                               // A-scale loads per step
-    constexpr int NSB_I = BSCALE == BSCALE_ROW ? T::BN / 64 : 1;    // B-scale loads per step
+    constexpr int NSA_I = T::BM / 64;                               // A-scale loads per chunk
+    constexpr int NSB_I = BSCALE == BSCALE_ROW ? T::BN / 64 : 1;    // B-scale loads per chunk
     constexpr int SB_SLOTS = NSB_I * 64;
-    static_assert(NSA_I + NSB_I <= NW, "one scale load per wave and step at most");
+    static_assert(NSA_I + NSB_I <= NW, "one scale load per wave and chunk at most");
     constexpr int DA = T::BM / 8 / NW, DB = T::BN / 8 / NW;         // 1 KB tile loads per wave
     static_assert(DA * 8 * NW == T::BM && DB * 8 * NW == T::BN, "whole 1 KB loads per wave");
+    // Scales are staged SC groups at a time: a slot's SC consecutive groups are one 16-byte load
+    // (one memory request per row instead of one per row and group: the scale rows of
+    // consecutive tile rows are K/128 * 4 bytes apart, so a per-group load of a tile's row
+    // scales touches a different line per row).  Chunk c covers the steps gb + c SC ..; two
+    // chunk buffers alternate.  A deeper stage ring (NS > 2) keeps one scale per step.
+    constexpr int SC = T::NS == 2 ? QR_SCALE_CHUNK : 1;
+    static_assert(SC == 1 || SC == 4, "scale chunk of 1 or 4 groups");
+    constexpr int SBUF = SC == 1 ? T::NS : 2;                       // scale buffers
 
     // Two LDS stages per operand; the global loads write them directly (no register staging).
     __shared__ __attribute__((aligned(1024))) uint8_t smA[T::NS][T::BM * kGroup];
     __shared__ __attribute__((aligned(1024))) uint8_t smB[T::NS][T::BN * kGroup];
-    __shared__ __attribute__((aligned(256))) float sS[T::NS][T::BM + SB_SLOTS];
+    __shared__ __attribute__((aligned(256))) float sS[SBUF][(T::BM + SB_SLOTS) * SC];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index: uniform across the wave, so say so (scalar offsets stay scalar)
@@ -243,7 +255,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const uint32_t ldsA = lds_addr_of(&smA[0][0]), ldsB = lds_addr_of(&smB[0][0]);
     const uint32_t ldsS = lds_addr_of(&sS[0][0]);
     const v4i_sgpr rS = sA_wave ? rSA : rSB;
-    auto issue_step = [&](int kg, int st) {
+    // kg: the group whose tiles go to stage st (clamped to the range); kt: the step it serves
+    // (unclamped), which decides the scale chunk
+    auto issue_step = [&](int kg, int kt, int st) {
         const uint32_t k0 = (uint32_t)kg * kGroup;
 #pragma unroll
         for (int j = 0; j < DA; ++j) {
@@ -255,9 +269,17 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             const int t = wave + j * NW;
             dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
         }
-        if (sA_wave || sB_wave)
-            dma4(rS, ldsS + (uint32_t)((st * (T::BM + SB_SLOTS) + sdst) * 4),
-                 soff + (uint32_t)kg * 4);
+        if (SC == 1) {
+            if (sA_wave || sB_wave)
+                dma4(rS, ldsS + (uint32_t)((st * (T::BM + SB_SLOTS) + sdst) * 4),
+                     soff + (uint32_t)kg * 4);
+        } else if ((sA_wave || sB_wave) && ((kt - gb) & (SC - 1)) == 0 && kt < ge) {
+            // the chunk of groups kt .. kt + SC - 1 (groups past the row end are loaded but
+            // never read; past the buffer they read as zeros)
+            const int c = (kt - gb) / SC;
+            dma16(rS, ldsS + (uint32_t)(((c & 1) * (T::BM + SB_SLOTS) + sdst) * SC * 4),
+                  soff + (uint32_t)kt * 4);
+        }
     };
 
     v4f acc[T::IM][T::JN];
@@ -282,8 +304,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     // fragments of the first MFMA are read first, then the other B fragments, then the
     // scales (first needed by the first promotion): every wave starts the step at the same
     // barrier, so the first MFMA should wait for as few LDS reads as possible.
-    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS) {
-        const float *tSA = tS, *tSB = tS + T::BM;
+    // tS: the scale buffer; q: the step's column in it (slot r of group q at tS[r SC + q])
+    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS, int q) {
+        const float *tSA = tS + q, *tSB = tS + T::BM * SC + q;
         v8i bf[T::JN];
         v8i afb[2];
         bf[0] = frag(tB, wn * T::TN);
@@ -296,7 +319,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         float sav[T::IM];
 #pragma unroll
         for (int i = 0; i < T::IM; ++i)
-            sav[i] = tSA[wm * T::TM + i * 16 + lr];
+            sav[i] = tSA[(wm * T::TM + i * 16 + lr) * SC];
         float sbw = 0.0f;
         float sbv[T::JN][4];
         if (BSCALE == BSCALE_ROW) {
@@ -304,11 +327,11 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             for (int j = 0; j < T::JN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sbv[j][r] = tSB[wn * T::TN + j * 16 + 4 * lq + r];
+                    sbv[j][r] = tSB[(wn * T::TN + j * 16 + 4 * lq + r) * SC];
         } else {
             // this wave's 128-column block within the tile (the tile starts on a block
             // boundary or lies inside one block)
-            sbw = tSB[T::BN >= kGroup ? (wn * T::TN) / kGroup : 0];
+            sbw = tSB[(T::BN >= kGroup ? (wn * T::TN) / kGroup : 0) * SC];
         }
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         // Software pipeline over single MFMAs (one M sub-tile x one N sub-tile): the partial
@@ -352,7 +375,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const int glast = ge - 1;
 #pragma unroll
     for (int p = 0; p < T::NS - 1; ++p)
-        issue_step(min(gb + p, glast), p);
+        issue_step(min(gb + p, glast), gb + p, p);
     // this wave's loads per step: its tile loads, plus one scale load on the scale waves
     auto wait_next = [&]() {
         constexpr int C = DA + DB;
@@ -369,8 +392,11 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     int st = 0, st_load = T::NS - 1;
 #pragma nounroll
     for (int kg = gb; kg < ge; ++kg) {
-        issue_step(min(kg + T::NS - 1, glast), st_load);
-        compute(smA[st], smB[st], sS[st]);
+        issue_step(min(kg + T::NS - 1, glast), kg + T::NS - 1, st_load);
+        if (SC == 1)
+            compute(smA[st], smB[st], sS[st], 0);
+        else
+            compute(smA[st], smB[st], sS[((kg - gb) / SC) & 1], (kg - gb) & (SC - 1));
         wait_next();   // this wave's loads of step k+1
         stage_barrier();
         st = st + 1 == T::NS ? 0 : st + 1;
