@@ -28,6 +28,7 @@
 #include "qr_device.h"
 #include "qr_internal.h"
 
+#include <algorithm>
 #include <mutex>
 
 // Scratch of the allocation-free FProp entry point: the K-split partial sums [split][M][N]
@@ -984,8 +985,9 @@ using CfgBig4 = TileCfg<256, 256, 2, 4>;   // prefill / training: 8 waves, 128x6
 using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
 using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
 using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
+using CfgW128 = TileCfg<256, 128, 4, 2>;   // decode, M <= 256 with large splits: 64x64 per wave
 
-enum { CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_SKINNY = 5 };
+enum { CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_SKINNY = 5, CFG_W128 = 6 };
 #ifndef QR_I8_SMALL_BN
 #define QR_I8_SMALL_BN 32
 #endif
@@ -1026,6 +1028,7 @@ void tile_dims(int cfg, int &bm, int &bn)
 {
     switch (cfg) {
     case CFG_BIG4: bm = CfgBig4::BM; bn = CfgBig4::BN; break;
+    case CFG_W128: bm = CfgW128::BM; bn = CfgW128::BN; break;
     case CFG_SKINNY: bm = 64; bn = 16 * kSkinnyNW; break;
     case CFG_M64: bm = CfgM64::BM; bn = CfgM64::BN; break;
     case CFG_M128: bm = CfgM128::BM; bn = CfgM128::BN; break;
@@ -1065,9 +1068,23 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     // decode batches of 65..256 rows this reads each weight panel once for all rows, where
     // 128x128 or 256x64 tiles re-read the whole activation for every 128 or 64 weight rows
     // (2.1x faster on a 32B layer's four linears at batch 256).
-    if (M >= QR_BIG_MIN_M)
+    // Decode batches of 65..256 rows whose 256x256 tiles would need a K split so large that
+    // the fp32 partial sums (split * M * N * 4 bytes) outweigh the weight (N * K bytes): 256x128
+    // tiles, twice as many, so half the split and half the partials.  On a 32B layer at batch
+    // 256: QKV 37.9 -> 33.6 us, O 34.4 -> 28.9 us; the down projection (K = 27648, partials
+    // 0.44x its weight) stays on 256x256 tiles (63.6 against 71.5 us on 256x128).
+    bool mid = false;
+    if (M >= QR_BIG_MIN_M) {
         p.cfg = CFG_BIG4;
-    else if (M <= 64 && bscale == BSCALE_BLOCK)
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256), nk0 = K / kGroup;
+        if (M <= 256 && bscale == BSCALE_BLOCK && big > 0 && big <= kCUs / 2 && nk0 > 1) {
+            const int64_t sp = std::min<int64_t>(kCUs / big, nk0);
+            if (sp * M * 4 > K) {
+                p.cfg = CFG_W128;
+                mid = true;
+            }
+        }
+    } else if (M <= 64 && bscale == BSCALE_BLOCK)
         p.cfg = CFG_SKINNY;   // decode: stream B once, no split
     else if (M <= 64)
         p.cfg = CFG_M64;
@@ -1090,7 +1107,7 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
         const int64_t kgps = (nk + split - 1) / split;
         split = (nk + kgps - 1) / kgps;
     }
-    if (p.cfg != CFG_BIG4 && p.cfg != CFG_SKINNY && tiles > 0 && tiles < 512 &&
+    if (p.cfg != CFG_BIG4 && p.cfg != CFG_SKINNY && !mid && tiles > 0 && tiles < 512 &&
         nk > 0) {
         split = (512 + tiles - 1) / tiles;
         const int64_t max_split = nk / 4 > 1 ? nk / 4 : 1;   // keep >= 4 groups per split
@@ -1106,7 +1123,7 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     // 256x256 tiles that would leave more than half of the CUs idle: split K so that the
     // tiles' splits make one wave of at most one workgroup per CU (a decode batch of 256 rows
     // against a 7168-wide weight has 28 tiles, 8 splits of 5 groups each)
-    if (p.cfg == CFG_BIG4 && tiles > 0 && tiles <= kCUs / 2 && nk > 1) {
+    if ((p.cfg == CFG_BIG4 || mid) && tiles > 0 && tiles <= kCUs / 2 && nk > 1) {
         split = kCUs / tiles;
         if (split > nk)
             split = nk;
@@ -1147,6 +1164,7 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
                       : launch_skinny<4>(out_bf16, a, stream);
         break;
     case CFG_BIG4: e = launch_t<CfgBig4>(bscale, out_bf16, a, blocks, stream); break;
+    case CFG_W128: e = launch_t<CfgW128>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M64: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_M128: e = launch_t<CfgM128>(bscale, out_bf16, a, blocks, stream); break;
     default: e = launch_t<CfgM256>(bscale, out_bf16, a, blocks, stream); break;
