@@ -14,7 +14,8 @@ input, at the 8B-layer shapes (hidden 4096, 8192 tokens; decode FFN 14336 at bat
   quant_dy_dual   1x128 rows and 128x1 columns (transposed) of dY [8192, 4096], one read
   dgrad           dX = dY W            8192 x 4096 x 4096, bf16 out
   wgrad           dW = dY^T X          4096 x 4096 x 8192, bf16 out
-  quant_x_dec     1x128 groups of the decode activation X [64, 4096]
+  norm_quant_dec  the norm in front of the decode linear with its 1x128 quantize fused in:
+                  h [64, 4096] -> codes and scales of RMSNorm(h) * gain
   fprop_decode    Y = X W^T            64 x 14336 x 4096 on the pre-quantized weight, bf16 out
 
 After the warm-up, a breakdown pass of K steps brackets every launch with HIP events on the
@@ -22,14 +23,19 @@ stream it runs on (each op's time and roofline fraction).  The timed pass of K s
 records events only around the dominant kernel's launch, so the step time carries no per-op
 event overhead.  The JSON line reports the step's GEMM throughput (all GEMM flops / step
 time) as `value`, each op's time with its roofline fraction, the roofline of the dominant
-kernel from its launches in the timed pass, and the CPU oracle timed on a bounded token slice
-of the same step.  Outside the step it also times the batched re-quantization of a 32B
-decoder layer's four weights (`weight_update`, once per optimizer step), the norm with the
-activation quantize fused in (`norm_quant`, the producer of FProp's operand), the INT8
-W8A8 variant at the same shapes (`int8_w8a8`), the 4-bit weight path at the decode shape
-(`w4a16`: quantizing the 14336x4096 weight, then the 64x14336x4096 GEMM with bf16 X) and the
-8B decoder layer's four FP8 linears at decode batch 64 (`decode_8b`) and the 32B decoder
-layer's four at decode batch 256 on the weight update's codes (`decode_32b`).
+kernel from its launches in the timed pass, and the CPU oracle timed on bounded slices of the
+same step (all cores and one core; quantizers and GEMMs separately).  Outside the step it also
+times, each after a cache-evicting read where the op is HBM-bound:
+  prefill_8b      the 1x128 quantize of X and FProp as one unit (combined TFLOP/s)
+  tiny_fprop      the tiny FProp workload's three launches (microseconds only)
+  decode_32b      the 32B decoder layer's four linears at decode batch 256 on the seeded,
+                  UAQ-folded inputs of that workload
+  ceilings        the best single-launch streaming rate over the decode GEMM's 60.84 MB
+  weight_update   the batched re-quantization of a 32B layer's four weights (once per
+                  optimizer step)
+  norm_quant      the norm with the activation quantize fused in (FProp's operand producer)
+  decode_8b       the 8B decoder layer's four FP8 linears at decode batch 64
+  int8_w8a8, w4a16  the INT8 and 4-bit weight variants at the same shapes
 """
 import argparse
 import hashlib
@@ -71,7 +77,9 @@ def op_table():
         "quant_dy_dual": ("hbm", T * H * 2 + 2 * T * H + 2 * T * (H // g) * 4),
         "dgrad": ("mfma", gemm_flops(T, H, H)),
         "wgrad": ("mfma", gemm_flops(H, H, T)),
-        "quant_x_dec": ("hbm", MD * H * 2 + MD * H + MD * (H // g) * 4),
+        # the decode hidden state's norm with the 1x128 quantize fused in: read h and the gain,
+        # write codes and scales
+        "norm_quant_dec": ("hbm", MD * H * 2 + H * 4 + MD * H + MD * (H // g) * 4),
         # decode is bound by streaming the weight: codes + block scales + A + Y
         "fprop_decode": ("hbm", F * H + (F // g) * (H // g) * 4 + MD * H + MD * (H // g) * 4
                          + MD * F * 2),
@@ -173,7 +181,8 @@ class Step:
                                                      *self.ws["dgrad"])),
             ("wgrad", lambda: qr.qr_gemm_fp8_bswgrad(self.qdYT, self.sdYT, self.qXT, self.sXT, T, H, H, self.dW, BF,
                                                      *self.ws["wgrad"])),
-            ("quant_x_dec", lambda: qr.qr_quant_act_1x128(self.Xd, MD, H, H, self.qXd, self.sXd, None, None)),
+            ("norm_quant_dec", lambda: qr.qr_rmsnorm_quant_1x128(self.Xd, MD, H, H, self.gain, 1e-6,
+                                                                 None, self.qXd, self.sXd)),
             ("fprop_decode", lambda: qr.qr_gemm_fp8_bsfprop(self.qXd, self.sXd, self.qWd, self.sWd, MD, F, H,
                                                             self.Yd, BF, *self.ws["decode"])),
         ]
@@ -231,18 +240,23 @@ def run_gpu(args):
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(end) / args.steps
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
-    normq = run_norm_quant(torch, qr, st)
-    int8 = run_int8(torch, qr, st)
-    w4 = run_w4a16(torch, qr, st)
+    extra = {}
+    extra["prefill_8b"] = run_prefill_combined(torch, qr, st)
+    extra["norm_quant"] = run_norm_quant(torch, qr, st)
+    extra["int8_w8a8"] = run_int8(torch, qr, st)
+    extra["w4a16"] = run_w4a16(torch, qr, st)
     del st, ops
     torch.cuda.empty_cache()
-    dec8 = run_decode_8b(torch, qr)
+    extra["tiny_fprop"] = run_tiny_fprop(torch, qr)
+    extra["ceilings"] = run_ceilings(torch)
     torch.cuda.empty_cache()
-    upd, codes = run_weight_update(torch, qr)
-    dec32 = run_decode_32b(torch, qr, codes)
-    del codes
+    extra["decode_8b"] = run_decode_8b(torch, qr)
     torch.cuda.empty_cache()
-    return step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec8, dec32
+    extra["weight_update"] = run_weight_update(torch, qr)
+    torch.cuda.empty_cache()
+    extra["decode_32b"] = run_decode_32b(torch, qr)
+    torch.cuda.empty_cache()
+    return step_ms, wall, per_op, dom, dom_ms, extra
 
 
 def run_norm_quant(torch, qr, st, iters=20):
@@ -413,7 +427,6 @@ def run_weight_update(torch, qr, iters=10):
         nbytes += n * k * (2 + 1 + 1) + 2 * nb * 4
     us = _median_us(torch, lambda: qr.qr_quant_w_128x128_batched(items), iters, flush=False)
     gbs = nbytes / (us * 1e-6) / 1e9
-    codes = [(q, s, n, k) for (_, n, k, _, q, s, _, _) in items]
     del ws, items
     torch.cuda.empty_cache()
     upd = {"workload": "32B decoder layer weights (QKV 7168x5120, O 5120x5120, gate+up "
@@ -421,7 +434,7 @@ def run_weight_update(torch, qr, iters=10):
                        "copies, one batched call",
            "us": round(us, 1), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": 1}
-    return upd, codes
+    return upd
 
 
 def run_decode_8b(torch, qr, iters=20):
@@ -459,18 +472,29 @@ def run_decode_8b(torch, qr, iters=20):
     return out
 
 
-def run_decode_32b(torch, qr, codes, iters=20):
-    """The 32B decoder layer's four linears at decode batch 256 on their 128x128 FP8 codes
-    (the weight update's output): 1x128 activation codes of X [256, K], then FProp with bf16
-    out.  Each GEMM is timed after a cache-evicting read, so its weight streams from HBM.
-    Algorithmic bytes = weight codes + block scales + activation codes and scales + bf16 Y."""
+def run_decode_32b(torch, qr, iters=20):
+    """The 32B decoder layer's four linears at decode batch 256 on the seeded, UAQ-folded
+    inputs of that workload (qr_synth.decode_32b_set: W ~ N(0, 0.02), s ~ U(1.5, 4) per input
+    column, X = s (.) X0 with 1% outlier channels): W' = fold(W, s) and its 128x128 codes (one
+    call, untimed: a one-time preprocessing), X's 1x128 codes (untimed: the norm in front
+    produces them), then FProp with bf16 out, timed after a cache-evicting read so the weight
+    streams from HBM.  Algorithmic bytes = weight codes + block scales + activation codes and
+    scales + bf16 Y."""
+    import qr_synth
     dev = "cuda:0"
     M, g = 256, 128
-    names = ["qkv", "o", "gate_up", "down"]
-    gen = torch.Generator(device=dev).manual_seed(6101)
     out, tot_us, tot_fl, tot_b = {}, 0.0, 0.0, 0
-    for name, (q, s, n, k) in zip(names, codes):
-        x = torch.randn((M, k), device=dev, generator=gen).to(torch.bfloat16)
+    t0 = time.time()
+    for lin in qr_synth.decode_32b_set():
+        name = lin.name.replace("decode_32b_", "")
+        n, k = lin.N, lin.K
+        w = torch.from_numpy(lin.w().view(np.int16)).to(dev).view(torch.bfloat16)
+        sc = torch.from_numpy(lin.uaq_s()).to(dev)
+        q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        s = torch.empty((n // g, k // g), dtype=torch.float32, device=dev)
+        qr.qr_uaq_fold_quant_w_128x128(w, n, k, k, sc, w, None, q, s)   # in place
+        del w
+        x = torch.from_numpy(lin.x().view(np.int16)).to(dev).view(torch.bfloat16)
         qx, sx = qr.quant_act(x)[:2]
         y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
         nb = qr.qr_gemm_workspace_bytes(0, M, n, k)
@@ -482,57 +506,207 @@ def run_decode_32b(torch, qr, codes, iters=20):
         tf, gbs = fl / (us * 1e-6) / 1e12, by / (us * 1e-6) / 1e9
         out[name] = {"shape": [M, n, k], "us": round(us, 2), "tflops": round(tf, 1),
                      "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                     "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4)}
+                     "frac_mfma": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "k_splits": nb // (M * n * 4) if nb else 1}
         tot_us, tot_fl, tot_b = tot_us + us, tot_fl + fl, tot_b + by
-        del x, qx, sx, y, ws
+        del q, s, sc, x, qx, sx, y, ws
+        torch.cuda.empty_cache()
+    log(f"decode_32b inputs drawn and timed in {time.time() - t0:.1f}s")
     out["layer"] = {"us": round(tot_us, 1), "tflops": round(tot_fl / (tot_us * 1e-6) / 1e12, 1),
                     "gbs": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
-                    "frac_hbm": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+                    "frac_hbm": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "frac_mfma": round(tot_fl / (tot_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                    "bytes": tot_b, "gflop": round(tot_fl / 1e9, 2)}
     out["workload"] = ("32B decoder layer at decode batch 256: QKV 5120->7168, O 5120->5120, "
-                       "gate+up 5120->55296, down 27648->5120; FP8 FProp, bf16 out, each "
-                       "after a cache-evicting read")
+                       "gate+up 5120->55296, down 27648->5120; seeded UAQ-folded weights "
+                       "(s ~ U(1.5, 4)) and activations s (.) X0, FProp, bf16 out, each after a "
+                       "cache-evicting read")
     return out
+
+
+def run_tiny_fprop(torch, qr, iters=50):
+    """The tiny FProp workload (X [256, 512] with 4 outlier channels, W [512, 512], fp32 out):
+    the 1x128 quantize of X, the 128x128 quantize of W and the GEMM, launched back to back; a
+    launch-latency-bound case, reported in microseconds only."""
+    import qr_synth
+    dev = "cuda:0"
+    lin = qr_synth.tiny_fprop()
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    x, w = bf(lin.x()), bf(lin.w())
+    M, N, K = lin.M, lin.N, lin.K
+    qx, sx = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((M, K // 128), device=dev)
+    qw, sw = torch.empty((N, K), dtype=torch.uint8, device=dev), torch.empty((N // 128, K // 128), device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    nb = qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, M, N, K)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    parts = {
+        "quant_x": lambda: qr.qr_quant_act_1x128(x, M, K, K, qx, sx, None, None),
+        "quant_w": lambda: qr.qr_quant_w_128x128(w, N, K, K, qw, sw, None, None),
+        "gemm": lambda: qr.qr_gemm_fp8_bsfprop(qx, sx, qw, sw, M, N, K, y, qr.QR_OUT_F32, ws, nb),
+    }
+    out = {k: round(_median_us(torch, f, iters, flush=False), 2) for k, f in parts.items()}
+
+    def whole():
+        for f in parts.values():
+            f()
+    out["total_us"] = round(_median_us(torch, whole, iters, flush=False), 2)
+    out["workload"] = "tiny FProp: X [256, 512] 1x128 + W [512, 512] 128x128 quantize, GEMM to fp32 [256, 512]"
+    return out
+
+
+def run_prefill_combined(torch, qr, st, iters=20):
+    """The prefill FProp with its activation quantize in front, as one unit: the 1x128 quantize
+    of X [8192, 4096] (rows only) and the GEMM 8192x4096x4096 (bf16 out), each after a
+    cache-evicting read, and the pair back to back after one."""
+    dev = "cuda:0"
+    q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    s = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    ws, nb = st.ws["fprop"]
+    quant = lambda: qr.qr_quant_act_1x128(st.X, T, H, H, q, s, None, None)
+    gemm = lambda: qr.qr_gemm_fp8_bsfprop(q, s, st.qW, st.sW, T, H, H, st.Y, qr.QR_OUT_BF16, ws, nb)
+
+    def both():
+        quant()
+        gemm()
+    qu, gu, bu = (_median_us(torch, f, iters) for f in (quant, gemm, both))
+    qb = T * H * 3 + T * (H // 128) * 4
+    fl = gemm_flops(T, H, H)
+    return {"workload": "1x128 quantize of X [8192, 4096] then FProp 8192x4096x4096, bf16 out",
+            "quant_us": round(qu, 2), "quant_gbs": round(qb / qu / 1e3, 1),
+            "quant_frac_hbm": round(qb / qu / 1e3 / PEAK_HBM_GBS, 4),
+            "gemm_us": round(gu, 2), "gemm_tflops": round(fl / gu / 1e6, 1),
+            "combined_us": round(bu, 2), "combined_tflops": round(fl / bu / 1e6, 1),
+            "combined_frac_mfma": round(fl / bu / 1e6 / PEAK_FP8_TFLOPS, 4)}
+
+
+def run_ceilings(torch, iters=20):
+    """What one launch streaming the decode GEMM's 60.84 MB (64 x 14336 x 4096: weight codes and
+    scales, activation, output) can reach on this GPU: a plain contiguous read of that many
+    bytes (libqr_ceiling.so; 256-thread workgroups, each reading one contiguous share, 16 bytes
+    per lane and four accesses in flight) over a sweep of grid sizes, after a cache-evicting
+    read, best grid reported; torch's copy of the same bytes for comparison.  A yardstick for
+    the decode kernel, not a roofline: the roofline stays the published 8 TB/s."""
+    import ctypes
+    import fp8_block_scaled_qr_amd as qr
+    from fp8_block_scaled_qr_amd import build as qb
+    dev = "cuda:0"
+    nbytes = F * H + (F // 128) * (H // 128) * 4 + MD * H + MD * (H // 128) * 4 + MD * F * 2
+    nbytes -= nbytes % 16
+    lib = ctypes.CDLL(qb.CEILING_LIB)
+    lib.qr_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    lib.qr_ceiling_stream_read.restype = ctypes.c_int
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sweep = {}
+    for grid in (256, 512, 1024, 2048, 4096, 8192, 16384):
+        def f(grid=grid):
+            rc = lib.qr_ceiling_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, grid,
+                                            ctypes.c_void_p(sink.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError(f"qr_ceiling_stream_read: {rc}")
+        us = _median_us(torch, f, iters)
+        sweep[grid] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1)}
+    best = min(sweep, key=lambda g: sweep[g]["us"])
+    dst = torch.empty_like(buf)
+    cu = _median_us(torch, lambda: dst.copy_(buf), iters)
+    return {"workload": f"one contiguous read of {nbytes / 1e6:.2f} MB (the 64x14336x4096 decode "
+                        f"GEMM's algorithmic bytes) after a cache-evicting read",
+            "bytes": nbytes, "read_sweep": sweep, "best_grid": best,
+            "best_us": sweep[best]["us"], "best_gbs": sweep[best]["gbs"],
+            "best_frac_hbm": round(sweep[best]["gbs"] / PEAK_HBM_GBS, 4),
+            "torch_copy": {"us": round(cu, 2), "gbs_read_plus_write": round(2 * nbytes / cu / 1e3, 1)}}
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def run_cpu_baseline(tokens):
-    """The oracle (plain C, fp64 products) on a token slice of the same step: the fold and
-    quantization of the full weight, the activation/gradient quantizers and all four GEMMs
-    restricted to `tokens` tokens (WGrad contracts over them; the decode GEMM keeps 64 rows
-    x 1/8 of the FFN outputs)."""
-    import oracle
-    import qr_synth
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    s = qr_synth.uniform_f32(3011, H, 1.5, 4.0)
-    x = qr_synth.normal_bf16(3001, (T, H), 1.0, 3003, qr_synth.n_outliers(H), col_scale=s)[:tokens]
-    w = qr_synth.normal_bf16(3002, (H, H), 0.02)
-    dy = qr_synth.backward_8b_dy()[:tokens]
-    dec = qr_synth.decode_8b()
-    xd, wd = dec.x(), dec.w()[: F // 8]
-    oracle.lib()
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_leg(oracle, x, dy, w, s, xd, wd, gemm_tokens):
+    """One timing of the oracle on the step's operations: the quantizers (fold + 128x128 blocks
+    with the transposed copy's work, X rows + columns, dY rows + columns, the decode activation)
+    over the given slices, then the four GEMMs with their contraction or token dim cut to
+    gemm_tokens (the decode one on the decode weight slice).  Returns (quant seconds, quant
+    bytes, GEMM seconds, GEMM flops)."""
+    t = x.shape[0]
     t0 = time.perf_counter()
-    wf, _ = oracle.uaq_fold(w, s, np.ones(H, np.float32))
+    wf, _ = oracle.uaq_fold(w, s, np.ones(w.shape[1], np.float32))
     qw, sw = oracle.quant_blocks(wf)
     qx, sx = oracle.quant_rows(x)
-    oracle.fprop(qx, sx, qw, sw)
+    qxT, sxT = oracle.quant_cols_T(x)
     qd, sd = oracle.quant_rows(dy)
     qdT, sdT = oracle.quant_cols_T(dy)
-    qxT, sxT = oracle.quant_cols_T(x)
-    oracle.dgrad(qd, sd, qw, sw)
-    oracle.wgrad(qdT, sdT, qxT, sxT)
     qxd, sxd = oracle.quant_rows(xd)
     qwd, swd = oracle.quant_blocks(wd)
+    tq = time.perf_counter() - t0
+    n, k = w.shape
+    qbytes = (n * k * 2 * 2 + 2 * n * k                     # fold (read + write), codes
+              + 2 * (t * k * 2 + 2 * t * k + 8 * t * k // 128)   # X and dY: read, both layouts
+              + xd.size * 3 + wd.size * 3)                   # decode activation and weight slice
+    g = gemm_tokens
+    t0 = time.perf_counter()
+    oracle.fprop(qx[:g], sx[:g], qw, sw)
+    oracle.dgrad(qd[:g], sd[:g], qw, sw)
+    oracle.wgrad(np.ascontiguousarray(qdT[:, :g]), np.ascontiguousarray(sdT[:, : g // 128]),
+                 np.ascontiguousarray(qxT[:, :g]), np.ascontiguousarray(sxT[:, : g // 128]))
     oracle.fprop(qxd, sxd, qwd, swd)
-    dt = time.perf_counter() - t0
-    flops = 3 * gemm_flops(tokens, H, H) + gemm_flops(MD, F // 8, H)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": (f"the full step's ops on a {tokens}-token slice (fold + 128x128 quantize of "
-                       f"the full 4096x4096 W, 1x128/128x1 quantizers of X and dY[:{tokens}], "
-                       f"FProp/DGrad/WGrad over {tokens} tokens, decode FProp 64 x {F // 8} x {H} "
-                       f"incl. quantizing that weight slice); value = the slice's GEMM flops / "
-                       f"oracle wall time")}
+    tg = time.perf_counter() - t0
+    flops = 3 * gemm_flops(g, n, k) + gemm_flops(xd.shape[0], wd.shape[0], k)
+    return tq, qbytes, tg, flops
+
+
+def run_cpu_baseline(tokens_all=4096, tokens_one=128):
+    """The oracle (plain C, fp64 products, OpenMP over rows) on bounded slices of the same
+    step, timed twice: with every thread the OpenMP runtime has (all host cores) and with one.
+    The all-core leg quantizes the first 2 * tokens_all tokens of X and dY and runs the GEMMs
+    over tokens_all tokens; the one-core leg uses 8 * tokens_one and tokens_one.  Both fold and
+    quantize the full 4096x4096 weight and a 1792-row slice of the decode weight."""
+    import ctypes
+    import oracle
+    import qr_synth
+    oracle.lib()
+    gomp = ctypes.CDLL("libgomp.so.1")
+    all_threads = int(gomp.omp_get_max_threads())
+    s = qr_synth.uniform_f32(3011, H, 1.5, 4.0)
+    x = qr_synth.normal_bf16(3001, (T, H), 1.0, 3003, qr_synth.n_outliers(H), col_scale=s)
+    w = qr_synth.normal_bf16(3002, (H, H), 0.02)
+    dy = qr_synth.backward_8b_dy()
+    dec = qr_synth.decode_8b()
+    xd, wd = dec.x(), dec.w()[: F // 8]
+    legs = {}
+    for name, threads, qtok, gtok in (("all_cores", all_threads, 2 * tokens_all, tokens_all),
+                                      ("one_core", 1, 8 * tokens_one, tokens_one)):
+        gomp.omp_set_num_threads(threads)
+        tq, qb, tg, fl = _oracle_leg(oracle, np.ascontiguousarray(x[:qtok]),
+                                     np.ascontiguousarray(dy[:qtok]), w, s, xd, wd, gtok)
+        legs[name] = {"threads": threads,
+                      "quantize": {"tokens": qtok, "seconds": round(tq, 3), "bytes": qb,
+                                   "GB/s": round(qb / tq / 1e9, 3)},
+                      "gemm": {"tokens": gtok, "seconds": round(tg, 3), "gflop": round(fl / 1e9, 2),
+                               "GFLOP/s": round(fl / tg / 1e9, 3)}}
+    gomp.omp_set_num_threads(all_threads)
+    a = legs["all_cores"]
+    return {"value": round(a["gemm"]["GFLOP/s"] / 1e3, 5), "unit": "TFLOP/s",
+            "cores": all_threads, "kind": "oracle", "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "sample": (f"the step's operations on bounded slices: quantizers (UAQ fold + 128x128 "
+                       f"blocks of the full 4096x4096 W, 1x128 rows and 128x1 columns of X and "
+                       f"dY, the decode activation and a {F // 8}x{H} decode-weight slice) and "
+                       f"GEMMs (FProp, DGrad, WGrad over the token slice, decode FProp "
+                       f"{MD}x{F // 8}x{H}); all cores: {2 * tokens_all} tokens quantized, "
+                       f"{tokens_all} in the GEMMs; one core: {8 * tokens_one} and {tokens_one}; "
+                       f"value = all-core GEMM flops / oracle seconds"),
+            "legs": legs}
 
 
 # ------------------------------------------------------------------ main
@@ -543,14 +717,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens in the all-core CPU oracle's GEMMs (twice that quantized)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    step_ms, wall, per_op, dom, dom_ms, upd, normq, int8, w4, dec8, dec32 = run_gpu(args)
+    step_ms, wall, per_op, dom, dom_ms, extra = run_gpu(args)
     table = op_table()
     kernels = {}
     for name, ms in per_op.items():
@@ -586,14 +761,9 @@ def main():
                    "gemm_gflop_per_step": round(gemm_total / 1e9, 2)},
         "roofline": roof,
         "kernels": kernels,
-        "weight_update": upd,
-        "decode_8b": dec8,
-        "decode_32b": dec32,
-        "norm_quant": normq,
-        "int8_w8a8": int8,
-        "w4a16": w4,
         "wall_s": round(wall, 3),
     }
+    out.update(extra)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = run_cpu_baseline(args.cpu_tokens)

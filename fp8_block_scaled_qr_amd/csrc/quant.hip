@@ -649,6 +649,82 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restric
     }
 }
 
+// The same norm and quantize for few rows (decode batches): one workgroup of SW waves per row.
+// Wave w takes the row's 512-column passes w, w + SW, ...; the waves' partial sums of squares
+// meet in LDS and every wave adds them in wave order, so the sum (and y) does not depend on
+// timing.  NP > 0: a wave keeps its NP passes in registers; NP == 0: it reads them twice.
+template <int NP, int SW>
+__global__ __launch_bounds__(64 * SW) void k_rmsnorm_quant_split(
+    const uint16_t *__restrict__ h, int64_t rows, int64_t cols, int64_t ldh,
+    const float *__restrict__ gain, float eps, uint16_t *__restrict__ y, uint8_t *__restrict__ q,
+    float *__restrict__ s)
+{
+    __shared__ float part[SW];
+    const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
+    const int w = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;   // grid = rows: every wave of the workgroup has a row
+    const int64_t ngc = (cols + kTile - 1) / kTile, npass = (ngc + 3) / 4;
+    const uint16_t *hr = h + row * ldh;
+    auto col_of = [&](int64_t p) { return (4 * p + sub) * kTile + 8 * li; };
+    auto load = [&](int64_t p) -> uint4 {
+        const int64_t c = col_of(p);   // cols % 8 == 0: an octet is all in or out
+        return p < npass && c < cols ? *reinterpret_cast<const uint4 *>(hr + c)
+                                     : make_uint4(0, 0, 0, 0);
+    };
+    float ss = 0.0f;
+    uint4 keep[NP > 0 ? NP : 1];
+    if (NP > 0) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            keep[j] = load(w + (int64_t)j * SW);
+            ss = sumsq8(keep[j], ss);
+        }
+    } else {
+        for (int64_t p = w; p < npass; p += SW)
+            ss = sumsq8(load(p), ss);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        ss += __shfl_xor(ss, o);
+    if (lane == 0)
+        part[w] = ss;
+    __syncthreads();
+    float tot = part[0];
+#pragma unroll
+    for (int k = 1; k < SW; ++k)
+        tot += part[k];
+    const float inv = 1.0f / sqrtf(tot / (float)cols + eps);
+
+    auto body = [&](int64_t p, const uint4 &v) {
+        const int64_t c = col_of(p);
+        const bool ok = p < npass && c < cols;
+        uint4 yv = make_uint4(0, 0, 0, 0);
+        if (ok) {
+            const float4 g0 = *reinterpret_cast<const float4 *>(gain + c);
+            const float4 g1 = *reinterpret_cast<const float4 *>(gain + c + 4);
+            yv = rms_apply(v, inv, g0, g1);
+            if (y)
+                *reinterpret_cast<uint4 *>(y + row * cols + c) = yv;
+        }
+        const Scale sc = make_scale(row16_max(absmax8(yv)));   // all 64 lanes take part
+        const uint2 c8 = tiny_scale(sc) ? encode8<true>(yv, sc) : encode8<false>(yv, sc);
+        if (ok)
+            *reinterpret_cast<uint2 *>(q + row * cols + c) = c8;
+        const int64_t g = 4 * p + sub;
+        if (li == 0 && p < npass && g < ngc)
+            s[row * ngc + g] = sc.s;
+    };
+    if (NP > 0) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+            if (w + (int64_t)j * SW < npass)   // uniform across the wave
+                body(w + (int64_t)j * SW, keep[j]);
+    } else {
+        for (int64_t p = w; p < npass; p += SW)
+            body(p, load(p));
+    }
+}
+
 // ---------------------------------------------------------------- INT8 W8A8 rows
 
 // 8 int8 codes of one 16-byte bf16 load: clamp(RNE(RN32(x / s)), +-127)
@@ -874,6 +950,17 @@ hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t rows, int64_t cols, i
     if (rows == 0 || cols == 0)
         return hipSuccess;
     const int64_t npass = ((cols + kTile - 1) / kTile + 3) / 4;
+    if (rows <= kSmallRows && npass >= 2) {
+        // few rows: a workgroup of 8 waves per row instead of one wave
+        const dim3 g1((unsigned)rows);
+        if (npass <= 8)
+            k_rmsnorm_quant_split<1, 8><<<g1, 512, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+        else if (npass <= 64)
+            k_rmsnorm_quant_split<8, 8><<<g1, 512, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+        else
+            k_rmsnorm_quant_split<0, 8><<<g1, 512, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (npass <= 8)
         k_rmsnorm_quant<8><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);

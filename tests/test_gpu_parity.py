@@ -130,7 +130,13 @@ def test_quant_w_batched():
 RMS_SHAPES = [(256, 512, 1e-6, "small"), (77, 200, 1e-6, "ragged rows, partial group"),
               (1, 8, 1e-5, "one row, 8 columns"), (300, 5120, 1e-6, "32B hidden: 10 passes"),
               (40, 27648, 1e-6, "down-proj width: row read twice"),
-              (8192, 4096, 1e-6, "prefill_8b hidden full size")]
+              (8192, 4096, 1e-6, "prefill_8b hidden full size"),
+              # few rows: a workgroup of 8 waves per row (one pass each, several passes kept
+              # in registers, and the re-read path), ragged columns
+              (64, 4096, 1e-6, "decode_8b hidden, 8 waves per row"),
+              (256, 5120, 1e-6, "32B decode hidden, passes in registers"),
+              (3, 1096, 1e-5, "few rows, ragged columns"),
+              (16, 70000, 1e-6, "few rows, row read twice")]
 
 
 @pytest.mark.parametrize("rows,cols,eps,name", RMS_SHAPES)
