@@ -34,6 +34,7 @@ times, each after a cache-evicting read where the op is HBM-bound:
   weight_update   the batched re-quantization of a 32B layer's four weights (once per
                   optimizer step)
   norm_quant      the norm with the activation quantize fused in (FProp's operand producer)
+  norm_quant_dual the norm emitting the 1x128 rows and the 128x1 columns from one read of h
   decode_8b       the 8B decoder layer's four FP8 linears at decode batch 64
   int8_w8a8, w4a16  the INT8 and 4-bit weight variants at the same shapes
 """
@@ -243,6 +244,7 @@ def run_gpu(args):
     extra = {}
     extra["prefill_8b"] = run_prefill_combined(torch, qr, st)
     extra["norm_quant"] = run_norm_quant(torch, qr, st)
+    extra["norm_quant_dual"] = run_norm_quant_dual(torch, qr, st)
     extra["int8_w8a8"] = run_int8(torch, qr, st)
     extra["w4a16"] = run_w4a16(torch, qr, st)
     del st, ops
@@ -273,6 +275,28 @@ def run_norm_quant(torch, qr, st, iters=20):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": "RMSNorm (gain carrying the UAQ s) + 1x128 quantize of h [8192, 4096], "
                         "codes and scales out (the FProp operand)",
+            "us": round(us, 2), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def run_norm_quant_dual(torch, qr, st, iters=20):
+    """The norm emitting both activation layouts on the prefill hidden state [8192, 4096] (the
+    step's X stands in for h; the gain carries the UAQ s): the row statistics, then the 1x128
+    rows for FProp and the 128x1 columns (transposed) for WGrad from one read of h.  Algorithmic
+    bytes: h once, the gain, both codes and scales, inv_rms."""
+    dev = "cuda:0"
+    g = st.s.clone()
+    inv = torch.empty(T, dtype=torch.float32, device=dev)
+    q, qT = torch.empty((T, H), dtype=torch.uint8, device=dev), torch.empty((H, T), dtype=torch.uint8, device=dev)
+    s = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    sT = torch.empty((H, T // 128), dtype=torch.float32, device=dev)
+    f = lambda: qr.qr_rmsnorm_quant_dual(st.X, T, H, H, g, 1e-6, inv, None, q, s, qT, sT)
+    us = _median_us(torch, f, iters)
+    nbytes = T * H * 2 + H * 4 + 2 * T * H + 2 * T * (H // 128) * 4 + T * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "RMSNorm (gain carrying the UAQ s) of h [8192, 4096] with its 1x128 rows "
+                        "and 128x1 columns (transposed) quantized from one read of h, inv_rms out "
+                        "(two launches: row statistics, then the tiles)",
             "us": round(us, 2), "bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
 

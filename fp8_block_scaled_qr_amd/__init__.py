@@ -32,7 +32,8 @@ EXPORTS = ("qr_status_string", "qr_abi_version", "qr_quant_act_1x128", "qr_quant
            "qr_quant_w_128x128_batched", "qr_rmsnorm_quant_1x128", "qr_quant_int8_rowwise",
            "qr_gemm_int8_w8a8", "qr_quant_w_nvfp4", "qr_gemm_w4a16", "qr_gemm_fp8_bsfprop",
            "qr_gemm_fp8_bsdgrad", "qr_gemm_fp8_bswgrad", "qr_gemm_workspace_bytes",
-           "qr_uaq_fold", "qr_uaq_fold_quant_w_128x128", "qr_gemm_fp8_bsfprop_noalloc")
+           "qr_uaq_fold", "qr_uaq_fold_quant_w_128x128", "qr_gemm_fp8_bsfprop_noalloc",
+           "qr_rmsnorm_quant_dual")
 QR_MAX_WEIGHT_BATCH = 4096
 QR_NVFP4_WORKSPACE_BYTES = 4096
 QR_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -75,6 +76,8 @@ def load():
     L.qr_quant_w_128x128_batched.restype = I32
     L.qr_rmsnorm_quant_1x128.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P]
     L.qr_rmsnorm_quant_1x128.restype = I32
+    L.qr_rmsnorm_quant_dual.argtypes = [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P, P, P, P]
+    L.qr_rmsnorm_quant_dual.restype = I32
     L.qr_quant_int8_rowwise.argtypes = [P, I64, I64, I64, P, P, P]
     L.qr_quant_int8_rowwise.restype = I32
     L.qr_gemm_int8_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
@@ -244,6 +247,20 @@ def qr_rmsnorm_quant_1x128(h, rows, cols, ld_h, gain, eps, y, q_row, s_row, stre
         _arg(y, "y", "bf16", n * 2, True), _arg(q_row, "q_row", "fp8", n, True),
         _arg(s_row, "s_row", "f32", _need(rows, _cdiv(cols, 128)) * 4, True), _stream(stream)),
         "qr_rmsnorm_quant_1x128")
+
+
+def qr_rmsnorm_quant_dual(h, rows, cols, ld_h, gain, eps, inv_rms, y, q_row, s_row, q_colT,
+                          s_colT, stream=None):
+    n = _need(rows, cols)
+    _check(load().qr_rmsnorm_quant_dual(
+        _arg(h, "h", "bf16", _strided(rows, cols, ld_h, 2)), rows, cols, ld_h,
+        _arg(gain, "gain", "f32", _need(cols) * 4, True), float(eps),
+        _arg(inv_rms, "inv_rms", "f32", _need(rows) * 4, True),
+        _arg(y, "y", "bf16", n * 2, True), _arg(q_row, "q_row", "fp8", n, True),
+        _arg(s_row, "s_row", "f32", _need(rows, _cdiv(cols, 128)) * 4, True),
+        _arg(q_colT, "q_colT", "fp8", n, True),
+        _arg(s_colT, "s_colT", "f32", _need(cols, _cdiv(rows, 128)) * 4, True),
+        _stream(stream)), "qr_rmsnorm_quant_dual")
 
 
 def qr_quant_int8_rowwise(x, rows, cols, ld_x, q, s, stream=None):
@@ -437,6 +454,26 @@ def rmsnorm_quant(h, gain, eps=1e-6, want_y=True, stream=None):
     s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=dev)
     qr_rmsnorm_quant_1x128(h, rows, cols, h.stride(0), gain, eps, y, q, s, stream)
     return y, q, s
+
+
+def rmsnorm_quant_dual(h, gain, eps=1e-6, row=True, col=True, want_y=False, stream=None):
+    """h: bf16 [rows, cols] on the GPU, gain fp32 [cols].  Returns (inv_rms, y or None, q_row,
+    s_row, q_colT, s_colT), with None for the pair not requested."""
+    import torch
+    rows, cols = h.shape
+    dev = h.device
+    inv = torch.empty(rows, dtype=torch.float32, device=dev)
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if want_y else None
+    q_row = s_row = q_colT = s_colT = None
+    if row:
+        q_row = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s_row = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=dev)
+    if col:
+        q_colT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        s_colT = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.float32, device=dev)
+    qr_rmsnorm_quant_dual(h, rows, cols, h.stride(0), gain, eps, inv, y, q_row, s_row, q_colT,
+                          s_colT, stream)
+    return inv, y, q_row, s_row, q_colT, s_colT
 
 
 def quant_int8(x, stream=None):

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 static_assert(qr::kNoAllocScratchBytes == QR_NOALLOC_SCRATCH_BYTES, "scratch size in qr.h");
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
@@ -228,6 +228,48 @@ qr_status qr_rmsnorm_quant_1x128(const void *h_bf16, int64_t rows, int64_t cols,
     return launch_status(qr::launch_rmsnorm_quant(
         static_cast<const uint16_t *>(h_bf16), rows, cols, ld_h, gain, eps,
         static_cast<uint16_t *>(y_bf16), q_row, s_row, (hipStream_t)stream));
+}
+
+qr_status qr_rmsnorm_quant_dual(const void *h_bf16, int64_t rows, int64_t cols, int64_t ld_h,
+                                const float *gain, float eps, float *inv_rms, void *y_bf16,
+                                uint8_t *q_row, float *s_row, uint8_t *q_colT, float *s_colT,
+                                qr_stream stream)
+{
+    if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim)
+        return QR_ERR_SHAPE;
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_colT == nullptr) != (s_colT == nullptr))
+        return QR_ERR_NULL;
+    const bool row = q_row != nullptr, col = q_colT != nullptr;
+    if (!row && !col)
+        return QR_ERR_NULL;
+    if (cols % 8 != 0 || ld_h % 8 != 0 || (rows > 0 && ld_h < cols) || (col && rows % 8 != 0) ||
+        ld_h >= kMaxLd || cdiv(rows, 128) > 65535)
+        return QR_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return QR_ERR_ARG;
+    if (rows == 0 || cols == 0)
+        return QR_OK;
+    if (!h_bf16 || !gain || !inv_rms)
+        return QR_ERR_NULL;
+    if (misaligned(h_bf16, 16) || misaligned(y_bf16, 16) || misaligned(q_row, 16) ||
+        misaligned(q_colT, 16) || misaligned(gain, 16) || misaligned(s_row, 4) ||
+        misaligned(s_colT, 4) || misaligned(inv_rms, 4))
+        return QR_ERR_ALIGN;
+    const Range ins[2] = {span(h_bf16, strided_bytes(rows, cols, ld_h, 2)), span(gain, cols * 4)};
+    const Range outs[6] = {span(inv_rms, rows * 4), span(y_bf16, y_bf16 ? rows * cols * 2 : 0),
+                           span(q_row, rows * cols), span(s_row, rows * cdiv(cols, 128) * 4),
+                           span(q_colT, rows * cols), span(s_colT, cols * cdiv(rows, 128) * 4)};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r))
+                return QR_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j]))
+                return QR_ERR_ALIAS;
+    }
+    return launch_status(qr::launch_rmsnorm_quant_dual(
+        static_cast<const uint16_t *>(h_bf16), rows, cols, ld_h, gain, eps, inv_rms,
+        static_cast<uint16_t *>(y_bf16), q_row, s_row, q_colT, s_colT, (hipStream_t)stream));
 }
 
 qr_status qr_quant_int8_rowwise(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld_x,

@@ -14,6 +14,7 @@ enum : int {
     QMODE_BLK = 4,    // 128x128 blocks, codes in input layout
     QMODE_BLKT = 8,   // 128x128 blocks, transposed copy of codes and scales
     QMODE_FOLD = 16,  // the UAQ fold applied to each tile before it is quantized
+    QMODE_NORM = 32,  // the RMSNorm applied to each tile before it is quantized
 };
 
 // One pass over x [rows, cols] (ld_x) in 128x128 tiles.
@@ -58,6 +59,14 @@ hipError_t launch_quant_w_batch(const WeightDesc *descs, int count, bool transpo
 hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld_h,
                                 const float *gain, float eps, uint16_t *y, uint8_t *q, float *s,
                                 hipStream_t stream);
+
+// The norm with both activation layouts from one read of h: inv [rows] = 1 / sqrt(mean(h^2) +
+// eps) (first pass), then y = RN_bf16((h * inv) * gain) quantized as launch_quant_tile's ROW
+// (q, s; may be null) and COL (qT, sT; may be null) modes would quantize it; y optional.
+hipError_t launch_rmsnorm_quant_dual(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld_h,
+                                     const float *gain, float eps, float *inv, uint16_t *y,
+                                     uint8_t *q, float *s, uint8_t *qT, float *sT,
+                                     hipStream_t stream);
 
 hipError_t launch_uaq_fold(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
                            const float *s, uint16_t *w_out, int64_t ld_out, float *gain,

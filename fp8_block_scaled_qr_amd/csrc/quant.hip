@@ -186,6 +186,44 @@ __device__ __forceinline__ uint4 fold8(const uint4 &v, const Fold8 &f)
                       res[4] | (res[5] << 16), res[6] | (res[7] << 16));
 }
 
+__device__ __forceinline__ float sumsq8(const uint4 &v, float ss)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = bf16_elem(v, i);
+        ss = __builtin_fmaf(x, x, ss);   // x * x is exact in binary32 (8-bit significands)
+    }
+    return ss;
+}
+
+// y = RN_bf16((h * inv) * gain) for 8 consecutive elements
+__device__ __forceinline__ uint4 rms_apply(const uint4 &v, float inv, const float4 &g0,
+                                           const float4 &g1)
+{
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16(bf16_elem(v, 2 * i) * inv * g[2 * i]) |
+               (f32_to_bf16(bf16_elem(v, 2 * i + 1) * inv * g[2 * i + 1]) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The norm in front of a linear layer with its 1x128 quantization fused in: one wave per row.
+// In pass p, lanes 16 t .. 16 t + 15 take 128-column group 4 p + t, 8 columns (16 bytes)
+// each, so a pass reads 1 KB of the row and a group's max is a 16-lane DPP reduction.  The
+// first phase sums h^2 (NP > 0: the row stays in registers, NP passes at most; NP == 0: the
+// second phase reads it again); the second forms y = RN_bf16((h * inv) * gain) with
+// inv = 1 / sqrt(sum / cols + eps) and encodes y exactly as the 1x128 quantizer does.
+// The norm ahead of an activation quantization: the tile's bf16 values h are replaced by
+// y = RN_bf16((h * inv[r]) * gain[c]) (the row statistics inv come from k_rms_inv) before the
+// maxima, and written to y if asked for.
+struct NormArgs {
+    const float *inv = nullptr;    // [rows]
+    const float *gain = nullptr;   // [cols]
+    uint16_t *y = nullptr;         // [rows, cols] dense, or nullptr
+};
+
 // The fold ahead of a 128x128 weight quantization: the tile's bf16 values are replaced by
 // RN_bf16(w / s[c]) before the block maxima, written to out, and the gain is scaled by s once.
 struct FoldArgs {
@@ -224,13 +262,15 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *x, int64_t rows,
                                             int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
                                             float *__restrict__ s, uint8_t *__restrict__ qT,
                                             float *__restrict__ sT, int64_t first, int64_t stride,
-                                            int64_t pend, const FoldArgs fa = FoldArgs{})
+                                            int64_t pend, const FoldArgs fa = FoldArgs{},
+                                            const NormArgs na = NormArgs{})
 {
     constexpr bool ROW = (MODE & QMODE_ROW) != 0;
     constexpr bool COL = (MODE & QMODE_COL) != 0;
     constexpr bool BLK = (MODE & QMODE_BLK) != 0;
     constexpr bool BLKT = (MODE & QMODE_BLKT) != 0;
     constexpr bool FOLD = (MODE & QMODE_FOLD) != 0;
+    constexpr bool NORM = (MODE & QMODE_NORM) != 0;
     constexpr bool ANYBLK = BLK || BLKT;
 
     __shared__ uint32_t red_col[4][kTile];
@@ -447,6 +487,21 @@ __device__ __forceinline__ void quant_tiles(const uint16_t *x, int64_t rows,
                     fa.gain[c + j] = fa.gain[c + j] * f.s[j];
             }
         }
+        if (NORM && c < cols) {
+            // this thread's 8 columns of the tile's rows 8 oq .. 8 oq + 7 (rows past the end
+            // stay zero)
+            const float4 g0 = *reinterpret_cast<const float4 *>(na.gain + c);
+            const float4 g1 = *reinterpret_cast<const float4 *>(na.gain + c + 4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t r = bi * kTile + 8 * oq + j;
+                if (r < rows) {
+                    v[j] = rms_apply(v[j], na.inv[r], g0, g1);
+                    if (na.y)
+                        *reinterpret_cast<uint4 *>(na.y + r * cols + c) = v[j];
+                }
+            }
+        }
         process(bi, bj, par, v);
         par ^= 1;
         pi += stride;
@@ -505,6 +560,48 @@ __global__ __launch_bounds__(256, 3) void k_fold_quant_w(const uint16_t *x,
     quant_tiles<MODE>(x, rows, cols, ldx, q, s, qT, sT, blockIdx.x, gridDim.x, nt, fa);
 }
 
+// The norm and the activation quantization in one pass over h (MODE = ROW and/or COL, plus
+// NORM): each tile is normalized in registers (and written to y if asked for), then quantized.
+template <int MODE>
+__global__ __launch_bounds__(256, 3) void k_norm_quant_tile(const uint16_t *__restrict__ h,
+                                                         int64_t rows, int64_t cols, int64_t ldh,
+                                                         uint8_t *__restrict__ q,
+                                                         float *__restrict__ s,
+                                                         uint8_t *__restrict__ qT,
+                                                         float *__restrict__ sT, NormArgs na)
+{
+    const int64_t ngc = (cols + kTile - 1) / kTile;
+    const int64_t nt = ((rows + kTile - 1) / kTile) * ngc;
+    quant_tiles<MODE>(h, rows, cols, ldh, q, s, qT, sT, blockIdx.x, gridDim.x, nt, FoldArgs{},
+                      na);
+}
+
+// A row's norm statistic inv = 1 / sqrt(mean(h^2) + eps), one wave per row, with the sum of
+// squares in k_rmsnorm_quant's order (lane sums over the 512-column passes in pass order, then
+// the same 64-lane butterfly), so the normalized values equal that kernel's.
+__global__ __launch_bounds__(256) void k_rms_inv(const uint16_t *__restrict__ h, int64_t rows,
+                                                 int64_t cols, int64_t ldh, float eps,
+                                                 float *__restrict__ inv)
+{
+    const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;   // the whole wave; no barrier follows
+    const int64_t ngc = (cols + kTile - 1) / kTile, npass = (ngc + 3) / 4;
+    const uint16_t *hr = h + row * ldh;
+    float ss = 0.0f;
+    for (int64_t p = 0; p < npass; ++p) {
+        const int64_t c = (4 * p + sub) * kTile + 8 * li;
+        const uint4 v = c < cols ? *reinterpret_cast<const uint4 *>(hr + c) : make_uint4(0, 0, 0, 0);
+        ss = sumsq8(v, ss);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        ss += __shfl_xor(ss, o);
+    if (lane == 0)
+        inv[row] = 1.0f / sqrtf(ss / (float)cols + eps);
+}
+
 // A list of weights quantized in one persistent launch (a weight update re-quantizes every
 // layer).  The tiles of all tensors form one round-robin sequence over the workgroups, so a
 // small tensor does not leave most of the grid idle.  The table travels by value in the
@@ -554,35 +651,6 @@ __global__ __launch_bounds__(256) void k_quant_rows_small(const uint16_t *__rest
 
 // ---------------------------------------------------------------- RMSNorm + 1x128 quantize
 
-__device__ __forceinline__ float sumsq8(const uint4 &v, float ss)
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float x = bf16_elem(v, i);
-        ss = __builtin_fmaf(x, x, ss);   // x * x is exact in binary32 (8-bit significands)
-    }
-    return ss;
-}
-
-// y = RN_bf16((h * inv) * gain) for 8 consecutive elements
-__device__ __forceinline__ uint4 rms_apply(const uint4 &v, float inv, const float4 &g0,
-                                           const float4 &g1)
-{
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        o[i] = f32_to_bf16(bf16_elem(v, 2 * i) * inv * g[2 * i]) |
-               (f32_to_bf16(bf16_elem(v, 2 * i + 1) * inv * g[2 * i + 1]) << 16);
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// The norm in front of a linear layer with its 1x128 quantization fused in: one wave per row.
-// In pass p, lanes 16 t .. 16 t + 15 take 128-column group 4 p + t, 8 columns (16 bytes)
-// each, so a pass reads 1 KB of the row and a group's max is a 16-lane DPP reduction.  The
-// first phase sums h^2 (NP > 0: the row stays in registers, NP passes at most; NP == 0: the
-// second phase reads it again); the second forms y = RN_bf16((h * inv) * gain) with
-// inv = 1 / sqrt(sum / cols + eps) and encodes y exactly as the 1x128 quantizer does.
 template <int NP>
 __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restrict__ h,
                                                        int64_t rows, int64_t cols, int64_t ldh,
@@ -913,6 +981,39 @@ hipError_t launch_fold_quant_w(const uint16_t *w, int64_t n, int64_t k, int64_t 
         k_fold_quant_w<BT><<<grid, 256, 0, stream>>>(w, n, k, ld_w, q, s, qT, sT, fa);
     else
         k_fold_quant_w<B><<<grid, 256, 0, stream>>>(w, n, k, ld_w, q, s, qT, sT, fa);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant_dual(const uint16_t *h, int64_t rows, int64_t cols, int64_t ld_h,
+                                     const float *gain, float eps, float *inv, uint16_t *y,
+                                     uint8_t *q, float *s, uint8_t *qT, float *sT,
+                                     hipStream_t stream)
+{
+    const int64_t nt = ((rows + kTile - 1) / kTile) * ((cols + kTile - 1) / kTile);
+    if (nt == 0)
+        return hipSuccess;
+    k_rms_inv<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(h, rows, cols, ld_h, eps, inv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    NormArgs na;
+    na.inv = inv;
+    na.gain = gain;
+    na.y = y;
+    constexpr int RC = QMODE_ROW | QMODE_COL | QMODE_NORM, R = QMODE_ROW | QMODE_NORM,
+                  C = QMODE_COL | QMODE_NORM;
+    const int mode = (q ? QMODE_ROW : 0) | (qT ? QMODE_COL : 0) | QMODE_NORM;
+    const void *fn = mode == RC ? reinterpret_cast<const void *>(&k_norm_quant_tile<RC>)
+                     : mode == R ? reinterpret_cast<const void *>(&k_norm_quant_tile<R>)
+                                 : reinterpret_cast<const void *>(&k_norm_quant_tile<C>);
+    const int64_t limit = persistent_grid(fn);
+    const dim3 grid((unsigned)(nt < limit ? nt : limit));
+    if (mode == RC)
+        k_norm_quant_tile<RC><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, q, s, qT, sT, na);
+    else if (mode == R)
+        k_norm_quant_tile<R><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, q, s, qT, sT, na);
+    else
+        k_norm_quant_tile<C><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, q, s, qT, sT, na);
     return hipGetLastError();
 }
 

@@ -208,6 +208,32 @@ qr_status qr_rmsnorm_quant_1x128(const void *h_bf16, int64_t rows, int64_t cols,
                                  float *s_row, qr_stream stream);
 
 /*
+ * The same norm emitting both activation layouts that training needs [JET, fine-grained GEMM
+ * quantization scheme: FProp takes the activation in 1x128 groups and WGrad takes it in 128x1
+ * groups, the two quantizations fused; practical advice: the activations kept for the backward
+ * pass are FP8].  One call: the row statistics
+ *   inv_rms[m] = 1 / sqrt(mean_c h[m, c]^2 + eps)
+ * (binary32, the sum of squares in qr_rmsnorm_quant_1x128's order for more than 256 rows), then
+ *   y[m, c] = RN_bf16((h[m, c] * inv_rms[m]) * gain[c])
+ * and from one read of h, y's 1x128 row codes and scales and its 128x1 column codes and scales
+ * stored transposed, exactly as qr_quant_act_1x128 would produce them from y.
+ *   h       bf16 [rows, cols], leading dimension ld_h.
+ *   gain    fp32 [cols];  eps >= 0, finite.
+ *   inv_rms fp32 [rows] out: the statistic above (also what the norm's backward pass needs).
+ *   y_bf16  NULL, or bf16 [rows, cols] (dense).
+ *   q_row / s_row, q_colT / s_colT: as for qr_quant_act_1x128; either pair may be NULL (both
+ *           members), not both.
+ * Size rules: rows, cols >= 0; cols % 8 == 0, ld_h % 8 == 0, ld_h < 2^22, ceil(rows/128) <=
+ * 65535; rows % 8 == 0 when the column pair is requested.  h, y, q_row, q_colT and gain 16-byte
+ * aligned, s_row, s_colT and inv_rms 4-byte aligned.  No output may overlap an input or another
+ * output.  A bad eps returns QR_ERR_ARG.  Two launches on `stream`.
+ */
+qr_status qr_rmsnorm_quant_dual(const void *h_bf16, int64_t rows, int64_t cols, int64_t ld_h,
+                                const float *gain, float eps, float *inv_rms, void *y_bf16,
+                                uint8_t *q_row, float *s_row, uint8_t *q_colT, float *s_colT,
+                                qr_stream stream);
+
+/*
  * Weight quantization, 128x128 blocks [JET]; run once per weight update.
  *
  * w: bf16 [n, k] (n = output features, k = input features), leading dimension ld_w.

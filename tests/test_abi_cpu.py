@@ -33,7 +33,7 @@ def L():
 
 def test_exports_match_header(L):
     declared = header_functions()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     out = subprocess.run(["nm", "-D", "--defined-only", qr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("qr_"))
@@ -44,7 +44,7 @@ def test_exports_match_header(L):
 
 
 def test_status_strings_and_version(L):
-    assert qr.abi_version() == 3
+    assert qr.abi_version() == 4
     for st in range(9):
         assert qr.status_string(st)
     assert "unknown" in qr.status_string(99)
@@ -348,3 +348,20 @@ def test_noalloc_scratch_holds_every_fprop_plan(L):
                 worst = max(worst, nb)
                 assert nb <= cap, (M, N, K, nb)
     assert worst > cap // 2                                           # the bound is tight
+
+
+def test_rmsnorm_quant_dual_validation(L):
+    f = lambda h, rows, cols, ld, g, eps, inv, y, q, s, qT, sT: L.qr_rmsnorm_quant_dual(
+        h, rows, cols, ld, g, ctypes.c_float(eps), inv, y, q, s, qT, sT, None)
+    assert f(A, 8, 128, 128, B, 1e-6, C, None, None, None, None, None) == NULL   # no output pair
+    assert f(A, 8, 128, 128, B, 1e-6, C, None, D, None, None, None) == NULL      # half a pair
+    assert f(A, 8, 128, 128, None, 1e-6, C, None, D, E, None, None) == NULL      # no gain
+    assert f(A, 8, 128, 128, B, 1e-6, None, None, D, E, None, None) == NULL      # no inv_rms
+    assert f(A, 12, 128, 128, B, 1e-6, C, None, None, None, D, E) == SHAPE       # colT: rows % 8
+    assert f(A, 8, 100, 104, B, 1e-6, C, None, D, E, None, None) == SHAPE        # cols % 8
+    assert f(A, 8, 128, 128, B, -1.0, C, None, D, E, None, None) == ARG          # eps
+    assert f(A, 8, 128, 128, B + 4, 1e-6, C, None, D, E, None, None) == ALIGN    # gain 16 B
+    assert f(A, 8, 128, 128, B, 1e-6, C + 2, None, D, E, None, None) == ALIGN    # inv 4 B
+    assert f(A, 8, 128, 128, B, 1e-6, A + 64, None, D, E, None, None) == ALIAS   # inv inside h
+    assert f(A, 8, 128, 128, B, 1e-6, C, None, D, D + 512, None, None) == ALIAS  # s inside q
+    assert f(A, 0, 128, 128, B, 1e-6, C, None, D, E, None, None) == OK           # empty

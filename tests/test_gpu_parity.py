@@ -175,6 +175,67 @@ def test_rmsnorm_quant(rows, cols, eps, name):
     assert_bitexact(host(s2), host(s), "scales without y")
 
 
+def _check_norm_y(yg, h, g, eps):
+    """The GPU's y against the oracle's RMSNorm: equal, or one bf16 ulp off where the exact
+    value lies within 2^-17 (relative) of a bf16 midpoint (binary32 evaluation)."""
+    yx, yb = oracle.rmsnorm(h, g, eps)
+    diff = yg.astype(np.int32) - yb.astype(np.int32)
+    bad = np.argwhere(diff != 0)
+    assert np.all(np.abs(diff) <= 1), "y off by more than one bf16 ulp"
+    for i, j in bad[:2000]:
+        lo, hi = sorted((int(yg[i, j]) & 0x7FFF, int(yb[i, j]) & 0x7FFF))
+        mid = (float(qr_synth.bf16_bits_to_f32(np.array([lo], np.uint16))[0]) +
+               float(qr_synth.bf16_bits_to_f32(np.array([hi], np.uint16))[0])) / 2
+        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]), (i, j, yx[i, j])
+    assert bad.shape[0] <= max(2, yg.size // 500)
+
+
+NORM_DUAL_SHAPES = [(256, 512, 1e-6, "small"), (200, 136, 1e-6, "ragged rows and columns"),
+                    (8, 8, 1e-5, "minimal"), (264, 392, 1e-6, "rows % 16 == 8, several tiles"),
+                    (64, 27648, 1e-6, "wide rows"), (8192, 4096, 1e-6, "prefill_8b hidden")]
+
+
+@pytest.mark.parametrize("rows,cols,eps,name", NORM_DUAL_SHAPES)
+def test_rmsnorm_quant_dual(rows, cols, eps, name):
+    """The norm emitting both layouts: inv_rms within the binary32 evaluation's bound of the
+    fp64 statistic; y as the single-layout norm's rule; the 1x128 rows and the transposed
+    128x1 columns bit-exact against the oracle's quantizers applied to the GPU's y; the same
+    codes without y and with one pair only; for more than 256 rows the single-layout entry
+    point's y and codes are reproduced bit for bit (same summation order)."""
+    say("rmsnorm_quant_dual", rows, cols, name)
+    rng = np.random.default_rng(rows * 5 + cols)
+    h = qr_synth.normal_bf16(rows * 11 + cols, (rows, cols), 1.0, 9, max(1, cols // 100))
+    g = (rng.uniform(0.5, 2.0, cols) * rng.uniform(1.5, 4.0, cols)).astype(np.float32)
+    if rows > 4:
+        h[1] = 0                                                  # a zero row (eps > 0)
+        h[2] = qr_synth.f32_to_bf16_bits(np.full(cols, 3.0e-39, np.float32))  # subnormals
+    hd, gd = dev_bf16(h), dev(g)
+    inv, y, q, s, qT, sT = qr.rmsnorm_quant_dual(hd, gd, eps, want_y=True)
+    hf = qr_synth.bf16_bits_to_f32(h).astype(np.float64)
+    inv64 = 1.0 / np.sqrt((hf * hf).mean(axis=1) + float(np.float32(eps)))
+    invg = host(inv).astype(np.float64)
+    assert np.all(np.abs(invg - inv64) <= 2.0 ** -18 * inv64), float(np.max(np.abs(invg / inv64 - 1)))
+    yg = host(y)
+    _check_norm_y(yg, h, g, eps)
+    rq, rs = oracle.quant_rows(np.ascontiguousarray(yg))
+    rqT, rsT = oracle.quant_cols_T(np.ascontiguousarray(yg))
+    assert_bitexact(host(q), rq, "row codes of y")
+    assert_bitexact(host(s), rs, "row scales of y")
+    assert_bitexact(host(qT), rqT, "colT codes of y")
+    assert_bitexact(host(sT), rsT, "colT scales of y")
+    _, _, q2, s2, qT2, sT2 = qr.rmsnorm_quant_dual(hd, gd, eps, want_y=False)
+    assert_bitexact(host(q2), rq, "row codes without y")
+    assert_bitexact(host(qT2), rqT, "colT codes without y")
+    _, _, q3, s3, _, _ = qr.rmsnorm_quant_dual(hd, gd, eps, col=False)
+    assert_bitexact(host(q3), rq, "row pair only")
+    _, _, _, _, qT4, sT4 = qr.rmsnorm_quant_dual(hd, gd, eps, row=False)
+    assert_bitexact(host(sT4), rsT, "column pair only")
+    if rows > 256:
+        y1, q1, s1 = qr.rmsnorm_quant(hd, gd, eps)
+        assert_bitexact(host(y1), yg, "y of the single-layout entry point")
+        assert_bitexact(host(q1), host(q), "row codes of the single-layout entry point")
+
+
 INT8_ROWS = [(256, 512), (77, 200), (1, 8), (300, 5120), (40, 27648), (8192, 4096)]
 
 
