@@ -82,7 +82,11 @@ enum {
     QR_ERR_SCRATCH = 8      /* the allocation-free GEMM's scratch is too small for the call  */
 };
 
-typedef enum { QR_OUT_F32 = 0, QR_OUT_BF16 = 1 } qr_out_dtype;
+/* Output element type of the GEMMs.  An int32_t rather than an enum type, so that a caller's
+ * out-of-range value reaches the validation (and returns QR_ERR_ARG) without being undefined
+ * behaviour in the implementation. */
+typedef int32_t qr_out_dtype;
+enum { QR_OUT_F32 = 0, QR_OUT_BF16 = 1 };
 
 typedef enum {
     QR_GEMM_FPROP = 0,   /* qr_gemm_fp8_bsfprop   */
