@@ -545,9 +545,16 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
     // A chunk c of a group: row c / 8, 16-byte chunk c % 8; thread t of the split takes
     // chunks (t + i * KTHREADS) mod ACHUNKS (duplicates write identical bytes to one place)
     auto a_chunk = [&](int i) { return (ktid + i * KTHREADS) % ACHUNKS; };
+    // LDS layout of an A group: 16-row blocks of 2 KB; chunk c (16 bytes) of row r sits in half
+    // c & 1 of its block, at slot 16 (c >> 1) + ((r & 15) ^ 2c).  A fragment read (lane l: row
+    // l % 16, chunks 2 (l / 16) + h) is then a per-lane constant offset, and both it and the
+    // chunk stores (a group of 16 lanes: two rows x 8 chunks) cover the 64 banks exactly once
+    // per 16 lanes; without the XOR the 8 chunks of a row would share one bank group.
     auto lds_off = [](int row, int c) -> int {
-        return (row >> 4) * 2048 + (c & 1) * 1024 + (((row & 15) + 16 * (c >> 1)) << 4);
+        return (row >> 4) * 2048 + (c & 1) * 1024 + ((16 * (c >> 1) + ((row & 15) ^ (2 * c))) << 4);
     };
+    const int fr_lo = lds_off(lane & 15, 2 * (lane >> 4));       // this lane's fragment slots
+    const int fr_hi = lds_off(lane & 15, 2 * (lane >> 4) + 1);
 
     // the ring
     u32x4 rbr[D][2];      // B fragment halves
@@ -622,9 +629,8 @@ __global__ __launch_bounds__(64 * NW * KS) void k_gemm_skinny(GemmArgs g)
         v4f p[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const uint8_t *q = &sA[t * 2048 + lane * 16];
-            const uint4 lo = *reinterpret_cast<const uint4 *>(q);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(q + 1024);
+            const uint4 lo = *reinterpret_cast<const uint4 *>(&sA[t * 2048 + fr_lo]);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(&sA[t * 2048 + fr_hi]);
             v8i af;
             af[0] = (int)lo.x; af[1] = (int)lo.y; af[2] = (int)lo.z; af[3] = (int)lo.w;
             af[4] = (int)hi.x; af[5] = (int)hi.y; af[6] = (int)hi.z; af[7] = (int)hi.w;
