@@ -647,9 +647,12 @@ def test_fprop_tiny_fp32_full():
                                    # 256x256 tiles with one K step, and with ragged M and N
                                    (300, 264, 128), (600, 520, 1152),
                                    # decode batches (M <= 64): ragged N, group counts that
-                                   # are not a multiple of the kernel's 8-group ring
+                                   # are not a multiple of the four-stage ring
                                    (5, 200, 1152), (17, 1000, 384), (33, 72, 640),
                                    (64, 264, 1280), (16, 8, 128),
+                                   # decode batches on weights wide enough for 128-wide tiles
+                                   # (more than 256 tiles of 64 rows), ragged N
+                                   (9, 16448, 256), (33, 16449, 384),
                                    # decode batches on narrow weights: K split across
                                    # workgroups (2 and 3 splits, the last one shorter)
                                    (40, 1000, 2304), (64, 520, 3200),
@@ -669,6 +672,15 @@ def test_fprop_shapes_full(M, N, K, out):
 def test_fprop_decode_8b_full():
     lin = qr_synth.decode_8b()
     print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, None, "decode_8b", literal=True))
+
+
+def test_fprop_decode_8b_gate_up_full():
+    """Decode batch 64 against the 8B gate+up projection (28672 rows: the 128-wide decode
+    tiles); every output."""
+    M, N, K = 64, 28672, 4096
+    x = qr_synth.normal_bf16(M + 3 * K, (M, K), 1.0, 11, max(1, K // 100))
+    w = qr_synth.normal_bf16(N + 3 * K, (N, K), 0.02)
+    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, None, f"{M}x{N}x{K}", literal=True))
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 14336), (64, 5120, 27648)])
@@ -809,7 +821,7 @@ def test_dgrad_wgrad_small_full(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(48, 384, 520), (8, 128, 1000), (48, 2304, 384)])
 def test_dgrad_decode_batch_full(M, N, K):
-    """DGrad with a small token count takes the skinny-M kernel; full comparison."""
+    """DGrad with a small token count takes the 64-row decode tiles; full comparison."""
     say("dgrad small M", M, N, K)
     dy = qr_synth.normal_bf16(M + N + 5, (M, N), 1e-3)
     w = qr_synth.normal_bf16(N * K + 5, (N, K), 0.02)
