@@ -110,6 +110,8 @@ struct GemmArgs {
 #define QR_PROMOTE_LAG 3
 #endif
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 // Workgroup barrier for the LDS stage ring, without the memory fence of __syncthreads():
 // that fence would also wait for the next steps' global loads still in flight.  Ordering is
 // explicit: each wave waits for its own LDS accesses (lgkmcnt(0)) so that the stage it wrote
@@ -170,8 +172,11 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     constexpr int SBUF = SC == 1 ? T::NS : 2;                       // scale buffers
 
     // Two LDS stages per operand; the global loads write them directly (no register staging).
-    __shared__ __attribute__((aligned(1024))) uint8_t smA[T::NS][T::BM * kGroup];
-    __shared__ __attribute__((aligned(1024))) uint8_t smB[T::NS][T::BN * kGroup];
+    // The stages, one block: A stages then B stages.  After the K loop the block holds the
+    // bf16 output tile on its way out (the epilogue below).
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::NS * (T::BM + T::BN) * kGroup];
+    auto smA = reinterpret_cast<uint8_t (*)[T::BM * kGroup]>(smem);
+    auto smB = reinterpret_cast<uint8_t (*)[T::BN * kGroup]>(smem + T::NS * T::BM * kGroup);
     __shared__ __attribute__((aligned(256))) float sS[SBUF][(T::BM + SB_SLOTS) * SC];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -389,6 +394,46 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
         vm_wait<0>();
 
     // ---- epilogue: lane holds C[m][n..n+3] for each sub-tile
+    // bf16 output of 64-column wave tiles: staged through LDS so that the stores are whole
+    // lines.  A lane's four values go to row r of the wave's region (128 bytes per row, the
+    // 16-byte chunk c at slot c ^ swz(r): conflict-free 8-byte writes), then each lane reads 16
+    // bytes back and a store instruction covers 8 rows x 128 bytes instead of 16 rows x 32.
+    // Measured on the 8192x4096x4096 GEMMs: FProp 150.4 -> 143.9 us, DGrad 145.9 -> 139.7,
+    // WGrad 159.4 -> 155.3, the 32B gate+up at batch 256 100.1 -> 95.1; non-temporal stores took
+    // another 1-2 %.  (The same staging for fp32 partial sums did not help the K-split shapes
+    // and slowed the bf16 kernels, so those keep the direct stores below.)
+    if constexpr (OUT_BF16 && T::TN == 64) {
+        static_assert(T::BM * T::BN * 2 <= T::NS * (T::BM + T::BN) * kGroup, "tile fits the stages");
+        if (g.split == 1 && (N & 7) == 0) {
+            if (T::NS > 2)
+                stage_barrier();   // every wave's last loads have landed (its vm_wait above)
+            uint8_t *ep = smem + wave * (T::TM * 128);
+#pragma unroll
+            for (int i = 0; i < T::IM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::JN; ++j) {
+                    const int r = i * 16 + lr, c = 2 * j + (lq >> 1);
+                    const v4f a = acc[i][j];
+                    uint2 o;
+                    o.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+                    o.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+                    *reinterpret_cast<uint2 *>(ep + r * 128 + ((c ^ swz(r)) << 4) + (lq & 1) * 8) = o;
+                }
+            const int c = lane & 7;
+            const int64_t n = n0 + wn * T::TN + c * 8;
+#pragma unroll
+            for (int it = 0; it < T::TM / 8; ++it) {
+                const int r = it * 8 + (lane >> 3);
+                const uint4 v = *reinterpret_cast<const uint4 *>(ep + r * 128 + ((c ^ swz(r)) << 4));
+                const int64_t m = m0 + wm * T::TM + r;
+                if (m < M && n < N)   // non-temporal: the output is not read again here
+                    __builtin_nontemporal_store(
+                        u32x4_t{v.x, v.y, v.z, v.w},
+                        reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(g.C) + m * N + n));
+            }
+            return;
+        }
+    }
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < T::IM; ++i) {
