@@ -540,8 +540,10 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
     constexpr int NW = T::WM * T::WN;
     constexpr int DA = T::BM / 8 / NW, DB = T::BN / 8 / NW;
     static_assert(DA * 8 * NW == T::BM && DB * 8 * NW == T::BN, "whole 1 KB loads per wave");
-    __shared__ __attribute__((aligned(1024))) uint8_t smA[2][T::BM * kGroup];
-    __shared__ __attribute__((aligned(1024))) uint8_t smB[2][T::BN * kGroup];
+    // NS stages of A then NS stages of B, one block (it also stages the bf16 output tile)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::NS * (T::BM + T::BN) * kGroup];
+    auto smA = reinterpret_cast<uint8_t (*)[T::BM * kGroup]>(smem);
+    auto smB = reinterpret_cast<uint8_t (*)[T::BN * kGroup]>(smem + T::NS * T::BM * kGroup);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -630,23 +632,78 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
         }
     };
 
-    // main loop: as the FP8 GEMM's (step k issues step k+1's loads into the other stage,
-    // computes, waits for its own loads, then the barrier publishes the stage)
+    // main loop: as the FP8 GEMM's (step k issues step k+NS-1's loads into the stage step k-1
+    // used, computes, waits for its own loads of step k+1, then the barrier publishes the
+    // stage; past the end of the range the loads re-read the last group into stages never read)
     const int glast = ge - 1;
-    if (gb < ge)
-        issue_step(gb, 0);
-    vm_wait<0>();
+    auto wait_next = [&]() {
+        if (T::NS == 2)
+            vm_wait<0>();
+        else
+            vm_wait<(T::NS - 2) * (DA + DB)>();
+    };
+    if (gb < ge) {
+#pragma unroll
+        for (int p = 0; p < T::NS - 1; ++p)
+            issue_step(min(gb + p, glast), p);
+    }
+    wait_next();
     stage_barrier();
+    int st = 0, st_load = T::NS - 1;
 #pragma nounroll
     for (int kg = gb; kg < ge; ++kg) {
-        const int st = (kg - gb) & 1;
-        issue_step(min(kg + 1, glast), st ^ 1);
+        issue_step(min(kg + T::NS - 1, glast), st_load);
         compute(smA[st], smB[st]);
-        vm_wait<0>();
+        wait_next();
+        stage_barrier();
+        st = st + 1 == T::NS ? 0 : st + 1;
+        st_load = st_load + 1 == T::NS ? 0 : st_load + 1;
+    }
+    if (T::NS > 2) {
+        vm_wait<0>();      // the last steps' re-reads land before the stages are reused
         stage_barrier();
     }
 
     // epilogue: lane holds C[m][n .. n + 3] of each sub-tile
+    // bf16 output of 64-column wave tiles: staged through LDS and stored as whole lines, as
+    // in the FP8 GEMM
+    if constexpr (OUT_BF16 && T::TN == 64) {
+        static_assert(T::BM * T::BN * 2 <= T::NS * (T::BM + T::BN) * kGroup, "tile fits the stages");
+        if (g.split == 1 && (N & 7) == 0) {
+            uint8_t *ep = smem + wave * (T::TM * 128);
+#pragma unroll
+            for (int i = 0; i < T::IM; ++i) {
+                const int64_t m = m0 + wm * T::TM + i * 16 + lr;
+                const float am = m < M ? g.sa[m] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < T::JN; ++j) {
+                    const int64_t n = n0 + wn * T::TN + j * 16 + 4 * lq;
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = n + r < N ? (float)acc[i][j][r] * (am * g.sb[n + r]) : 0.0f;
+                    const int rr = i * 16 + lr, c = 2 * j + (lq >> 1);
+                    uint2 o;
+                    o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+                    o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<uint2 *>(ep + rr * 128 + ((c ^ swz(rr)) << 4) + (lq & 1) * 8) = o;
+                }
+            }
+            const int c = lane & 7;
+            const int64_t n = n0 + wn * T::TN + c * 8;
+#pragma unroll
+            for (int it = 0; it < T::TM / 8; ++it) {
+                const int r = it * 8 + (lane >> 3);
+                const uint4 v = *reinterpret_cast<const uint4 *>(ep + r * 128 + ((c ^ swz(r)) << 4));
+                const int64_t m = m0 + wm * T::TM + r;
+                if (m < M && n < N)
+                    __builtin_nontemporal_store(
+                        u32x4_t{v.x, v.y, v.z, v.w},
+                        reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(g.C) + m * N + n));
+            }
+            return;
+        }
+    }
     const bool vec_ok = (N & 3) == 0;
     if (g.split > 1) {
         // this split's exact int32 partial sums; the scales are applied once, after the sum
@@ -760,9 +817,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_i8(const int32_t *__restr
 
 // Tile configurations, indexed by GemmPlan::cfg.
 using CfgBig4 = TileCfg<256, 256, 2, 4>;   // prefill / training: 8 waves, 128x64 per wave
-using CfgM64 = TileCfg<64, 128, 1, 4>;     // decode, M <= 64
-using CfgM128 = TileCfg<128, 128, 2, 2>;   // decode, M <= 128
-using CfgM256 = TileCfg<256, 64, 4, 2>;    // decode, M <= 256: 8 waves, 64x32 per wave
+using CfgM64 = TileCfg<64, 128, 1, 4>;     // M <= 64 with per-row B scales
 using CfgW128 = TileCfg<256, 128, 4, 2>;   // decode, M <= 256 with large splits: 64x64 per wave
 // Decode batches of at most 64 rows with per-block B scales: 64-row tiles whose four-stage ring
 // keeps three groups of loads in flight (the weight is streamed once; deeper rings measured
@@ -771,17 +826,12 @@ using CfgW128 = TileCfg<256, 128, 4, 2>;   // decode, M <= 256 with large splits
 using CfgDec64 = TileCfg<64, 64, 1, 4, 4>;     // 4 waves of 64x16
 using CfgDec128 = TileCfg<64, 128, 1, 8, 4>;   // 8 waves of 64x16
 
-enum { CFG_M64 = 1, CFG_M128 = 2, CFG_M256 = 3, CFG_BIG4 = 4, CFG_DEC64 = 5, CFG_W128 = 6,
-       CFG_DEC128 = 7 };
-#ifndef QR_I8_SMALL_BN
-#define QR_I8_SMALL_BN 32
-#endif
-#ifndef QR_I8_SMALL_WN
-#define QR_I8_SMALL_WN 2
-#endif
-// INT8 GEMM for decode-sized M: 64x32 tiles, 2 waves (64x16 each), so a 14336-wide weight
-// gives 448 workgroups (the HBM stream needs many of them in flight)
-using CfgI8Small = TileCfg<64, QR_I8_SMALL_BN, 1, QR_I8_SMALL_WN>;
+enum { CFG_M64 = 1, CFG_BIG4 = 4, CFG_DEC64 = 5, CFG_W128 = 6, CFG_DEC128 = 7 };
+// INT8 GEMM for decode-sized M: the FP8 decode tiles, 64x64 with 4 waves (64x16 each) and a
+// four-stage ring.  Against the earlier 64x32 two-wave, two-stage tiles (event medians after a
+// cache-evicting read): 64x14336x4096 29.7 -> 20.6 us, 64x4096x14336 46.9 -> 20.0, 16x14336x4096
+// 28.3 -> 18.2, 64x28672x4096 37.6 -> 34.6; 64x32 tiles with four stages were in between.
+using CfgI8Small = TileCfg<64, 64, 1, 4, 4>;
 
 void tile_dims(int cfg, int &bm, int &bn)
 {
@@ -790,9 +840,7 @@ void tile_dims(int cfg, int &bm, int &bn)
     case CFG_W128: bm = CfgW128::BM; bn = CfgW128::BN; break;
     case CFG_DEC64: bm = CfgDec64::BM; bn = CfgDec64::BN; break;
     case CFG_DEC128: bm = CfgDec128::BM; bn = CfgDec128::BN; break;
-    case CFG_M64: bm = CfgM64::BM; bn = CfgM64::BN; break;
-    case CFG_M128: bm = CfgM128::BM; bn = CfgM128::BN; break;
-    default: bm = CfgM256::BM; bn = CfgM256::BN; break;
+    default: bm = CfgM64::BM; bn = CfgM64::BN; break;
     }
 }
 
@@ -815,9 +863,6 @@ hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hi
 
 }  // namespace
 
-#ifndef QR_BIG_MIN_M
-#define QR_BIG_MIN_M 65
-#endif
 constexpr int64_t kCUs = 256;   // MI355X compute units: one 256x256 workgroup each
 
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
@@ -834,7 +879,7 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     // 256: QKV 37.9 -> 33.6 us, O 34.4 -> 28.9 us; the down projection (K = 27648, partials
     // 0.44x its weight) stays on 256x256 tiles (63.6 against 71.5 us on 256x128).
     bool mid = false;
-    if (M >= QR_BIG_MIN_M) {
+    if (M > 64) {
         p.cfg = CFG_BIG4;
         const int64_t big = ((M + 255) / 256) * ((N + 255) / 256), nk0 = K / kGroup;
         if (M <= 256 && bscale == BSCALE_BLOCK && big > 0 && big <= kCUs / 2 && nk0 > 1) {
@@ -846,12 +891,8 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
         }
     } else if (M <= 64 && bscale == BSCALE_BLOCK)
         p.cfg = (N + 63) / 64 > kCUs ? CFG_DEC128 : CFG_DEC64;   // decode: stream B once
-    else if (M <= 64)
-        p.cfg = CFG_M64;
-    else if (M <= 128)
-        p.cfg = CFG_M128;
     else
-        p.cfg = CFG_M256;
+        p.cfg = CFG_M64;
     int bm, bn;
     tile_dims(p.cfg, bm, bn);
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
@@ -923,9 +964,7 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     case CFG_DEC128: e = launch_t<CfgDec128>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_BIG4: e = launch_t<CfgBig4>(bscale, out_bf16, a, blocks, stream); break;
     case CFG_W128: e = launch_t<CfgW128>(bscale, out_bf16, a, blocks, stream); break;
-    case CFG_M64: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
-    case CFG_M128: e = launch_t<CfgM128>(bscale, out_bf16, a, blocks, stream); break;
-    default: e = launch_t<CfgM256>(bscale, out_bf16, a, blocks, stream); break;
+    default: e = launch_t<CfgM64>(bscale, out_bf16, a, blocks, stream); break;
     }
     if (e != hipSuccess || plan.split <= 1)
         return e;
@@ -942,12 +981,12 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     return hipGetLastError();
 }
 
-// INT8 plan: cfg 1 = 256x256 tiles, 0 = 64x32 tiles.  256x256 tiles when they give at least
+// INT8 plan: cfg 1 = 256x256 tiles, 0 = 64x64 tiles.  256x256 tiles when they give at least
 // half of the CUs a workgroup (prefill and training sizes, and wide weights at decode batches
-// up to 256: 256x55296x5120 runs in 110 us instead of 225 on 64x32 tiles).  Below that, M > 64
+// up to 256: 256x55296x5120 ran in 110 us instead of 225 on 64x32 tiles).  Below that, M > 64
 // still takes 256x256 tiles (each weight panel is read once for all rows) with K split across
 // workgroups so that the tiles' splits make one wave of at most one workgroup per CU, as the
-// FP8 plan does; M <= 64 takes 64x32 tiles, which fill the chip at any width, and splits K only
+// FP8 plan does; M <= 64 takes 64x64 tiles, and splits K only
 // when even those leave half of the CUs idle (at least 8 groups per split).
 GemmPlan plan_gemm_i8(int64_t M, int64_t N, int64_t K)
 {

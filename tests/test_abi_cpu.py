@@ -253,9 +253,9 @@ def test_gemm_workspace(L):
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_DGRAD, 200, 4096, 14336) > 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_WGRAD, 8192, 4096, 4096) == 0
     # INT8: int32 partials; 256 rows against a 5120-wide weight give 20 tiles x 12 splits, a
-    # 64-row batch against a 4096-wide one 128 narrow tiles x 2 splits
+    # 64-row batch against a 4096-wide one 64 tiles of 64x64 x 4 splits
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 256, 5120, 27648) == 12 * 256 * 5120 * 4
-    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 4096, 14336) == 2 * 64 * 4096 * 4
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 4096, 14336) == 4 * 64 * 4096 * 4
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 14336, 4096) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 8192, 4096, 4096) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, 64, 64, 131072 + 128) == 0  # invalid K

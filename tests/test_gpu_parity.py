@@ -281,11 +281,14 @@ def _int8_scaled_exact(qa, sa, qb, sb):
 
 
 # (77, 200, 384), (300, 264, 256), (520, 304, 384): 256x256 tiles with K split 3, 2, 3 ways;
-# (64, 512, 4096) and (40, 1000, 2304): 64x32 tiles split 4 and 2 ways; (130, 201, 512): an odd
-# N on a 4-way split (scalar partial stores and sums); the rest unsplit
+# (64, 512, 4096) and (40, 1000, 2304): 64x64 tiles split 4 and 2 ways; (130, 201, 512): an odd
+# N on a 4-way split (scalar partial stores and sums); (520, 264, 128) and (520, 300, 128):
+# unsplit 256x256 tiles with ragged M and N, the bf16 output staged through LDS (N % 8 == 0)
+# and stored directly (N % 8 != 0); the rest unsplit
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (64, 1000, 1024), (1, 128, 128),
                                    (300, 264, 256), (520, 304, 384), (17, 72, 640),
-                                   (64, 512, 4096), (40, 1000, 2304), (130, 201, 512)])
+                                   (64, 512, 4096), (40, 1000, 2304), (130, 201, 512),
+                                   (520, 264, 128), (520, 300, 128)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_gemm_int8(M, N, K, out):
     say("gemm_int8", M, N, K, out)
@@ -328,7 +331,7 @@ def test_gemm_int8_full_size(M, N, K):
     """The 8B prefill shape, the 8B decode shape, the 32B down (K split 12 ways) and gate+up
     projections at batch 256, a ragged-M batch on the 256x256 tiles (128 tiles, the smallest
     count that takes them without a split), the 32B QKV at batch 256 (split 8 ways) and the 8B
-    down at batch 64 (narrow tiles, split 2 ways); every output."""
+    down at batch 64 (64x64 tiles, split 4 ways); every output."""
     say("gemm_int8 full", M, N, K)
     qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
     y = out_f64(qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_BF16))
@@ -646,6 +649,9 @@ def test_fprop_tiny_fp32_full():
                                    (520, 136, 384),
                                    # 256x256 tiles with one K step, and with ragged M and N
                                    (300, 264, 128), (600, 520, 1152),
+                                   # unsplit tiles with ragged M and N % 8 == 0: the bf16 output
+                                   # staged through LDS on 256x256 and on 256x128 tiles
+                                   (2050, 4104, 128), (200, 16392, 512),
                                    # decode batches (M <= 64): ragged N, group counts that
                                    # are not a multiple of the four-stage ring
                                    (5, 200, 1152), (17, 1000, 384), (33, 72, 640),
