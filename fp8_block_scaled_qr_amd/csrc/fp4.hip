@@ -16,6 +16,8 @@
 #include "qr_device.h"
 #include "qr_internal.h"
 
+#include <type_traits>
+
 namespace qr {
 
 namespace {
@@ -68,17 +70,6 @@ __global__ __launch_bounds__(256) void k_nvfp4_amax(const uint16_t *__restrict__
         partial[blockIdx.x] = umax(umax(red[0], red[1]), umax(red[2], red[3]));
 }
 
-// E2M1 code of a binary32 quotient: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even
-// code (the midpoints 0.25, 1.25, 2.5, 5 go down, 0.75, 1.75, 3.5 up), saturating at 6; the
-// sign of v is kept.
-__device__ __forceinline__ uint32_t e2m1_code(float v)
-{
-    const float a = fabsf(v);
-    const uint32_t idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-                         (a >= 3.5f) + (a > 5.0f);
-    return idx | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // Pass 2: every workgroup reduces the partial maxima to t, then a thread encodes one block of
 // 16 elements at a time (two 16-byte loads, one 8-byte code store, one scale byte).
 __global__ __launch_bounds__(256) void k_nvfp4_quant(const uint16_t *__restrict__ w, int64_t n,
@@ -119,13 +110,42 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant(const uint16_t *__restrict_
                      __fdiv_rn(__uint_as_float(ab << 16), u), 0.0f, 0, false) & 0xFFu;
             e = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)sb, 0), t);
         }
-        uint32_t out[2] = {0u, 0u};
+        // Element codes.  The code of RN32(x / e) depends only on which interval between two
+        // consecutive midpoints (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) that quotient lies in.
+        // q = RN32(x * RN32(1 / e)) lies within 1.5 ulp of x / e, hence within 2.5 ulp of
+        // RN32(x / e).  Every midpoint has a significand of 1, 1.25, 1.5 or 1.75: its 23
+        // fraction bits are a multiple of 2^21.  So unless q's fraction bits lie within 4 of
+        // such a multiple (or q is not finite), both quotients sit strictly inside the same
+        // interval and q gives the code; the rare rest take the division itself.  The hardware
+        // conversion with scale 1 rounds to the nearest E2M1 value, ties to the even code,
+        // saturating at 6 and keeping the sign of zero (the rule above, checked on the device).
+        const float rcp = e != 0.0f ? __fdiv_rn(1.0f, e) : 0.0f;
+        const bool rcp_ok = e != 0.0f && __builtin_isfinite(rcp);
+        auto near = [](float q) {
+            const uint32_t b = __float_as_uint(q);
+            return ((b >> 23) & 0xFFu) == 0xFFu || (((b & 0x7FFFFFu) + 4u) & 0x1FFFFFu) <= 8u;
+        };
+        // elements 2p and 2p + 1 of vv into byte p of old
+        auto pair = [&](auto pc, const uint4 &vv, uint32_t old) -> uint32_t {
+            constexpr int P = decltype(pc)::value;
+            const float xa = bf16_elem(vv, 2 * P), xb = bf16_elem(vv, 2 * P + 1);
+            float qa = xa * rcp, qb = xb * rcp;
+            if (!rcp_ok || near(qa) || near(qb)) {
+                qa = e != 0.0f ? __fdiv_rn(xa, e) : xa * 0.0f;
+                qb = e != 0.0f ? __fdiv_rn(xb, e) : xb * 0.0f;
+            }
+            return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, qa, qb, 1.0f, P);
+        };
+        uint32_t out[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float x = bf16_elem(i < 8 ? v0 : v1, i & 7);
-            const uint32_t c = e != 0.0f ? e2m1_code(__fdiv_rn(x, e))
-                                         : ((__float_as_uint(x) >> 28) & 8u);
-            out[i >> 3] |= c << (4 * (i & 7));
+        for (int h = 0; h < 2; ++h) {
+            const uint4 &vv = h == 0 ? v0 : v1;
+            uint32_t o = 0u;
+            o = pair(std::integral_constant<int, 0>{}, vv, o);
+            o = pair(std::integral_constant<int, 1>{}, vv, o);
+            o = pair(std::integral_constant<int, 2>{}, vv, o);
+            o = pair(std::integral_constant<int, 3>{}, vv, o);
+            out[h] = o;
         }
         *reinterpret_cast<uint2 *>(codes + r * (k / 2) + 8 * bc) = make_uint2(out[0], out[1]);
         bscale[r * bpr + bc] = (uint8_t)sb;

@@ -363,6 +363,44 @@ def test_quant_nvfp4(n, k):
     assert_bitexact(host(t), np.array([rt], np.float32), "tensor scale")
 
 
+def test_quant_nvfp4_midpoint_quotients():
+    """Quotients x / e exactly on the E2M1 midpoints (ties to the even code), exactly on E2M1
+    values, and one bf16 step either side of them: the tensor amax 2.625 makes t = 2^-10 and
+    each block's amax 6 c t makes its scale code the E4M3 value c, so e = c t and every x = m e
+    is exact in bf16.  Exact quotients take the kernel's division path, their neighbours the
+    reciprocal path; both must match the oracle bit for bit."""
+    say("quant_nvfp4 midpoint quotients")
+    f32 = np.float32
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    vals = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    cs = [448.0, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 0.5, 0.625, 0.875, 6.0, 10.0, 13.0,
+          104.0, 0.1875, 28.0, 52.0, 240.0]
+    rows = []
+    for b, c in enumerate(cs):
+        e = c * 2.0 ** -10
+        for variant in range(4):
+            x = np.empty(16)
+            x[0] = 6.0 * e                                   # the block amax: code 6 (7)
+            base = mids if variant % 2 == 0 else vals
+            x[1:8] = base * e
+            x[8:15] = -base * e
+            x[15] = 2.5 * e
+            xb = qr_synth.f32_to_bf16_bits(x.astype(f32))
+            if variant >= 2:   # one bf16 step up or down from each (amax elements kept)
+                step = np.where(np.arange(16) % 2 == 0, 1, -1).astype(np.int32)
+                step[np.abs(x) == 6.0 * e] = 0   # the block amax stays the largest magnitude
+                mag = (xb & 0x7FFF).astype(np.int32) + step * (1 if variant == 2 else -1)
+                xb = ((xb & 0x8000) | np.clip(mag, 0, 0x7F7F)).astype(np.uint16)
+            rows.append(xb)
+    w = np.concatenate(rows).reshape(-1, 256)
+    codes, bs, t = qr.quant_nvfp4(dev_bf16(w))
+    rc, rb, rt = oracle.quant_nvfp4(w)
+    assert rt == 2.0 ** -10
+    assert_bitexact(host(bs), rb, "block scales")
+    assert_bitexact(host(codes), rc, "codes")
+    assert_bitexact(host(t), np.array([rt], np.float32), "tensor scale")
+
+
 def test_quant_nvfp4_strided_and_zero():
     say("quant_nvfp4 strided, zero")
     big = qr_synth.normal_bf16(13, (96, 640), 0.02)
