@@ -178,8 +178,9 @@ __device__ __forceinline__ v8bf dequant8(uint32_t codes8, float sc)
 //   [32 q, 32 q + 32) of its row (16 bytes) into registers.
 //   W block scales: the step's 8 scale bytes of each of the 64 rows go to a per-wave LDS ring
 //   by two direct-to-LDS dword loads (lane = row); each lane reads back its 2 bytes per block.
-//   X: the lane's K range of its row of X (4 x 16 bytes per block of 16 rows) goes to the same
-//   ring by direct-to-LDS loads, and each fragment read back serves the 4 W blocks.
+//   X: the step's 16 MB rows x 256 bytes go to the same ring by direct-to-LDS loads of whole
+//   lines (4 rows x 256 bytes per instruction), row-major with the 16-byte chunk c of row r at
+//   slot c ^ (r % 16); each fragment read back (conflict-free) serves the 4 W blocks.
 //   All three run D steps ahead, refilled together at the end of each step: loads retire in
 //   order, so a stream kept shallower than another would cap the other's depth at its own.
 //   The ring's wait is explicit (vm_wait); the compiler's own, for the code registers, counts
@@ -220,7 +221,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const uint16_t *__restric
     const uint32_t soff = (uint32_t)(lane * kb);   // + 8 s + 4 h
     // X through a buffer descriptor over rows m0 .. M - 1: rows past M read zeros
     const v4i_sgpr rx = make_rsrc_sgpr(X + m0 * K, (uint32_t)((M - m0) * K * 2));
-    const uint32_t xoff = (uint32_t)((ln * K + 32 * lq) * 2);   // + (16 mb K + 128 s + 8 t) 2
+    // this lane's chunk of a 4-row x 256-byte X load: row 4 p + lane / 16 of the block, chunk
+    // (lane % 16) ^ row (the LDS slot it lands in is lane % 16)
+    const int xr = lane >> 4, xs_slot = lane & 15;
+    auto x_off = [&](int mb, int p, int64_t s) -> uint32_t {
+        const int r = 16 * mb + 4 * p + xr;
+        const int c = xs_slot ^ (r & 15);
+        return (uint32_t)(((int64_t)r * K + 128 * s + 8 * c) * 2);
+    };
     const uint32_t ring = lds_addr_of(&xring[wave][0][0]);
 
     auto step_of = [&](int64_t i) { return wave + 4 * (i < mine ? i : mine - 1); };
@@ -237,9 +245,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const uint16_t *__restric
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                dma16(rx, ring + (uint32_t)(slot * SLOT + (mb * 4 + t) * 1024),
-                      xoff + (uint32_t)((16 * mb * K + 128 * s + 8 * t) * 2));
+            for (int p = 0; p < 4; ++p)
+                dma16(rx, ring + (uint32_t)(slot * SLOT + (mb * 4 + p) * 1024), x_off(mb, p, s));
     };
 
     v4f acc[4][MB];
@@ -283,8 +290,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const uint16_t *__restric
                         }
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb) {
+                            // row 16 mb + l % 16, K offsets 32 q + 8 t .. + 7 = chunk 4 q + t
                             const v8bf xf = *reinterpret_cast<const v8bf *>(
-                                xs + (mb * 4 + t) * 1024 + 16 * lane);
+                                xs + (16 * mb + ln) * 256 + (((4 * lq + t) ^ ln) << 4));
 #pragma unroll
                             for (int nb = 0; nb < 4; ++nb)
                                 acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
