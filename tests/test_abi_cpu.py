@@ -243,6 +243,17 @@ def test_gemm_workspace(L):
     assert nb > 0 and nb % (200 * 14336 * 4) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 14336, 4096) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 4096, 4096) == 4 * 64 * 4096 * 4
+    # decode batches: 64-wide tiles split K only while they give at most 128 workgroups (8192
+    # columns: 128 tiles x 2 splits; one more tile column: no split); 128-wide tiles (more than
+    # 256 tiles of 64) never split
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 8192, 4096) == 2 * 64 * 8192 * 4
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 8256, 4096) == 0
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 64, 28672, 4096) == 0
+    # 65..256 rows: 256x128 tiles where 256x256 ones would split K so far that the partials
+    # outweigh the weight (QKV of the 32B layer: 56 tiles x 4 splits), 256x256 tiles otherwise
+    # (its down projection: 20 tiles x 12 splits)
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 256, 7168, 5120) == 4 * 256 * 7168 * 4
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 256, 5120, 27648) == 12 * 256 * 5120 * 4
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 8192, 4096, 4096) == 0
     assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, 200, 14336, 100) == 0    # invalid K
     assert qr.qr_gemm_workspace_bytes(9, 200, 14336, 4096) == 0
