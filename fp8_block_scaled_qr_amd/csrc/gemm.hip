@@ -981,7 +981,7 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     return hipGetLastError();
 }
 
-// INT8 plan: cfg 1 = 256x256 tiles, 0 = 64x64 tiles.  256x256 tiles when they give at least
+// INT8 plan: cfg 1 = 256x256 tiles, 2 = 256x128 tiles, 0 = 64x64 tiles.  256x256 tiles when they give at least
 // half of the CUs a workgroup (prefill and training sizes, and wide weights at decode batches
 // up to 256: 256x55296x5120 ran in 110 us instead of 225 on 64x32 tiles).  Below that, M > 64
 // still takes 256x256 tiles (each weight panel is read once for all rows) with K split across
@@ -996,8 +996,20 @@ GemmPlan plan_gemm_i8(int64_t M, int64_t N, int64_t K)
     const int64_t small_tiles = ((M + CfgI8Small::BM - 1) / CfgI8Small::BM) *
                                 ((N + CfgI8Small::BN - 1) / CfgI8Small::BN);
     p.cfg = big_tiles >= kCUs / 2 || M > 64 ? 1 : 0;
+    // As in the FP8 plan: decode batches of 65..256 rows whose 256x256 tiles would split K so
+    // far that the int32 partials outweigh the weight take 256x128 tiles (cfg 2), twice the
+    // tiles and half the split (the 32B QKV and O at batch 256).
+    if (p.cfg == 1 && M <= 256 && big_tiles > 0 && big_tiles <= kCUs / 2 && nk > 1 &&
+        std::min<int64_t>(kCUs / big_tiles, nk) * M * 4 > K)
+        p.cfg = 2;
+    const int64_t mid_tiles = ((M + CfgW128::BM - 1) / CfgW128::BM) *
+                              ((N + CfgW128::BN - 1) / CfgW128::BN);
     int64_t split = 1;
-    if (p.cfg == 1 && big_tiles > 0 && big_tiles < kCUs / 2 && nk > 1) {
+    if (p.cfg == 2 && nk > 1) {
+        split = kCUs / mid_tiles;
+        if (split > nk)
+            split = nk;
+    } else if (p.cfg == 1 && big_tiles > 0 && big_tiles < kCUs / 2 && nk > 1) {
         split = kCUs / big_tiles;
         if (split > nk)
             split = nk;
@@ -1031,8 +1043,9 @@ hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const
     a.nk = (int)(K / kGroup);
     a.split = plan.split;
     a.kgps = (a.nk + plan.split - 1) / plan.split;
-    const bool big = plan.cfg == 1;
-    const int bm = big ? CfgBig4::BM : CfgI8Small::BM, bn = big ? CfgBig4::BN : CfgI8Small::BN;
+    const bool big = plan.cfg == 1, mid = plan.cfg == 2;
+    const int bm = big ? CfgBig4::BM : mid ? CfgW128::BM : CfgI8Small::BM;
+    const int bn = big ? CfgBig4::BN : mid ? CfgW128::BN : CfgI8Small::BN;
     a.tilesM = (int)((M + bm - 1) / bm);
     a.tilesN = (int)((N + bn - 1) / bn);
     const unsigned blocks = (unsigned)(a.tilesM * a.tilesN * plan.split);
@@ -1041,6 +1054,11 @@ hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const
             k_gemm_i8<CfgBig4, true><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
         else
             k_gemm_i8<CfgBig4, false><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
+    } else if (mid) {
+        if (out_bf16)
+            k_gemm_i8<CfgW128, true><<<blocks, CfgW128::THREADS, 0, stream>>>(a);
+        else
+            k_gemm_i8<CfgW128, false><<<blocks, CfgW128::THREADS, 0, stream>>>(a);
     } else {
         if (out_bf16)
             k_gemm_i8<CfgI8Small, true><<<blocks, CfgI8Small::THREADS, 0, stream>>>(a);

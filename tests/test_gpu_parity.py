@@ -280,7 +280,8 @@ def _int8_scaled_exact(qa, sa, qb, sb):
     return S.astype(np.float32) * scale
 
 
-# (77, 200, 384), (300, 264, 256), (520, 304, 384): 256x256 tiles with K split 3, 2, 3 ways;
+# (77, 200, 384): 256x128 tiles with K split 3 ways; (300, 264, 256), (520, 304, 384): 256x256
+# tiles with K split 2 and 3 ways;
 # (64, 512, 4096) and (40, 1000, 2304): 64x64 tiles split 4 and 2 ways; (130, 201, 512): an odd
 # N on a 4-way split (scalar partial stores and sums); (520, 264, 128) and (520, 300, 128):
 # unsplit 256x256 tiles with ragged M and N, the bf16 output staged through LDS (N % 8 == 0)
@@ -330,7 +331,7 @@ def test_gemm_int8_empty_zero_k_and_workspace_reuse():
 def test_gemm_int8_full_size(M, N, K):
     """The 8B prefill shape, the 8B decode shape, the 32B down (K split 12 ways) and gate+up
     projections at batch 256, a ragged-M batch on the 256x256 tiles (128 tiles, the smallest
-    count that takes them without a split), the 32B QKV at batch 256 (split 8 ways) and the 8B
+    count that takes them without a split), the 32B QKV at batch 256 (256x128 tiles, split 4 ways) and the 8B
     down at batch 64 (64x64 tiles, split 4 ways); every output."""
     say("gemm_int8 full", M, N, K)
     qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
