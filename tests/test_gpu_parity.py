@@ -706,7 +706,11 @@ def test_fprop_tiny_fp32_full():
                                    # and without one, the split reduction over an odd M * N)
                                    (77, 77, 384), (2048, 4097, 128), (300, 201, 256),
                                    (5, 13, 1152), (40, 14337, 256), (64, 1001, 2304),
-                                   (1, 3, 128)])
+                                   (1, 3, 128),
+                                   # the planner's row boundaries: 65 rows (256x128 tiles, one
+                                   # K group per split) and 257 rows (256x256 tiles over two row
+                                   # bands, the last of 4 splits shorter)
+                                   (65, 1000, 2304), (257, 7168, 1280)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_fprop_shapes_full(M, N, K, out):
     x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 7, max(1, K // 100))
