@@ -865,6 +865,9 @@ hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hi
 
 constexpr int64_t kCUs = 256;   // MI355X compute units: one 256x256 workgroup each
 
+// Fewest K groups per split on the 256-row tiles.
+constexpr int64_t kMinSplitGroups = 3;
+
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
 {
     GemmPlan p;
@@ -924,11 +927,14 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     }
     // 256x256 tiles that would leave more than half of the CUs idle: split K so that the
     // tiles' splits make one wave of at most one workgroup per CU (a decode batch of 256 rows
-    // against a 7168-wide weight has 28 tiles, 8 splits of 5 groups each)
+    // against a 7168-wide weight has 28 tiles, 8 splits of 5 groups each), keeping at least
+    // kMinSplitGroups groups per split.  With one or two groups a split's ring fill, partial
+    // sums and their sum cost more than the parallelism gains (256x4096x1024: 26.9 us on 8
+    // splits, 20.0 on 2; 200x2048x896: 18.5 on 7, 16.1 on 2).
     if ((p.cfg == CFG_BIG4 || mid) && tiles > 0 && tiles <= kCUs / 2 && nk > 1) {
-        split = kCUs / tiles;
-        if (split > nk)
-            split = nk;
+        split = std::min<int64_t>(kCUs / tiles, nk / kMinSplitGroups);
+        if (split < 1)
+            split = 1;
         const int64_t kgps = (nk + split - 1) / split;
         split = (nk + kgps - 1) / kgps;
     }
@@ -1005,14 +1011,11 @@ GemmPlan plan_gemm_i8(int64_t M, int64_t N, int64_t K)
     const int64_t mid_tiles = ((M + CfgW128::BM - 1) / CfgW128::BM) *
                               ((N + CfgW128::BN - 1) / CfgW128::BN);
     int64_t split = 1;
+    // (at least kMinSplitGroups groups per split, as in the FP8 plan)
     if (p.cfg == 2 && nk > 1) {
-        split = kCUs / mid_tiles;
-        if (split > nk)
-            split = nk;
+        split = std::max<int64_t>(1, std::min<int64_t>(kCUs / mid_tiles, nk / kMinSplitGroups));
     } else if (p.cfg == 1 && big_tiles > 0 && big_tiles < kCUs / 2 && nk > 1) {
-        split = kCUs / big_tiles;
-        if (split > nk)
-            split = nk;
+        split = std::max<int64_t>(1, std::min<int64_t>(kCUs / big_tiles, nk / kMinSplitGroups));
     } else if (p.cfg == 0 && small_tiles > 0 && small_tiles <= kCUs / 2 && nk >= 16) {
         split = kCUs / small_tiles;
         if (split > nk / 8)

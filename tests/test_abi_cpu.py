@@ -214,18 +214,18 @@ def gemm(L, name, a, sa, b, sb, M, N, K, y, dt, ws, wsb):
 def test_gemm_validation(L, name):
     # the contraction size is K for FProp, N for DGrad, M for WGrad
     contraction = {"qr_gemm_fp8_bsfprop": 2, "qr_gemm_fp8_bsdgrad": 1, "qr_gemm_fp8_bswgrad": 0}[name]
-    dims = [512, 512, 512]
+    dims = [2048, 2048, 2048]
     bad = list(dims)
     bad[contraction] = 200
     assert gemm(L, name, A, B, C, D, *bad, E, 1, None, 0) == SHAPE
-    assert gemm(L, name, A, B, C, D, -1, 512, 512, E, 1, None, 0) == SHAPE
+    assert gemm(L, name, A, B, C, D, -1, 2048, 2048, E, 1, None, 0) == SHAPE
     assert gemm(L, name, A, B, C, D, *dims, E, 7, None, 0) == ARG
     assert gemm(L, name, None, B, C, D, *dims, E, 1, None, 0) == NULL
     assert gemm(L, name, A, B, C, D, *dims, None, 1, None, 0) == NULL
     assert gemm(L, name, A + 4, B, C, D, *dims, E, 1, None, 0) == ALIGN
     assert gemm(L, name, A, B + 2, C, D, *dims, E, 1, None, 0) == ALIGN
-    # 512^3 splits K over its four 256x256 tiles, so a (large enough) workspace is passed
-    ws, wsb = 6 << 40, qr.qr_gemm_workspace_bytes(0, 512, 512, 512)
+    # 2048^3 splits K 4 ways over its 64 256x256 tiles, so a (large enough) workspace is passed
+    ws, wsb = 6 << 40, qr.qr_gemm_workspace_bytes(0, 2048, 2048, 2048)
     assert wsb > 0
     assert gemm(L, name, A, B, C, D, *dims, E, 1, None, 0) == WORKSPACE
     assert gemm(L, name, A, B, C, D, *dims, A + 64, 1, ws, wsb) == ALIAS    # output over A

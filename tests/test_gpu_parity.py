@@ -312,7 +312,7 @@ def test_gemm_int8_empty_zero_k_and_workspace_reuse():
                          4, 8, 0, y, qr.QR_OUT_F32)
     assert float(y.abs().max()) == 0.0
     qr.qr_gemm_int8_w8a8(None, None, None, None, 0, 8, 128, y, qr.QR_OUT_F32)   # M = 0
-    shapes = [(300, 264, 1024), (100, 136, 512)]
+    shapes = [(300, 264, 1024), (100, 136, 1152)]
     nb = max(qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, *sh) for sh in shapes)
     assert all(qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, *sh) > 0 for sh in shapes)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
@@ -707,9 +707,9 @@ def test_fprop_tiny_fp32_full():
                                    (77, 77, 384), (2048, 4097, 128), (300, 201, 256),
                                    (5, 13, 1152), (40, 14337, 256), (64, 1001, 2304),
                                    (1, 3, 128),
-                                   # the planner's row boundaries: 65 rows (256x128 tiles, one
-                                   # K group per split) and 257 rows (256x256 tiles over two row
-                                   # bands, the last of 4 splits shorter)
+                                   # the planner's row boundaries: 65 rows (256x128 tiles, 6
+                                   # splits of 3 K groups) and 257 rows (256x256 tiles over two
+                                   # row bands, the last of 3 splits shorter)
                                    (65, 1000, 2304), (257, 7168, 1280)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_fprop_shapes_full(M, N, K, out):

@@ -47,9 +47,9 @@ def _both(M, N, K, seed, out):
     return nb, y, y_ref
 
 
-# (large, then smaller): 32B QKV at batch 256 (8 K splits, 59 MB of partials) then the 8B
-# down projection at batch 64 (4 splits, 4 MB); a 3-split decode then an unsplit one; a
-# ragged 256x256-tile split (odd M * N) then a smaller ragged one
+# (large, then smaller): 32B QKV at batch 256 (4 K splits on 256x128 tiles, 29 MB of partials)
+# then the 8B O projection at batch 64 (4 splits, 4 MB); a 2-split decode then an unsplit one;
+# a ragged split on one 256x128 tile (odd M * N, 2 splits) then a smaller unsplit ragged one
 PAIRS = [((256, 7168, 5120), (64, 4096, 4096)),
          ((64, 1000, 2304), (16, 200, 384)),
          ((201, 77, 1024), (77, 77, 384))]
