@@ -425,7 +425,11 @@ def _check_w4a16(y, Y, S):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 1000, 1024), (17, 72, 640), (1, 128, 128),
-                                   (100, 264, 256), (200, 520, 384)])
+                                   (100, 264, 256), (200, 520, 384),
+                                   # decode batches: ragged N with K steps that do not divide
+                                   # among the four waves, long K, N % 4 != 0
+                                   (33, 1000, 4608), (5, 72, 8192), (64, 264, 2176),
+                                   (7, 13, 4608), (7, 13, 2304)])
 def test_gemm_w4a16(M, N, K):
     say("gemm_w4a16", M, N, K)
     x = qr_synth.normal_bf16(M + N + K, (M, K), 1.0, 3, max(1, K // 100))
