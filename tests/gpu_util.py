@@ -3,6 +3,9 @@ check of the GEMMs against the oracle (test code only)."""
 import numpy as np
 import torch
 
+import oracle
+import qr_synth
+
 GEMM_TOL = 2e-3    # |gpu - oracle| <= GEMM_TOL * sum_k |a_k b_k| per output element
 
 
@@ -62,6 +65,28 @@ def assert_gemm_close(gpu: np.ndarray, Y: np.ndarray, S: np.ndarray, what: str,
     assert bad.size == 0, (f"{what}: {bad.size} of {gpu.size} outside tolerance; worst err/S "
                            f"{rel.max():.3e} at {np.unravel_index(np.argmax(rel), rel.shape)}")
     return float(rel.max()) if rel.size else 0.0, float(ys.max()) if ys.size else 0.0
+
+
+def check_norm_y(yg, h, g, eps):
+    """The GPU's y against the oracle's RMSNorm: equal, or one bf16 ulp off where the exact
+    value lies within 2^-17 (relative) of a bf16 midpoint (binary32 evaluation)."""
+    yx, yb = oracle.rmsnorm(h, g, eps)
+    diff = yg.astype(np.int32) - yb.astype(np.int32)
+    bad = np.argwhere(diff != 0)
+    assert np.all(np.abs(diff) <= 1), "y off by more than one bf16 ulp"
+    for i, j in bad[:2000]:
+        lo, hi = sorted((int(yg[i, j]) & 0x7FFF, int(yb[i, j]) & 0x7FFF))
+        mid = (float(qr_synth.bf16_bits_to_f32(np.array([lo], np.uint16))[0]) +
+               float(qr_synth.bf16_bits_to_f32(np.array([hi], np.uint16))[0])) / 2
+        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]), (i, j, yx[i, j])
+    assert bad.shape[0] <= max(2, yg.size // 500)
+
+
+def check_w4a16(y, Y, S):
+    """fp32 accumulation of K exact products: |y - Y| <= K 2^-23 sum |x w| t, plus the output
+    rounding (bf16: 2^-8 |Y|)."""
+    err = np.abs(y - Y)
+    assert np.all(err <= S + 2.0 ** -8 * np.abs(Y) + 1e-30), float(np.max(err / (S + 1e-30)))
 
 
 def sample_positions(M, N, count, seed, tile=128):

@@ -13,9 +13,9 @@ import torch
 import fp8_block_scaled_qr_amd as qr
 import oracle
 import qr_synth
-from gpu_util import (assert_bitexact, assert_gemm_close, dev, dev_bf16, g_gemm_dgrad,
-                      g_gemm_fprop, g_gemm_wgrad, g_quant_act, g_quant_w, host, out_f64,
-                      sample_positions)
+from gpu_util import (assert_bitexact, assert_gemm_close, check_norm_y, check_w4a16, dev,
+                      dev_bf16, g_gemm_dgrad, g_gemm_fprop, g_gemm_wgrad, g_quant_act, g_quant_w,
+                      host, out_f64, sample_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -157,37 +157,13 @@ def test_rmsnorm_quant(rows, cols, eps, name):
     hd, gd = dev_bf16(h), dev(g)
     y, q, s = qr.rmsnorm_quant(hd, gd, eps)
     yg = host(y)
-    yx, yb = oracle.rmsnorm(h, g, eps)
-    diff = yg.astype(np.int32) - yb.astype(np.int32)
-    bad = np.argwhere(diff != 0)
-    assert np.all(np.abs(diff) <= 1), "y off by more than one bf16 ulp"
-    for i, j in bad[:2000]:
-        lo, hi = sorted((int(yg[i, j]) & 0x7FFF, int(yb[i, j]) & 0x7FFF))
-        mid = (float(qr_synth.bf16_bits_to_f32(np.array([lo], np.uint16))[0]) +
-               float(qr_synth.bf16_bits_to_f32(np.array([hi], np.uint16))[0])) / 2
-        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]), (i, j, yx[i, j])
-    assert bad.shape[0] <= max(2, yg.size // 500)
+    check_norm_y(yg, h, g, eps)
     rq, rs = oracle.quant_rows(np.ascontiguousarray(yg))
     assert_bitexact(host(q), rq, "codes of y")
     assert_bitexact(host(s), rs, "scales of y")
     _, q2, s2 = qr.rmsnorm_quant(hd, gd, eps, want_y=False)
     assert_bitexact(host(q2), host(q), "codes without y")
     assert_bitexact(host(s2), host(s), "scales without y")
-
-
-def _check_norm_y(yg, h, g, eps):
-    """The GPU's y against the oracle's RMSNorm: equal, or one bf16 ulp off where the exact
-    value lies within 2^-17 (relative) of a bf16 midpoint (binary32 evaluation)."""
-    yx, yb = oracle.rmsnorm(h, g, eps)
-    diff = yg.astype(np.int32) - yb.astype(np.int32)
-    bad = np.argwhere(diff != 0)
-    assert np.all(np.abs(diff) <= 1), "y off by more than one bf16 ulp"
-    for i, j in bad[:2000]:
-        lo, hi = sorted((int(yg[i, j]) & 0x7FFF, int(yb[i, j]) & 0x7FFF))
-        mid = (float(qr_synth.bf16_bits_to_f32(np.array([lo], np.uint16))[0]) +
-               float(qr_synth.bf16_bits_to_f32(np.array([hi], np.uint16))[0])) / 2
-        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]), (i, j, yx[i, j])
-    assert bad.shape[0] <= max(2, yg.size // 500)
 
 
 NORM_DUAL_SHAPES = [(256, 512, 1e-6, "small"), (200, 136, 1e-6, "ragged rows and columns"),
@@ -216,7 +192,7 @@ def test_rmsnorm_quant_dual(rows, cols, eps, name):
     invg = host(inv).astype(np.float64)
     assert np.all(np.abs(invg - inv64) <= 2.0 ** -18 * inv64), float(np.max(np.abs(invg / inv64 - 1)))
     yg = host(y)
-    _check_norm_y(yg, h, g, eps)
+    check_norm_y(yg, h, g, eps)
     rq, rs = oracle.quant_rows(np.ascontiguousarray(yg))
     rqT, rsT = oracle.quant_cols_T(np.ascontiguousarray(yg))
     assert_bitexact(host(q), rq, "row codes of y")
@@ -417,13 +393,6 @@ def test_quant_nvfp4_strided_and_zero():
     assert host(t)[0] == 0.0 and not host(bs).any()
 
 
-def _check_w4a16(y, Y, S):
-    """fp32 accumulation of K exact products: |y - Y| <= K 2^-23 sum |x w| t, plus the output
-    rounding (bf16: 2^-8 |Y|)."""
-    err = np.abs(y - Y)
-    assert np.all(err <= S + 2.0 ** -8 * np.abs(Y) + 1e-30), float(np.max(err / (S + 1e-30)))
-
-
 @pytest.mark.parametrize("M,N,K", [(64, 1000, 1024), (17, 72, 640), (1, 128, 128),
                                    (100, 264, 256), (200, 520, 384),
                                    # decode batches: ragged N with K steps that do not divide
@@ -439,7 +408,7 @@ def test_gemm_w4a16(M, N, K):
     y = out_f64(qr.gemm_w4a16(dev_bf16(x), codes, bs, t, out_dtype=qr.QR_OUT_F32))
     Y = oracle.gemm_w4a16(x, hc, hb, ht)
     absw = oracle.gemm_w4a16(x & np.uint16(0x7FFF), hc & np.uint8(0x77), hb, ht)  # sum |x w| t
-    _check_w4a16(y, Y, K * 2.0 ** -23 * np.abs(absw))
+    check_w4a16(y, Y, K * 2.0 ** -23 * np.abs(absw))
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 14336, 4096), (256, 5120, 27648)])
@@ -453,7 +422,7 @@ def test_gemm_w4a16_full_size_sampled(M, N, K):
     mi, ni = sample_positions(M, N, 2048, seed=M + N)
     Y = oracle.gemm_w4a16(x, hc, hb, ht, sample=(mi, ni))
     absw = oracle.gemm_w4a16(x & np.uint16(0x7FFF), hc & np.uint8(0x77), hb, ht, sample=(mi, ni))
-    _check_w4a16(y[mi, ni], Y, K * 2.0 ** -23 * np.abs(absw))
+    check_w4a16(y[mi, ni], Y, K * 2.0 ** -23 * np.abs(absw))
 
 
 def test_quant_strided_input():
