@@ -102,6 +102,8 @@ struct GemmArgs {
     int nk;             // K / 128
     int tilesM, tilesN;
     int split, kgps;    // number of K splits, groups per split
+    int krot;           // K-start rotation: > 0 multiplier of the workgroup id, < 0 (negated)
+                        // multiplier of the XCD index, 0 none
 };
 
 // The promotion of a unit's partial sum runs QR_PROMOTE_LAG MFMAs after the MFMA that made it,
@@ -148,6 +150,19 @@ __device__ __forceinline__ void tile_of(int pos, int tilesM, int tilesN, int &tm
 #ifndef QR_SCALE_CHUNK
 #define QR_SCALE_CHUNK 4
 #endif
+
+// K-start rotation for weight-streaming launches: a workgroup starts its K walk at a step set
+// by its id times this multiplier.  Used where the tiles form one row band and K is not split
+// (decode batches): every workgroup then streams its own weight rows, and without the rotation
+// all of them read the same 128-byte column of rows 4 KB or more apart at the same time,
+// which the memory system serves more slowly than spread offsets (64x14336x4096: 21.6 ->
+// 20.3 us, 64x28672x4096: 33.4 -> 29.3, 256x55296x5120: 91.2 -> 88.5; event medians after a
+// cache-evicting read).  Tiles over several row bands share A and B panels through L2 at
+// the same K step, so all tiles of one XCD keep one order (rotated per workgroup,
+// 8192x4096x4096 ran 128 -> 154 us); the XCDs, each with its own L2, start at different steps
+// (XCD x at x scale chunks before the end: 1-2 % faster on the 8192x4096x4096 GEMMs).
+constexpr int kKRotMul = 5;
+constexpr int kKRotXcd = 1;
 
 template <class T, int BSCALE, bool OUT_BF16>
 __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
@@ -241,9 +256,32 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     const uint32_t ldsA = lds_addr_of(&smA[0][0]), ldsB = lds_addr_of(&smB[0][0]);
     const uint32_t ldsS = lds_addr_of(&sS[0][0]);
     const v4i_sgpr rS = sA_wave ? rSA : rSB;
-    // kg: the group whose tiles go to stage st (clamped to the range); kt: the step it serves
-    // (unclamped), which decides the scale chunk
-    auto issue_step = [&](int kg, int kt, int st) {
+    // The K range is walked from a rotated start: step v of the range [gb, ge) takes group
+    // gb + (v + rot) mod len.  Workgroups (or XCDs) that started together then read different
+    // K offsets of their rows instead of the same 128-byte column of every row at once.  Ids
+    // are dealt round-robin to the 8 XCDs, so blockIdx.x % 8 is the XCD.
+    const int len = __builtin_amdgcn_readfirstlane(ge - gb);   // uniform
+    int rot = 0;
+    if (g.krot != 0 && len > 1) {
+        const uint32_t h = g.krot > 0 ? (uint32_t)blockIdx.x * (uint32_t)g.krot
+                                      : (blockIdx.x & 7u) * (uint32_t)(-g.krot);
+        if (SC == 1) {
+            rot = (int)(h % (uint32_t)len);
+        } else {
+            // the wrap must fall on a scale-chunk boundary: len - rot is a multiple of SC
+            const int j = (int)(h % (uint32_t)(len / SC + 1));
+            rot = (len - SC * j) % len;
+        }
+        rot = __builtin_amdgcn_readfirstlane(rot);   // uniform: keep the step walk scalar
+    }
+    auto grp = [&](int v) {
+        const int x = v + rot;
+        return gb + (x >= len ? x - len : x);
+    };
+    // v: the step whose tiles go to stage st (steps past the range re-load the last step's
+    // group into a stage that is never read); the step also decides the scale chunk
+    auto issue_step = [&](int v, int st) {
+        const int kg = grp(min(v, len - 1));
         const uint32_t k0 = (uint32_t)kg * kGroup;
 #pragma unroll
         for (int j = 0; j < DA; ++j) {
@@ -259,12 +297,13 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             if (sA_wave || sB_wave)
                 dma4(rS, ldsS + (uint32_t)((st * (T::BM + SB_SLOTS) + sdst) * 4),
                      soff + (uint32_t)kg * 4);
-        } else if ((sA_wave || sB_wave) && ((kt - gb) & (SC - 1)) == 0 && kt < ge) {
-            // the chunk of groups kt .. kt + SC - 1 (groups past the row end are loaded but
-            // never read; past the buffer they read as zeros)
-            const int c = (kt - gb) / SC;
+        } else if ((sA_wave || sB_wave) && (v & (SC - 1)) == 0 && v < len) {
+            // the chunk of groups kg .. kg + SC - 1, consecutive because the rotation wraps on
+            // a chunk boundary (groups past the range are loaded but never read; past the
+            // buffer they read as zeros)
+            const int c = v / SC;
             dma16(rS, ldsS + (uint32_t)(((c & 1) * (T::BM + SB_SLOTS) + sdst) * SC * 4),
-                  soff + (uint32_t)kt * 4);
+                  soff + (uint32_t)kg * 4);
         }
     };
 
@@ -358,10 +397,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     // lets the NS-2 later steps' loads stay in flight), so after it the next stage is
     // complete.  Past the end of the K range the loads re-read the last group (clamped) into
     // stages that are never read.
-    const int glast = ge - 1;
 #pragma unroll
     for (int p = 0; p < T::NS - 1; ++p)
-        issue_step(min(gb + p, glast), gb + p, p);
+        issue_step(p, p);
     // this wave's loads per step: its tile loads, plus one scale load on the scale waves
     auto wait_next = [&]() {
         constexpr int C = DA + DB;
@@ -377,12 +415,12 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     stage_barrier();
     int st = 0, st_load = T::NS - 1;
 #pragma nounroll
-    for (int kg = gb; kg < ge; ++kg) {
-        issue_step(min(kg + T::NS - 1, glast), kg + T::NS - 1, st_load);
+    for (int v = 0; v < len; ++v) {
+        issue_step(v + T::NS - 1, st_load);
         if (SC == 1)
             compute(smA[st], smB[st], sS[st], 0);
         else
-            compute(smA[st], smB[st], sS[((kg - gb) / SC) & 1], (kg - gb) & (SC - 1));
+            compute(smA[st], smB[st], sS[(v / SC) & 1], v & (SC - 1));
         wait_next();   // this wave's loads of step k+1
         stage_barrier();
         st = st + 1 == T::NS ? 0 : st + 1;
@@ -523,6 +561,7 @@ struct GemmI8Args {
     int nk;              // K / 128
     int tilesM, tilesN;
     int split, kgps;     // K splits across workgroups, groups per split
+    int krot;            // K-start rotation multiplier per workgroup id (0: none)
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -635,24 +674,34 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
     // main loop: as the FP8 GEMM's (step k issues step k+NS-1's loads into the stage step k-1
     // used, computes, waits for its own loads of step k+1, then the barrier publishes the
     // stage; past the end of the range the loads re-read the last group into stages never read)
-    const int glast = ge - 1;
+    // The K walk starts at a rotated step as in the FP8 GEMM (the integer sums are exact, so
+    // the order does not change the result): step v takes group gb + (v + rot) mod len.
+    const int len = __builtin_amdgcn_readfirstlane(ge - gb);   // uniform
+    const uint32_t h = g.krot > 0 ? (uint32_t)blockIdx.x * (uint32_t)g.krot
+                                  : (blockIdx.x & 7u) * (uint32_t)(-g.krot);
+    const int rot = g.krot != 0 && len > 1
+                        ? __builtin_amdgcn_readfirstlane((int)(h % (uint32_t)len)) : 0;
+    auto grp = [&](int v) {
+        const int x = min(v, len - 1) + rot;
+        return gb + (x >= len ? x - len : x);
+    };
     auto wait_next = [&]() {
         if (T::NS == 2)
             vm_wait<0>();
         else
             vm_wait<(T::NS - 2) * (DA + DB)>();
     };
-    if (gb < ge) {
+    if (len > 0) {
 #pragma unroll
         for (int p = 0; p < T::NS - 1; ++p)
-            issue_step(min(gb + p, glast), p);
+            issue_step(grp(p), p);
     }
     wait_next();
     stage_barrier();
     int st = 0, st_load = T::NS - 1;
 #pragma nounroll
-    for (int kg = gb; kg < ge; ++kg) {
-        issue_step(min(kg + T::NS - 1, glast), st_load);
+    for (int v = 0; v < len; ++v) {
+        issue_step(grp(v + T::NS - 1), st_load);
         compute(smA[st], smB[st]);
         wait_next();
         stage_barrier();
@@ -962,6 +1011,7 @@ hipError_t launch_gemm(int bscale, bool out_bf16, const uint8_t *A, const float 
     a.tilesN = (int)((N + bn - 1) / bn);
     a.split = plan.split;
     a.kgps = (a.nk + plan.split - 1) / plan.split;
+    a.krot = plan.split > 1 ? 0 : a.tilesM == 1 ? kKRotMul : -kKRotXcd;
     a.C = plan.split > 1 ? ws : C;
     const int blocks = a.tilesM * a.tilesN * plan.split;
     hipError_t e;
@@ -1051,6 +1101,7 @@ hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const
     const int bn = big ? CfgBig4::BN : mid ? CfgW128::BN : CfgI8Small::BN;
     a.tilesM = (int)((M + bm - 1) / bm);
     a.tilesN = (int)((N + bn - 1) / bn);
+    a.krot = plan.split > 1 ? 0 : a.tilesM == 1 ? kKRotMul : -kKRotXcd;
     const unsigned blocks = (unsigned)(a.tilesM * a.tilesN * plan.split);
     if (big) {
         if (out_bf16)
