@@ -164,7 +164,7 @@ __device__ __forceinline__ void tile_of(int pos, int tilesM, int tilesN, int &tm
 constexpr int kKRotMul = 5;
 constexpr int kKRotXcd = 1;
 
-template <class T, int BSCALE, bool OUT_BF16>
+template <class T, int BSCALE, bool OUT_BF16, bool EB = false>
 __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
 {
     // Scale slots: BM row scales of A, then the B scales (BN row scales, or the tile's
@@ -185,6 +185,14 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     constexpr int SC = T::NS == 2 ? QR_SCALE_CHUNK : 1;
     static_assert(SC == 1 || SC == 4, "scale chunk of 1 or 4 groups");
     constexpr int SBUF = SC == 1 ? T::NS : 2;                       // scale buffers
+    // EB (two-stage rings, weight-streaming launches): the B tile of step v + 2 is issued
+    // halfway through step v instead of at the start of step v + 1.  A wave reads all of a
+    // step's B fragments at its start, so after a barrier that follows them the B half of the
+    // stage is free; the B loads then have about a step and a half of lead instead of one, for
+    // one more barrier per step.
+    constexpr bool EARLY_B = EB && T::NS == 2;
+    constexpr int EB_AT = T::IM * T::JN / 2 - 1;   // the MFMA after which the barrier sits
+    static_assert(!EARLY_B || EB_AT >= 0, "early B needs MFMAs in the step");
 
     // Two LDS stages per operand; the global loads write them directly (no register staging).
     // The stages, one block: A stages then B stages.  After the K loop the block holds the
@@ -280,7 +288,16 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     };
     // v: the step whose tiles go to stage st (steps past the range re-load the last step's
     // group into a stage that is never read); the step also decides the scale chunk
-    auto issue_step = [&](int v, int st) {
+    auto issue_b = [&](int v, int st) {
+        const uint32_t k0 = (uint32_t)grp(min(v, len - 1)) * kGroup;
+#pragma unroll
+        for (int j = 0; j < DB; ++j) {
+            const int t = wave + j * NW;
+            dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
+        }
+    };
+    // the A tile and the scales of step v (with EARLY_B the B tile goes separately)
+    auto issue_a = [&](int v, int st) {
         const int kg = grp(min(v, len - 1));
         const uint32_t k0 = (uint32_t)kg * kGroup;
 #pragma unroll
@@ -288,11 +305,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
             const int t = wave + j * NW;
             dma16(rA, ldsA + (uint32_t)(st * T::BM * kGroup + t * 1024), tile_voff(t) + k0);
         }
-#pragma unroll
-        for (int j = 0; j < DB; ++j) {
-            const int t = wave + j * NW;
-            dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
-        }
+        if (!EARLY_B)
+            issue_b(v, st);
         if (SC == 1) {
             if (sA_wave || sB_wave)
                 dma4(rS, ldsS + (uint32_t)((st * (T::BM + SB_SLOTS) + sdst) * 4),
@@ -330,7 +344,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     // scales (first needed by the first promotion): every wave starts the step at the same
     // barrier, so the first MFMA should wait for as few LDS reads as possible.
     // tS: the scale buffer; q: the step's column in it (slot r of group q at tS[r SC + q])
-    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS, int q) {
+    auto compute = [&](const uint8_t *tA, const uint8_t *tB, const float *tS, int q, auto &&mid) {
         const float *tSA = tS + q, *tSB = tS + T::BM * SC + q;
         v8i bf[T::JN];
         v8i afb[2];
@@ -383,6 +397,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
                                                                            0, 0, 0, 127, 0, 127);
             if (u >= QR_PROMOTE_LAG)
                 promote(u - QR_PROMOTE_LAG);
+            if (EARLY_B && u == EB_AT)
+                mid();
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -396,14 +412,22 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     // the barrier each wave waits for its own loads of step k+1 (loads retire in order, so it
     // lets the NS-2 later steps' loads stay in flight), so after it the next stage is
     // complete.  Past the end of the K range the loads re-read the last group (clamped) into
-    // stages that are never read.
+    // stages that are never read.  With two stages the B tiles run further ahead (EARLY_B):
+    // step k issues step k+2's B tile halfway through, into its own stage's B half, and the
+    // wait before the barrier leaves those loads in flight (they are the wave's last DB).
 #pragma unroll
     for (int p = 0; p < T::NS - 1; ++p)
-        issue_step(p, p);
+        issue_a(p, p);
+    if (EARLY_B) {
+        issue_b(0, 0);
+        issue_b(1, 1);
+    }
     // this wave's loads per step: its tile loads, plus one scale load on the scale waves
     auto wait_next = [&]() {
         constexpr int C = DA + DB;
-        if (T::NS == 2) {
+        if (EARLY_B) {
+            vm_wait<DB>();   // all but the B tile of two steps ahead
+        } else if (T::NS == 2) {
             vm_wait<0>();
         } else if (sA_wave || sB_wave) {
             vm_wait<(T::NS - 2) * (C + 1)>();
@@ -416,11 +440,17 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     int st = 0, st_load = T::NS - 1;
 #pragma nounroll
     for (int v = 0; v < len; ++v) {
-        issue_step(v + T::NS - 1, st_load);
+        issue_a(v + T::NS - 1, st_load);
+        // EARLY_B: once every wave holds this step's B fragments (they are read at the start
+        // of the step), the B half of this stage takes the B tile of step v + 2
+        auto mid = [&]() {
+            stage_barrier();
+            issue_b(v + 2, st);
+        };
         if (SC == 1)
-            compute(smA[st], smB[st], sS[st], 0);
+            compute(smA[st], smB[st], sS[st], 0, mid);
         else
-            compute(smA[st], smB[st], sS[(v / SC) & 1], v & (SC - 1));
+            compute(smA[st], smB[st], sS[(v / SC) & 1], v & (SC - 1), mid);
         wait_next();   // this wave's loads of step k+1
         stage_barrier();
         st = st + 1 == T::NS ? 0 : st + 1;
@@ -428,7 +458,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     }
     // with more than two stages the last NS-2 steps' loads (clamped re-reads into stages that
     // are never read) are still in flight: they land before the workgroup's LDS is released
-    if (T::NS > 2)
+    if (T::NS > 2 || EARLY_B)
         vm_wait<0>();
 
     // ---- epilogue: lane holds C[m][n..n+3] for each sub-tile
@@ -443,7 +473,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm(GemmArgs g)
     if constexpr (OUT_BF16 && T::TN == 64) {
         static_assert(T::BM * T::BN * 2 <= T::NS * (T::BM + T::BN) * kGroup, "tile fits the stages");
         if (g.split == 1 && (N & 7) == 0) {
-            if (T::NS > 2)
+            if (T::NS > 2 || EARLY_B)
                 stage_barrier();   // every wave's last loads have landed (its vm_wait above)
             uint8_t *ep = smem + wave * (T::TM * 128);
 #pragma unroll
@@ -893,19 +923,29 @@ void tile_dims(int cfg, int &bm, int &bn)
     }
 }
 
-template <class T, int BSCALE, bool OUT_BF16>
+template <class T, int BSCALE, bool OUT_BF16, bool EB = false>
 hipError_t launch_cfg(const GemmArgs &a, int blocks, hipStream_t stream)
 {
-    k_gemm<T, BSCALE, OUT_BF16><<<blocks, T::THREADS, 0, stream>>>(a);
+    k_gemm<T, BSCALE, OUT_BF16, EB><<<blocks, T::THREADS, 0, stream>>>(a);
     return hipGetLastError();
 }
 
+// The early B loads (EB) serve launches whose tiles form one row band (decode batches of up to
+// 256 rows streaming a weight: the 32B layer's four linears at batch 256 went 220.9 -> 213.2 us
+// in whole-bench A/B runs, gate+up 91.1 -> 85.2 and QKV 34.0 -> 32.0 in isolation).  The
+// training GEMMs' tiles share panels through L2 and have their loads in flight longer already;
+// there the extra barrier cost about 1 % in the same A/B runs, so they keep one barrier.
 template <class T>
 hipError_t launch_t(int bscale, bool out_bf16, const GemmArgs &a, int blocks, hipStream_t s)
 {
     if (bscale == BSCALE_ROW)
         return out_bf16 ? launch_cfg<T, BSCALE_ROW, true>(a, blocks, s)
                         : launch_cfg<T, BSCALE_ROW, false>(a, blocks, s);
+    if constexpr (T::NS == 2) {
+        if (a.tilesM == 1)
+            return out_bf16 ? launch_cfg<T, BSCALE_BLOCK, true, true>(a, blocks, s)
+                            : launch_cfg<T, BSCALE_BLOCK, false, true>(a, blocks, s);
+    }
     return out_bf16 ? launch_cfg<T, BSCALE_BLOCK, true>(a, blocks, s)
                     : launch_cfg<T, BSCALE_BLOCK, false>(a, blocks, s);
 }
