@@ -603,7 +603,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // stages.  A 32-byte fragment (lane l: row l % 16, 16-byte chunks 2 (l / 16) and
 // 2 (l / 16) + 1 of the 128-byte K step) feeds two 16x16x64 MFMAs, one per chunk; A and B use
 // the same lane-to-K assignment, so together the two cover all 128 K of the step.
-template <class T, bool OUT_BF16>
+template <class T, bool OUT_BF16, bool EB = false>
 __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
 {
     constexpr int NW = T::WM * T::WN;
@@ -646,6 +646,16 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
         return (uint32_t)(row * K + ((lslot ^ swz(row)) << 4));
     };
     const uint32_t ldsA = lds_addr_of(&smA[0][0]), ldsB = lds_addr_of(&smB[0][0]);
+    // EB: the B tile of step v + 2 goes out halfway through step v, as in the FP8 GEMM
+    constexpr bool EARLY_B = EB && T::NS == 2;
+    auto issue_b = [&](int kg, int st) {
+        const uint32_t k0 = (uint32_t)kg * kGroup;
+#pragma unroll
+        for (int j = 0; j < DB; ++j) {
+            const int t = wave + j * NW;
+            dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
+        }
+    };
     auto issue_step = [&](int kg, int st) {
         const uint32_t k0 = (uint32_t)kg * kGroup;
 #pragma unroll
@@ -653,11 +663,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
             const int t = wave + j * NW;
             dma16(rA, ldsA + (uint32_t)(st * T::BM * kGroup + t * 1024), tile_voff(t) + k0);
         }
-#pragma unroll
-        for (int j = 0; j < DB; ++j) {
-            const int t = wave + j * NW;
-            dma16(rB, ldsB + (uint32_t)(st * T::BN * kGroup + t * 1024), tile_voff(t) + k0);
-        }
+        if (!EARLY_B)
+            issue_b(kg, st);
     };
 
     v4i acc[T::IM][T::JN];
@@ -677,7 +684,7 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
         f.hi = *reinterpret_cast<const v4i *>(p + frag_hi);
         return f;
     };
-    auto compute = [&](const uint8_t *tA, const uint8_t *tB) {
+    auto compute = [&](const uint8_t *tA, const uint8_t *tB, auto &&mid) {
         Frag bf[T::JN];
 #pragma unroll
         for (int j = 0; j < T::JN; ++j)
@@ -698,6 +705,8 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
             for (int j = 0; j < T::JN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[j].hi, afb[i & 1].hi,
                                                                    acc[i][j], 0, 0, 0);
+            if (EARLY_B && i == T::IM / 2 - 1)
+                mid();
         }
     };
 
@@ -716,7 +725,9 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
         return gb + (x >= len ? x - len : x);
     };
     auto wait_next = [&]() {
-        if (T::NS == 2)
+        if (EARLY_B)
+            vm_wait<DB>();   // all but the B tile of two steps ahead
+        else if (T::NS == 2)
             vm_wait<0>();
         else
             vm_wait<(T::NS - 2) * (DA + DB)>();
@@ -725,6 +736,10 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
 #pragma unroll
         for (int p = 0; p < T::NS - 1; ++p)
             issue_step(grp(p), p);
+        if (EARLY_B) {
+            issue_b(grp(0), 0);
+            issue_b(grp(1), 1);
+        }
     }
     wait_next();
     stage_barrier();
@@ -732,13 +747,17 @@ __global__ __launch_bounds__(T::THREADS) void k_gemm_i8(GemmI8Args g)
 #pragma nounroll
     for (int v = 0; v < len; ++v) {
         issue_step(grp(v + T::NS - 1), st_load);
-        compute(smA[st], smB[st]);
+        auto mid = [&]() {
+            stage_barrier();
+            issue_b(grp(v + 2), st);
+        };
+        compute(smA[st], smB[st], mid);
         wait_next();
         stage_barrier();
         st = st + 1 == T::NS ? 0 : st + 1;
         st_load = st_load + 1 == T::NS ? 0 : st_load + 1;
     }
-    if (T::NS > 2) {
+    if (T::NS > 2 || EARLY_B) {
         vm_wait<0>();      // the last steps' re-reads land before the stages are reused
         stage_barrier();
     }
@@ -1143,16 +1162,22 @@ hipError_t launch_gemm_i8(bool out_bf16, const int8_t *A, const float *sa, const
     a.tilesN = (int)((N + bn - 1) / bn);
     a.krot = plan.split > 1 ? 0 : a.tilesM == 1 ? kKRotMul : -kKRotXcd;
     const unsigned blocks = (unsigned)(a.tilesM * a.tilesN * plan.split);
-    if (big) {
+    const bool eb = a.tilesM == 1;   // one row band: the early B loads (as the FP8 GEMM)
+    if (big && eb) {
+        if (out_bf16)
+            k_gemm_i8<CfgBig4, true, true><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
+        else
+            k_gemm_i8<CfgBig4, false, true><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
+    } else if (big) {
         if (out_bf16)
             k_gemm_i8<CfgBig4, true><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
         else
             k_gemm_i8<CfgBig4, false><<<blocks, CfgBig4::THREADS, 0, stream>>>(a);
     } else if (mid) {
         if (out_bf16)
-            k_gemm_i8<CfgW128, true><<<blocks, CfgW128::THREADS, 0, stream>>>(a);
+            k_gemm_i8<CfgW128, true, true><<<blocks, CfgW128::THREADS, 0, stream>>>(a);
         else
-            k_gemm_i8<CfgW128, false><<<blocks, CfgW128::THREADS, 0, stream>>>(a);
+            k_gemm_i8<CfgW128, false, true><<<blocks, CfgW128::THREADS, 0, stream>>>(a);
     } else {
         if (out_bf16)
             k_gemm_i8<CfgI8Small, true><<<blocks, CfgI8Small::THREADS, 0, stream>>>(a);
