@@ -691,6 +691,40 @@ def test_fprop_shapes_full(M, N, K, out):
     print(_fprop_case(None, x, w, out, name=f"{M}x{N}x{K}"))
 
 
+# The K-walk paths of the 256-row tiles, every output: one row band without a K split (each
+# workgroup's K start rotated, the early B loads) with 1, 2, 5 and 11 K groups, where a rotation
+# wraps inside a 4-group scale chunk unless it is kept on a chunk boundary (11 groups: rotations
+# of 0, 7 and 3; 5 groups: 0 and 1), on 256x256 tiles (65 and 200 rows, more than 128 tiles) and
+# 256x128 tiles (256 rows, 2 groups).
+SINGLE_BAND = [(200, 9000, 128), (256, 4104, 256), (100, 33024, 640), (65, 33000, 1408)]
+
+
+@pytest.mark.parametrize("M,N,K", SINGLE_BAND)
+def test_fprop_single_band_k_walk(M, N, K):
+    x = qr_synth.normal_bf16(M * 5 + N + K, (M, K), 1.0, 3, max(1, K // 100))
+    w = qr_synth.normal_bf16(M + 3 * N + K, (N, K), 0.02)
+    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, name=f"single band {M}x{N}x{K}"))
+
+
+@pytest.mark.parametrize("M,N,K", SINGLE_BAND)
+def test_gemm_int8_single_band_k_walk(M, N, K):
+    say("gemm_int8 single band", M, N, K)
+    qa, sa, qb, sb = _int8_case(M, N, K, 5 * M + N)
+    y = qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_F32)
+    assert np.array_equal(host(y), _int8_scaled_exact(qa, sa, qb, sb))
+
+
+def test_fprop_multi_band_xcd_rotation_sampled():
+    """Tiles over five row bands without a K split (130 tiles): each XCD starts its K walk at its
+    own scale chunk, 11 groups, so the start wraps inside the range; sampled outputs with every
+    tile edge."""
+    M, N, K = 1280, 6656, 1408
+    x = qr_synth.normal_bf16(17, (M, K), 1.0, 5, 14)
+    w = qr_synth.normal_bf16(19, (N, K), 0.02)
+    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, sample=sample_positions(M, N, 4096, seed=M + K),
+                      name="multi band 1280x6656x1408"))
+
+
 def test_fprop_decode_8b_full():
     lin = qr_synth.decode_8b()
     print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_BF16, None, "decode_8b", literal=True))
