@@ -975,6 +975,8 @@ constexpr int64_t kCUs = 256;   // MI355X compute units: one 256x256 workgroup e
 
 // Fewest K groups per split on the 256-row tiles.
 constexpr int64_t kMinSplitGroups = 3;
+// Most K steps per workgroup of the 256-row tiles for which a product moves to the decode tiles.
+constexpr int64_t kShortKSteps = 6;
 
 GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
 {
@@ -1045,6 +1047,28 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
             split = 1;
         const int64_t kgps = (nk + split - 1) / split;
         split = (nk + kgps - 1) / kgps;
+    }
+    // Short K walks on the 256-row tiles: when their workgroups would walk only a few K steps
+    // each and K is split (partial sums for a few steps) or there are few of them, the decode
+    // tiles (64 rows, a four-stage ring) are faster: 64x64 tiles up to 256 of them, else
+    // 64x128.  Event medians after a cache-evicting read, 256-row plan -> decode tiles:
+    // 256x512x512 11.0 -> 7.0 us, 1024x1024x1024 23.5 -> 8.8, 2048x2048x2048 36.4 -> 26.1,
+    // 4096x2048x1024 36.6 -> 30.2, 1024x4096x512 (64 tiles, unsplit) 15.6 -> 13.9.  Unsplit
+    // launches with more workgroups keep the 256-row tiles (200x16000x512, 125 workgroups: 11.4
+    // against 13.8), as do the 32B layer's decode batches (7 or more steps per workgroup).
+    const int64_t wgs = tiles * split;
+    if (bscale == BSCALE_BLOCK && M > 64 && nk > 0 && (nk + split - 1) / split <= kShortKSteps &&
+        (split > 1 || wgs <= kCUs / 4)) {
+        const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+        p.cfg = t64 <= kCUs ? CFG_DEC64 : CFG_DEC128;
+        tile_dims(p.cfg, bm, bn);
+        const int64_t t = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        split = 1;
+        if (t <= kCUs / 2 && nk >= 16) {   // the decode split rule above
+            split = std::min<int64_t>(kCUs / t, nk / 8);
+            const int64_t kgps = (nk + split - 1) / split;
+            split = (nk + kgps - 1) / kgps;
+        }
     }
     p.split = (int)split;
     p.ws_bytes = split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;

@@ -214,7 +214,10 @@ def gemm(L, name, a, sa, b, sb, M, N, K, y, dt, ws, wsb):
 def test_gemm_validation(L, name):
     # the contraction size is K for FProp, N for DGrad, M for WGrad
     contraction = {"qr_gemm_fp8_bsfprop": 2, "qr_gemm_fp8_bsdgrad": 1, "qr_gemm_fp8_bswgrad": 0}[name]
-    dims = [2048, 2048, 2048]
+    kind = {"qr_gemm_fp8_bsfprop": 0, "qr_gemm_fp8_bsdgrad": 1, "qr_gemm_fp8_bswgrad": 2}[name]
+    # shapes whose plans split K, so that a workspace is needed: 128 rows (64x64 decode tiles,
+    # 4 and 2 splits) for FProp and DGrad, 2048^3 (64 256x256 tiles, 4 splits) for WGrad
+    dims = [2048, 2048, 2048] if kind == 2 else [128, 2048, 4096]
     bad = list(dims)
     bad[contraction] = 200
     assert gemm(L, name, A, B, C, D, *bad, E, 1, None, 0) == SHAPE
@@ -224,8 +227,7 @@ def test_gemm_validation(L, name):
     assert gemm(L, name, A, B, C, D, *dims, None, 1, None, 0) == NULL
     assert gemm(L, name, A + 4, B, C, D, *dims, E, 1, None, 0) == ALIGN
     assert gemm(L, name, A, B + 2, C, D, *dims, E, 1, None, 0) == ALIGN
-    # 2048^3 splits K 4 ways over its 64 256x256 tiles, so a (large enough) workspace is passed
-    ws, wsb = 6 << 40, qr.qr_gemm_workspace_bytes(0, 2048, 2048, 2048)
+    ws, wsb = 6 << 40, qr.qr_gemm_workspace_bytes(kind, *dims)
     assert wsb > 0
     assert gemm(L, name, A, B, C, D, *dims, E, 1, None, 0) == WORKSPACE
     assert gemm(L, name, A, B, C, D, *dims, A + 64, 1, ws, wsb) == ALIAS    # output over A

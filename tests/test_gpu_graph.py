@@ -31,8 +31,9 @@ def _ws(kind, M, N, K):
 
 def _build():
     """Inputs, outputs and the calls of one captured step (small shapes that still take every
-    plan: split and unsplit 256-row tiles, one row band with early B loads, the decode tiles
-    with a split, the batched norm paths, INT8 with a split, the 4-bit path)."""
+    plan: the 256-row tiles over several row bands and in one band with early B loads and a K
+    split, the decode tiles with and without a split, the batched norm paths, INT8 with a split,
+    the 4-bit path)."""
     f32, bf, i8 = torch.float32, torch.bfloat16, torch.int8
     T, N, K = 640, 1024, 768                        # tokens, output features, input features
     rng = np.random.default_rng(5)
@@ -52,6 +53,8 @@ def _build():
     Wn = dev_bf16(qr_synth.normal_bf16(52, (4096, 1024), 0.02))
     X4 = dev_bf16(qr_synth.normal_bf16(53, (64, 1024), 1.0))
     W4 = dev_bf16(qr_synth.normal_bf16(54, (1000, 1024), 0.02))
+    Xs = dev_bf16(qr_synth.normal_bf16(55, (200, 8192), 1.0))
+    Ws = dev_bf16(qr_synth.normal_bf16(56, (4096, 8192), 0.02))
 
     o = {}
     o["Wf"], o["qW"], o["sW"] = _e(N, K, dt=bf), _e(N, K), _e(N // 128, K // 128, dt=f32)
@@ -73,11 +76,15 @@ def _build():
                                                        _e(32, 8, dt=f32), _e(200, 4096, dt=bf))
     o["c4"], o["b4"], o["t4"], o["Y4"] = (_e(1000, 512), _e(1000, 64), _e(1, dt=f32),
                                           _e(64, 1000, dt=bf))
+    o["qXs"], o["sXs"], o["qWs"], o["sWs"], o["Ys"] = (_e(200, 8192), _e(200, 64, dt=f32), _e(4096, 8192),
+                                                       _e(32, 64, dt=f32), _e(200, 4096, dt=bf))
     ws = {"fprop": _ws(qr.QR_GEMM_FPROP, T, N, K), "dgrad": _ws(qr.QR_GEMM_DGRAD, T, N, K),
           "wgrad": _ws(qr.QR_GEMM_WGRAD, T, N, K), "dec": _ws(qr.QR_GEMM_FPROP, 64, 4096, 4096),
-          "band": _ws(qr.QR_GEMM_FPROP, 200, 9000, 512), "i8": _ws(qr.QR_GEMM_INT8, 200, 1000, 2048)}
+          "band": _ws(qr.QR_GEMM_FPROP, 200, 9000, 512), "i8": _ws(qr.QR_GEMM_INT8, 200, 1000, 2048),
+          "split": _ws(qr.QR_GEMM_FPROP, 200, 4096, 8192)}
     ws4 = _e(qr.QR_NVFP4_WORKSPACE_BYTES)
-    assert ws["fprop"][1] > 0 and ws["dec"][1] > 0 and ws["i8"][1] > 0, "split paths expected"
+    # split paths: the decode tiles (64 rows), 256x128 tiles (one row band, 8 splits), INT8
+    assert ws["dec"][1] > 0 and ws["split"][1] > 0 and ws["i8"][1] > 0, "split paths expected"
     assert ws["band"][1] == 0, "one row band, unsplit, expected"
     BF, F32 = qr.QR_OUT_BF16, qr.QR_OUT_F32
 
@@ -106,6 +113,9 @@ def _build():
         qr.qr_quant_w_nvfp4(W4, 1000, 1024, 1024, o["c4"], o["b4"], o["t4"], ws4,
                             qr.QR_NVFP4_WORKSPACE_BYTES)
         qr.qr_gemm_w4a16(X4, o["c4"], o["b4"], o["t4"], 64, 1000, 1024, o["Y4"], BF)
+        qr.qr_quant_act_1x128(Xs, 200, 8192, 8192, o["qXs"], o["sXs"], None, None)
+        qr.qr_quant_w_128x128(Ws, 4096, 8192, 8192, o["qWs"], o["sWs"], None, None)
+        qr.qr_gemm_fp8_bsfprop(o["qXs"], o["sXs"], o["qWs"], o["sWs"], 200, 4096, 8192, o["Ys"], BF, *ws["split"])
 
     o["gain_d"] = dev(np.full(4096, 1.25, np.float32))
     outputs = [k for k in o if k != "gain_d"]

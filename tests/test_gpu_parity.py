@@ -656,13 +656,15 @@ def test_fprop_tiny_fp32_full():
     print(_fprop_case(lin, lin.x(), lin.w(), qr.QR_OUT_F32, name="tiny_fprop", literal=True))
 
 
+# Products of these sizes with M > 64 mostly take the 64-row decode tiles (their K walks on
+# 256-row tiles would be short); the comments name what a shape exercises.
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (1, 128, 128), (300, 264, 256),
                                    (129, 1000, 640), (64, 512, 1024), (256, 384, 2048),
                                    (520, 136, 384),
-                                   # 256x256 tiles with one K step, and with ragged M and N
+                                   # one K step, and ragged M and N over several row bands
                                    (300, 264, 128), (600, 520, 1152),
-                                   # unsplit tiles with ragged M and N % 8 == 0: the bf16 output
-                                   # staged through LDS on 256x256 and on 256x128 tiles
+                                   # unsplit 256-row tiles with ragged M and N % 8 == 0: the bf16
+                                   # output staged through LDS on 256x256 and on 256x128 tiles
                                    (2050, 4104, 128), (200, 16392, 512),
                                    # decode batches (M <= 64): ragged N, group counts that
                                    # are not a multiple of the four-stage ring
@@ -680,9 +682,9 @@ def test_fprop_tiny_fp32_full():
                                    (77, 77, 384), (2048, 4097, 128), (300, 201, 256),
                                    (5, 13, 1152), (40, 14337, 256), (64, 1001, 2304),
                                    (1, 3, 128),
-                                   # the planner's row boundaries: 65 rows (256x128 tiles, 6
-                                   # splits of 3 K groups) and 257 rows (256x256 tiles over two
-                                   # row bands, the last of 3 splits shorter)
+                                   # the planner's row boundaries: 65 rows (the decode tiles
+                                   # over two row bands, 2 K splits) and 257 rows (64x128 tiles
+                                   # over five row bands)
                                    (65, 1000, 2304), (257, 7168, 1280)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_fprop_shapes_full(M, N, K, out):
@@ -696,7 +698,7 @@ def test_fprop_shapes_full(M, N, K, out):
 # wraps inside a 4-group scale chunk unless it is kept on a chunk boundary (11 groups: rotations
 # of 0, 7 and 3; 5 groups: 0 and 1), on 256x256 tiles (65 and 200 rows, more than 128 tiles) and
 # 256x128 tiles (256 rows, 2 groups).
-SINGLE_BAND = [(200, 9000, 128), (256, 4104, 256), (100, 33024, 640), (65, 33000, 1408)]
+SINGLE_BAND = [(200, 9000, 128), (256, 9000, 256), (100, 33024, 640), (65, 33000, 1408)]
 
 
 @pytest.mark.parametrize("M,N,K", SINGLE_BAND)
@@ -712,6 +714,18 @@ def test_gemm_int8_single_band_k_walk(M, N, K):
     qa, sa, qb, sb = _int8_case(M, N, K, 5 * M + N)
     y = qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_F32)
     assert np.array_equal(host(y), _int8_scaled_exact(qa, sa, qb, sb))
+
+
+def test_fprop_multi_band_split_sampled():
+    """256x256 tiles over five row bands with K split 3 ways (11 groups per split, the last one
+    shorter; ragged M and N): the split path of the multi-band tiles, sampled outputs with every
+    tile edge."""
+    M, N, K = 1030, 4100, 4096
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_FPROP, M, N, K) == 3 * M * N * 4
+    x = qr_synth.normal_bf16(23, (M, K), 1.0, 5, 40)
+    w = qr_synth.normal_bf16(29, (N, K), 0.02)
+    print(_fprop_case(None, x, w, qr.QR_OUT_BF16, sample=sample_positions(M, N, 4096, seed=M + N),
+                      name="multi band split 1030x4100x4096"))
 
 
 def test_fprop_multi_band_xcd_rotation_sampled():

@@ -49,10 +49,11 @@ def _both(M, N, K, seed, out):
 
 # (large, then smaller): 32B QKV at batch 256 (4 K splits on 256x128 tiles, 29 MB of partials)
 # then the 8B O projection at batch 64 (4 splits, 4 MB); a 2-split decode then an unsplit one;
-# a ragged split on one 256x128 tile (odd M * N, 2 splits) then a smaller unsplit ragged one
+# a ragged split of 201 rows on the 64-row tiles (odd M * N, 2 splits) then a smaller unsplit
+# ragged one
 PAIRS = [((256, 7168, 5120), (64, 4096, 4096)),
          ((64, 1000, 2304), (16, 200, 384)),
-         ((201, 77, 1024), (77, 77, 384))]
+         ((201, 77, 2048), (77, 77, 384))]
 
 
 @pytest.mark.parametrize("first,second", PAIRS)
