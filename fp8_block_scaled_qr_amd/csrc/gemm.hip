@@ -1158,6 +1158,22 @@ GemmPlan plan_gemm_i8(int64_t M, int64_t N, int64_t K)
         const int64_t kgps = (nk + split - 1) / split;
         split = (nk + kgps - 1) / kgps;
     }
+    // Short K walks on the 256-row tiles take the 64x64 tiles instead, as in the FP8 plan (up
+    // to 1024 of them: there is no 64x128 INT8 form).  Old plan -> 64x64 tiles, event medians
+    // after a cache-evicting read: 256x512x512 16.2 -> 8.6 us, 1024x1024x1024 23.1 -> 10.1,
+    // 2048x2048x2048 36.2 -> 27.6, 1024x4096x512 24.6 -> 17.0; 2048x4096x1536 (2048 small
+    // tiles) keeps its plan (36.8 against 42.8).
+    const int64_t wgs = (p.cfg == 2 ? mid_tiles : big_tiles) * split;
+    if (p.cfg != 0 && nk > 0 && (nk + split - 1) / split <= kShortKSteps &&
+        (split > 1 || wgs <= kCUs / 4) && small_tiles <= 4 * kCUs) {
+        p.cfg = 0;
+        split = 1;
+        if (small_tiles <= kCUs / 2 && nk >= 16) {   // the 64x64 split rule above
+            split = std::min<int64_t>(kCUs / small_tiles, nk / 8);
+            const int64_t kgps = (nk + split - 1) / split;
+            split = (nk + kgps - 1) / kgps;
+        }
+    }
     p.split = (int)split;
     p.ws_bytes = split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
     return p;

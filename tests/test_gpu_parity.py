@@ -249,22 +249,25 @@ def _check_int8(y, Y, out):
 
 
 def _int8_scaled_exact(qa, sa, qb, sb):
-    """The entry point's definition in binary32: float(exact integer sum) * (sa[m] * sb[n])."""
-    S = qa.astype(np.int64) @ qb.astype(np.int64).T
+    """The entry point's definition in binary32: float(exact integer sum) * (sa[m] * sb[n]).
+    The integer sums are formed in binary64, exact because every partial sum is an integer of
+    magnitude at most K * 127^2 < 2^53."""
+    assert qa.shape[1] * 127 * 127 < 2 ** 53
+    S = qa.astype(np.float64) @ qb.astype(np.float64).T
     assert np.abs(S).max(initial=0) < 2 ** 31
     scale = sa.astype(np.float32)[:, None] * sb.astype(np.float32)[None, :]
     return S.astype(np.float32) * scale
 
 
-# (77, 200, 384): 256x128 tiles with K split 3 ways; (300, 264, 256), (520, 304, 384): 256x256
-# tiles with K split 2 and 3 ways;
-# (64, 512, 4096) and (40, 1000, 2304): 64x64 tiles split 4 and 2 ways; (130, 201, 512): an odd
-# N on a 4-way split (scalar partial stores and sums); (520, 264, 128) and (520, 300, 128):
-# unsplit 256x256 tiles with ragged M and N, the bf16 output staged through LDS (N % 8 == 0)
-# and stored directly (N % 8 != 0); the rest unsplit
+# Small products (their K walks on 256-row tiles would be short) take the 64x64 tiles: most of
+# the shapes below, (64, 512, 4096) and (40, 1000, 2304) split 4 and 2 ways, and (130, 201, 2048)
+# an odd N on a 2-way split (scalar partial stores and sums).  (2050, 4104, 128) and
+# (2050, 4100, 128): unsplit 256x256 tiles with ragged M and N, the bf16 output staged through
+# LDS (N % 8 == 0) and stored directly (N % 8 != 0).
 @pytest.mark.parametrize("M,N,K", [(77, 200, 384), (64, 1000, 1024), (1, 128, 128),
                                    (300, 264, 256), (520, 304, 384), (17, 72, 640),
                                    (64, 512, 4096), (40, 1000, 2304), (130, 201, 512),
+                                   (130, 201, 2048), (2050, 4104, 128), (2050, 4100, 128),
                                    (520, 264, 128), (520, 300, 128)])
 @pytest.mark.parametrize("out", [qr.QR_OUT_F32, qr.QR_OUT_BF16])
 def test_gemm_int8(M, N, K, out):
@@ -275,6 +278,17 @@ def test_gemm_int8(M, N, K, out):
     if out == qr.QR_OUT_F32:
         # split or not, the integer sum is exact and scaled once: equal bits
         assert np.array_equal(y.cpu().numpy(), _int8_scaled_exact(qa, sa, qb, sb))
+
+
+def test_gemm_int8_multi_band_split_exact():
+    """256x256 tiles over three row bands with K split 10 ways (7 groups per split, the last
+    one shorter): bit-exact fp32 against float(exact sum) * (sa * sb)."""
+    M, N, K = 520, 2048, 8192
+    say("gemm_int8 multi-band split", M, N, K)
+    assert qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, M, N, K) == 10 * M * N * 4
+    qa, sa, qb, sb = _int8_case(M, N, K, 31)
+    y = qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_F32)
+    assert np.array_equal(host(y), _int8_scaled_exact(qa, sa, qb, sb))
 
 
 def test_gemm_int8_empty_zero_k_and_workspace_reuse():
@@ -288,7 +302,7 @@ def test_gemm_int8_empty_zero_k_and_workspace_reuse():
                          4, 8, 0, y, qr.QR_OUT_F32)
     assert float(y.abs().max()) == 0.0
     qr.qr_gemm_int8_w8a8(None, None, None, None, 0, 8, 128, y, qr.QR_OUT_F32)   # M = 0
-    shapes = [(300, 264, 1024), (100, 136, 1152)]
+    shapes = [(200, 5888, 5120), (100, 136, 2048)]   # 256x128 tiles split 5 ways; 64x64 split 2
     nb = max(qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, *sh) for sh in shapes)
     assert all(qr.qr_gemm_workspace_bytes(qr.QR_GEMM_INT8, *sh) > 0 for sh in shapes)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
@@ -306,9 +320,9 @@ def test_gemm_int8_empty_zero_k_and_workspace_reuse():
                                    (64, 4096, 14336)])
 def test_gemm_int8_full_size(M, N, K):
     """The 8B prefill shape, the 8B decode shape, the 32B down (K split 12 ways) and gate+up
-    projections at batch 256, a ragged-M batch on the 256x256 tiles (128 tiles, the smallest
-    count that takes them without a split), the 32B QKV at batch 256 (256x128 tiles, split 4 ways) and the 8B
-    down at batch 64 (64x64 tiles, split 4 ways); every output."""
+    projections at batch 256, a ragged-M batch with two K groups on 256 unsplit 256x128 tiles,
+    the 32B QKV at batch 256 (256x128 tiles, split 4 ways) and the 8B down at batch 64 (64x64
+    tiles, split 4 ways); every output."""
     say("gemm_int8 full", M, N, K)
     qa, sa, qb, sb = _int8_case(M, N, K, 3 * M + N)
     y = out_f64(qr.gemm_int8(dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=qr.QR_OUT_BF16))
