@@ -1053,11 +1053,13 @@ GemmPlan plan_gemm(int bscale, int64_t M, int64_t N, int64_t K)
     // tiles (64 rows, a four-stage ring) are faster: 64x64 tiles up to 256 of them, else
     // 64x128.  Event medians after a cache-evicting read, 256-row plan -> decode tiles:
     // 256x512x512 11.0 -> 7.0 us, 1024x1024x1024 23.5 -> 8.8, 2048x2048x2048 36.4 -> 26.1,
-    // 4096x2048x1024 36.6 -> 30.2, 1024x4096x512 (64 tiles, unsplit) 15.6 -> 13.9.  Unsplit
-    // launches with more workgroups keep the 256-row tiles (200x16000x512, 125 workgroups: 11.4
-    // against 13.8), as do the 32B layer's decode batches (7 or more steps per workgroup).
+    // 4096x2048x1024 36.6 -> 30.2, 1024x4096x512 (64 tiles, unsplit) 15.6 -> 13.9; WGrad with
+    // per-row B scales, dW 1024x1024 over 1024 tokens 25.3 -> 9.0, 4096x1024 over 1024 tokens
+    // 31.3 -> 18.8.  Unsplit launches with more workgroups keep the 256-row tiles (200x16000x512,
+    // 125 workgroups: 11.4 against 13.8; dW 4096x4096 over 512 tokens: 21.7 against 40.8), as do
+    // the 32B layer's decode batches (7 or more steps per workgroup).
     const int64_t wgs = tiles * split;
-    if (bscale == BSCALE_BLOCK && M > 64 && nk > 0 && (nk + split - 1) / split <= kShortKSteps &&
+    if (M > 64 && nk > 0 && (nk + split - 1) / split <= kShortKSteps &&
         (split > 1 || wgs <= kCUs / 4)) {
         const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
         p.cfg = t64 <= kCUs ? CFG_DEC64 : CFG_DEC128;

@@ -216,8 +216,9 @@ def test_gemm_validation(L, name):
     contraction = {"qr_gemm_fp8_bsfprop": 2, "qr_gemm_fp8_bsdgrad": 1, "qr_gemm_fp8_bswgrad": 0}[name]
     kind = {"qr_gemm_fp8_bsfprop": 0, "qr_gemm_fp8_bsdgrad": 1, "qr_gemm_fp8_bswgrad": 2}[name]
     # shapes whose plans split K, so that a workspace is needed: 128 rows (64x64 decode tiles,
-    # 4 and 2 splits) for FProp and DGrad, 2048^3 (64 256x256 tiles, 4 splits) for WGrad
-    dims = [2048, 2048, 2048] if kind == 2 else [128, 2048, 4096]
+    # 4 and 2 splits) for FProp and DGrad, dW 512x1024 over 4096 tokens (64x64 tiles, 2 splits)
+    # for WGrad
+    dims = [4096, 512, 1024] if kind == 2 else [128, 2048, 4096]
     bad = list(dims)
     bad[contraction] = 200
     assert gemm(L, name, A, B, C, D, *bad, E, 1, None, 0) == SHAPE
