@@ -27,7 +27,8 @@ kernel from its launches in the timed pass, and the CPU oracle timed on bounded 
 same step (all cores and one core; quantizers and GEMMs separately).  Outside the step it also
 times, each after a cache-evicting read where the op is HBM-bound:
   prefill_8b      the 1x128 quantize of X and FProp as one unit (combined TFLOP/s)
-  tiny_fprop      the tiny FProp workload's three launches (microseconds only)
+  tiny_fprop      the tiny FProp workload's three launches (microseconds only), as the host
+                  issues them and with each call queued behind a long read (GPU-side time)
   decode_32b      the 32B decoder layer's four linears at decode batch 256 on the seeded,
                   UAQ-folded inputs of that workload
   ceilings        the best single-launch streaming rate over the decode GEMM's 60.84 MB
@@ -574,6 +575,11 @@ def run_tiny_fprop(torch, qr, iters=50):
         for f in parts.values():
             f()
     out["total_us"] = round(_median_us(torch, whole, iters, flush=False), 2)
+    # The same calls with a long read queued ahead of each, so every launch is already in the
+    # queue when the GPU reaches it: the GPU-side time, dispatch gaps included. The figures
+    # above are paced by the host's per-call cost (the GPU waits for each launch).
+    for k, f in list(parts.items()) + [("total", whole)]:
+        out[f"queued_{k}_us"] = round(_median_us(torch, f, iters, flush=True), 2)
     out["workload"] = "tiny FProp: X [256, 512] 1x128 + W [512, 512] 128x128 quantize, GEMM to fp32 [256, 512]"
     return out
 
