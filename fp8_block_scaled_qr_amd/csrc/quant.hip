@@ -196,25 +196,25 @@ __device__ __forceinline__ float sumsq8(const uint4 &v, float ss)
     return ss;
 }
 
-// y = RN_bf16((h * inv) * gain) for 8 consecutive elements
+// y = RN_bf16((h * inv) * gain) for 8 consecutive elements.  The binary32 products are
+// rounded to bf16 in pairs by the packed conversion, round to nearest even (finite values,
+// subnormals kept).
 __device__ __forceinline__ uint4 rms_apply(const uint4 &v, float inv, const float4 &g0,
                                            const float4 &g1)
 {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        o[i] = f32_to_bf16(bf16_elem(v, 2 * i) * inv * g[2 * i]) |
-               (f32_to_bf16(bf16_elem(v, 2 * i + 1) * inv * g[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) {
+        const f32x2_t t = {bf16_elem(v, 2 * i) * inv * g[2 * i],
+                           bf16_elem(v, 2 * i + 1) * inv * g[2 * i + 1]};
+        o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(t, bf16x2_t));
+    }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// The norm in front of a linear layer with its 1x128 quantization fused in: one wave per row.
-// In pass p, lanes 16 t .. 16 t + 15 take 128-column group 4 p + t, 8 columns (16 bytes)
-// each, so a pass reads 1 KB of the row and a group's max is a 16-lane DPP reduction.  The
-// first phase sums h^2 (NP > 0: the row stays in registers, NP passes at most; NP == 0: the
-// second phase reads it again); the second forms y = RN_bf16((h * inv) * gain) with
-// inv = 1 / sqrt(sum / cols + eps) and encodes y exactly as the 1x128 quantizer does.
 // The norm ahead of an activation quantization: the tile's bf16 values h are replaced by
 // y = RN_bf16((h * inv[r]) * gain[c]) (the row statistics inv come from k_rms_inv) before the
 // maxima, and written to y if asked for.
@@ -651,7 +651,15 @@ __global__ __launch_bounds__(256) void k_quant_rows_small(const uint16_t *__rest
 
 // ---------------------------------------------------------------- RMSNorm + 1x128 quantize
 
-template <int NP>
+// The norm in front of a linear layer with its 1x128 quantization fused in: one wave per row.
+// In pass p, lanes 16 t .. 16 t + 15 take 128-column group 4 p + t, 8 columns (16 bytes)
+// each, so a pass reads 1 KB of the row and a group's max is a 16-lane DPP reduction.  The
+// first phase sums h^2 (NP > 0: the row stays in registers, NP passes at most; NP == 0: the
+// second phase reads it again); the second forms y = RN_bf16((h * inv) * gain) with
+// inv = 1 / sqrt(sum / cols + eps) and encodes y exactly as the 1x128 quantizer does.
+// FULL: cols is exactly NP passes (4096 columns for NP = 8), so no column checks; the gain
+// octets of the next pass are loaded while the current one is encoded.
+template <int NP, bool FULL>
 __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restrict__ h,
                                                        int64_t rows, int64_t cols, int64_t ldh,
                                                        const float *__restrict__ gain, float eps,
@@ -659,16 +667,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restric
                                                        uint8_t *__restrict__ q,
                                                        float *__restrict__ s)
 {
+    static_assert(!FULL || NP > 0, "whole passes keep the row in registers");
     const int lane = threadIdx.x & 63, sub = lane >> 4, li = lane & 15;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows)
         return;   // the whole wave; no barrier follows
-    const int64_t ngc = (cols + kTile - 1) / kTile, npass = (ngc + 3) / 4;
+    const int64_t ngc = (cols + kTile - 1) / kTile, npass = FULL ? NP : (ngc + 3) / 4;
     const uint16_t *hr = h + row * ldh;
-    auto col_of = [&](int64_t p) { return (4 * p + sub) * kTile + 8 * li; };
+    auto col_of = [&](int64_t p) { return (int)((4 * p + sub) * kTile + 8 * li); };
+    auto in_row = [&](int64_t c) { return FULL || c < cols; };
     auto load = [&](int64_t p) -> uint4 {
         const int64_t c = col_of(p);   // cols % 8 == 0: an octet is all in or out
-        return c < cols ? *reinterpret_cast<const uint4 *>(hr + c) : make_uint4(0, 0, 0, 0);
+        return in_row(c) ? *reinterpret_cast<const uint4 *>(hr + c) : make_uint4(0, 0, 0, 0);
     };
     float ss = 0.0f;
     uint4 keep[NP > 0 ? NP : 1];
@@ -687,13 +697,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restric
         ss += __shfl_xor(ss, o);       // every lane ends with the same sum
     const float inv = 1.0f / sqrtf(ss / (float)cols + eps);
 
-    auto body = [&](int64_t p, const uint4 &v) {
+    // the gain octet of pass p; a column past the row reads octet 0 instead (values unused)
+    auto gload = [&](int64_t p, float4 &g0, float4 &g1) {
+        const int64_t c = in_row(col_of(p)) ? col_of(p) : 0;
+        g0 = *reinterpret_cast<const float4 *>(gain + c);
+        g1 = *reinterpret_cast<const float4 *>(gain + c + 4);
+    };
+    auto body = [&](int64_t p, const uint4 &v, const float4 &g0, const float4 &g1) {
         const int64_t c = col_of(p);
-        const bool ok = c < cols;
+        const bool ok = in_row(c);
         uint4 yv = make_uint4(0, 0, 0, 0);
         if (ok) {
-            const float4 g0 = *reinterpret_cast<const float4 *>(gain + c);
-            const float4 g1 = *reinterpret_cast<const float4 *>(gain + c + 4);
             yv = rms_apply(v, inv, g0, g1);
             if (y)
                 *reinterpret_cast<uint4 *>(y + row * cols + c) = yv;
@@ -703,17 +717,27 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t *__restric
         if (ok)
             *reinterpret_cast<uint2 *>(q + row * cols + c) = c8;
         const int64_t g = 4 * p + sub;
-        if (li == 0 && g < ngc)
+        if (li == 0 && (FULL || g < ngc))
             s[row * ngc + g] = sc.s;
     };
     if (NP > 0) {
+        float4 ga0, ga1, gb0, gb1;
+        gload(0, ga0, ga1);
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-            if (p < npass)   // uniform across the wave
-                body(p, keep[p]);
+            if (p < npass) {   // uniform across the wave
+                if (p + 1 < NP && p + 1 < npass)
+                    gload(p + 1, gb0, gb1);     // one pass ahead
+                body(p, keep[p], ga0, ga1);
+                ga0 = gb0;
+                ga1 = gb1;
+            }
     } else {
-        for (int64_t p = 0; p < npass; ++p)
-            body(p, load(p));
+        for (int64_t p = 0; p < npass; ++p) {
+            float4 g0, g1;
+            gload(p, g0, g1);
+            body(p, load(p), g0, g1);
+        }
     }
 }
 
@@ -1063,12 +1087,14 @@ hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t rows, int64_t cols, i
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((rows + 3) / 4));
-    if (npass <= 8)
-        k_rmsnorm_quant<8><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+    if (cols == 8 * 512)   // whole passes only
+        k_rmsnorm_quant<8, true><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+    else if (npass <= 8)
+        k_rmsnorm_quant<8, false><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
     else if (npass <= 16)
-        k_rmsnorm_quant<16><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+        k_rmsnorm_quant<16, false><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
     else
-        k_rmsnorm_quant<0><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
+        k_rmsnorm_quant<0, false><<<grid, 256, 0, stream>>>(h, rows, cols, ld_h, gain, eps, y, q, s);
     return hipGetLastError();
 }
 

@@ -69,7 +69,8 @@ def assert_gemm_close(gpu: np.ndarray, Y: np.ndarray, S: np.ndarray, what: str,
 
 def check_norm_y(yg, h, g, eps):
     """The GPU's y against the oracle's RMSNorm: equal, or one bf16 ulp off where the exact
-    value lies within 2^-17 (relative) of a bf16 midpoint (binary32 evaluation)."""
+    value lies within 2^-17 (relative) of a bf16 midpoint, plus 2^-149 where the binary32
+    product is subnormal (its rounding there is absolute, up to 2^-150)."""
     yx, yb = oracle.rmsnorm(h, g, eps)
     diff = yg.astype(np.int32) - yb.astype(np.int32)
     bad = np.argwhere(diff != 0)
@@ -78,7 +79,7 @@ def check_norm_y(yg, h, g, eps):
         lo, hi = sorted((int(yg[i, j]) & 0x7FFF, int(yb[i, j]) & 0x7FFF))
         mid = (float(qr_synth.bf16_bits_to_f32(np.array([lo], np.uint16))[0]) +
                float(qr_synth.bf16_bits_to_f32(np.array([hi], np.uint16))[0])) / 2
-        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]), (i, j, yx[i, j])
+        assert abs(abs(yx[i, j]) - mid) <= 2.0 ** -17 * abs(yx[i, j]) + 2.0 ** -149, (i, j, yx[i, j])
     assert bad.shape[0] <= max(2, yg.size // 500)
 
 

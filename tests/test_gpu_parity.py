@@ -154,6 +154,8 @@ def test_rmsnorm_quant(rows, cols, eps, name):
     if rows > 4:
         h[1] = 0                                                  # a zero row (eps > 0)
         h[2] = qr_synth.f32_to_bf16_bits(np.full(cols, 3.0e-39, np.float32))  # subnormals
+    if cols >= 256:
+        g[128:256] *= np.float32(1e-39)     # a group whose y values are all subnormal
     hd, gd = dev_bf16(h), dev(g)
     y, q, s = qr.rmsnorm_quant(hd, gd, eps)
     yg = host(y)
@@ -185,6 +187,8 @@ def test_rmsnorm_quant_dual(rows, cols, eps, name):
     if rows > 4:
         h[1] = 0                                                  # a zero row (eps > 0)
         h[2] = qr_synth.f32_to_bf16_bits(np.full(cols, 3.0e-39, np.float32))  # subnormals
+    if cols >= 256:
+        g[128:256] *= np.float32(1e-39)     # a group whose y values are all subnormal
     hd, gd = dev_bf16(h), dev(g)
     inv, y, q, s, qT, sT = qr.rmsnorm_quant_dual(hd, gd, eps, want_y=True)
     hf = qr_synth.bf16_bits_to_f32(h).astype(np.float64)
