@@ -131,6 +131,7 @@ RMS_SHAPES = [(256, 512, 1e-6, "small"), (77, 200, 1e-6, "ragged rows, partial g
               (1, 8, 1e-5, "one row, 8 columns"), (300, 5120, 1e-6, "32B hidden: 10 passes"),
               (40, 27648, 1e-6, "down-proj width: row read twice"),
               (8192, 4096, 1e-6, "prefill_8b hidden full size"),
+              (333, 4096, 1e-5, "whole 512-column passes, rows % 4 != 0"),
               # few rows: a workgroup of 8 waves per row (one pass each, several passes kept
               # in registers, and the re-read path), ragged columns
               (64, 4096, 1e-6, "decode_8b hidden, 8 waves per row"),
