@@ -2,7 +2,12 @@
 oracle: the shapes are drawn across the planner's regions (decode batches of at most 64 rows,
 65..256-row batches, larger products), with ragged sizes and contraction lengths of 1 to 20
 groups, so that tile choices, K splits (and their three-groups rule) and ragged tails are met
-in combinations the hand-picked cases do not list.  The draw is fixed by the seed."""
+in combinations the hand-picked cases do not list.  The draw is fixed by the seed.
+
+QR_RANDOM_SHAPES_SEED (default 20261203) and QR_RANDOM_SHAPES_SCALE (default 1, a multiplier
+on every case count) widen the sweep: each family draws from the seed plus its own offset."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -23,6 +28,10 @@ def setup_module(module):
     qr.load()
 
 
+_SEED = int(os.environ.get("QR_RANDOM_SHAPES_SEED", "20261203"))
+_SCALE = int(os.environ.get("QR_RANDOM_SHAPES_SCALE", "1"))
+
+
 def _draw(seed, count, make):
     rng = np.random.Generator(np.random.PCG64(seed))
     return [make(rng) for _ in range(count)]
@@ -37,7 +46,7 @@ def _fprop_shape(rng):
     return M, N, K
 
 
-FPROP_SHAPES = _draw(20261203, 32, _fprop_shape)
+FPROP_SHAPES = _draw(_SEED + 0, 32 * _SCALE, _fprop_shape)
 
 
 @pytest.mark.parametrize("M,N,K", FPROP_SHAPES)
@@ -67,7 +76,7 @@ def _backward_shape(rng):
     return M, N, K
 
 
-BACKWARD_SHAPES = _draw(20261204, 12, _backward_shape)
+BACKWARD_SHAPES = _draw(_SEED + 1, 12 * _SCALE, _backward_shape)
 
 
 @pytest.mark.parametrize("M,N,K", BACKWARD_SHAPES)
@@ -101,7 +110,7 @@ def _int8_shape(rng):
     return M, N, K
 
 
-INT8_SHAPES = _draw(20261205, 12, _int8_shape)
+INT8_SHAPES = _draw(_SEED + 2, 12 * _SCALE, _int8_shape)
 
 
 @pytest.mark.parametrize("M,N,K", INT8_SHAPES)
@@ -132,7 +141,7 @@ def _quant_shape(rng):
     return 8 * int(rng.integers(1, 90)), 8 * int(rng.integers(1, 160))
 
 
-QUANT_SHAPES = _draw(20261206, 12, _quant_shape)
+QUANT_SHAPES = _draw(_SEED + 3, 12 * _SCALE, _quant_shape)
 
 
 @pytest.mark.parametrize("rows,cols", QUANT_SHAPES)
@@ -161,7 +170,7 @@ def _norm_shape(rng):
     return rows, cols
 
 
-NORM_SHAPES = _draw(20261207, 12, _norm_shape)
+NORM_SHAPES = _draw(_SEED + 4, 12 * _SCALE, _norm_shape)
 
 
 @pytest.mark.parametrize("rows,cols", NORM_SHAPES)
@@ -199,7 +208,7 @@ def _w4_shape(rng):
     return M, N, K
 
 
-W4_SHAPES = _draw(20261208, 12, _w4_shape)
+W4_SHAPES = _draw(_SEED + 5, 12 * _SCALE, _w4_shape)
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
